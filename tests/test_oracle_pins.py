@@ -1,0 +1,365 @@
+"""Pins for the CPU oracle: checks against facts the pages and mathematics fix,
+never against the oracle's own formulas retyped.
+
+Citations are to the FP4 training write-up "微软首创FP4训练框架，训练效果媲美BF16"
+(format, granularity, rounding, ScaleShift, outlier-clamp and compensation
+paragraphs) unless stated otherwise.
+"""
+import math
+import multiprocessing as mp
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as wl
+
+GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+# ---------------------------------------------------------------------------
+# E2M1 encoder: exhaustive against a brute-force nearest search
+# ---------------------------------------------------------------------------
+def _brute_nearest(y32):
+    """Nearest grid magnitude by explicit distance search in float64; on a tie
+    the larger magnitude wins (round half away from zero); NaN -> index 0."""
+    y = y32.astype(np.float64)
+    best = np.zeros(y.shape, dtype=np.uint8)
+    bestd = np.abs(y - 0.0)
+    for idx in range(1, 8):
+        d = np.abs(y - GRID[idx])
+        with np.errstate(invalid="ignore"):
+            take = d <= bestd
+        best = np.where(take, np.uint8(idx), best)
+        bestd = np.where(take, d, bestd)
+    return best
+
+
+def _check_chunk(start):
+    n = 1 << 24
+    bits = np.arange(start, start + n, dtype=np.uint64).astype(np.uint32)
+    y = bits.view(np.float32)
+    got = O.encode_magnitude(y)
+    want = _brute_nearest(y)
+    # NaN patterns: no midpoint reached, and no distance compares -> 0 both ways
+    bad = np.nonzero(got != want)[0]
+    return int(bad.size), (int(bits[bad[0]]) if bad.size else None)
+
+
+@pytest.mark.slow
+def test_e2m1_encoder_exhaustive_all_fp32_patterns():
+    """Every sign-clear float32 bit pattern y (the encoder sees y = |x|*inv >= 0,
+    or NaN): midpoint counting == nearest search (R3). 2^31 patterns."""
+    starts = [c << 24 for c in range(128)]
+    with mp.get_context("fork").Pool(min(8, mp.cpu_count())) as pool:
+        res = pool.map(_check_chunk, starts, chunksize=4)
+    nbad = sum(r[0] for r in res)
+    first = [r[1] for r in res if r[1] is not None]
+    assert nbad == 0, f"{nbad} mismatches, first bit pattern {first[:1]}"
+
+
+def test_e2m1_encoder_special_points():
+    """Grid points map to themselves, midpoints go up, saturation, NaN -> 0."""
+    for i, g in enumerate(GRID):
+        assert O.encode_magnitude(np.float32(g)) == i
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    for i, t in enumerate(mids):
+        assert O.encode_magnitude(np.float32(t)) == i + 1          # tie -> larger
+        below = np.nextafter(np.float32(t), np.float32(0))
+        assert O.encode_magnitude(below) == i                      # just below -> smaller
+    assert O.encode_magnitude(np.float32(6.0000005)) == 7
+    assert O.encode_magnitude(np.float32(np.inf)) == 7
+    assert O.encode_magnitude(np.float32(np.nan)) == 0
+    assert O.encode_magnitude(np.float32(1e-45)) == 0
+    neg_nan = np.array([0xFF800001, 0xFFC00000, 0xFFFFFFFF], dtype=np.uint32).view(np.float32)
+    assert not O.encode_magnitude(neg_nan).any()
+
+
+# ---------------------------------------------------------------------------
+# Scales: exact rounding through Fractions
+# ---------------------------------------------------------------------------
+def _rn32_fraction(fr: Fraction) -> np.float32:
+    """Round an exact rational to the nearest float32, ties to even, by
+    comparing exact distances to the two float32 neighbours."""
+    approx = np.float32(float(fr))
+    cands = {approx, np.nextafter(approx, np.float32(np.inf)),
+             np.nextafter(approx, np.float32(-np.inf))}
+    best = None
+    for c in cands:
+        if not np.isfinite(c):
+            continue
+        d = abs(Fraction(float(c)) - fr)
+        key = (d, int(np.array(c, np.float32).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return np.float32(best[1])
+
+
+def test_scales_exactly_rounded_tiny_workload():
+    """s = RN32(amax/6) and inv = RN32(6/amax) for every row of the tiny workload."""
+    L = wl.make_layer("tiny")
+    A = L.A.f32
+    amax = np.abs(A).max(axis=1)
+    s, inv = O.vector_scales(amax)
+    for i in range(A.shape[0]):
+        fa = Fraction(float(amax[i]))
+        assert s[i] == _rn32_fraction(fa / 6), i
+        assert inv[i] == _rn32_fraction(6 / fa), i
+
+
+def test_power_of_two_metamorphic():
+    """Scaling a row by 2^p leaves its codes unchanged and scales s by 2^p."""
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((16, 300)).astype(np.float32)
+    c0, s0 = O.quantize_rows(X)
+    for p in (-20, -3, 1, 7, 30):
+        f = np.float32(2.0 ** p)
+        c1, s1 = O.quantize_rows(X * f)
+        assert np.array_equal(c0, c1)
+        assert np.array_equal(s1, s0 * f)
+
+
+def test_grid_exact_rows_round_trip():
+    """Rows that already are s*{grid values} quantize without error (R1, R2)."""
+    rng = np.random.default_rng(5)
+    R, L = 64, 200
+    mags = rng.integers(0, 8, size=(R, L))
+    mags[:, 0] = 7                                     # each row's amax is 6*s
+    signs = rng.choice([-1.0, 1.0], size=(R, L))
+    scale = 2.0 ** rng.integers(-30, 30, size=R)
+    X = (np.array(GRID)[mags] * signs * scale[:, None]).astype(np.float32)
+    codes, s = O.quantize_rows(X)
+    assert np.array_equal(s, scale.astype(np.float32))
+    back = O.decode(codes) * s[:, None].astype(np.float64)
+    assert np.array_equal(back, X.astype(np.float64))
+
+
+def test_zero_and_subnormal_rows():
+    """amax = 0: every code is +0/-0 with scale 0; subnormal amax: inv = Inf (R3, R4)."""
+    X = np.zeros((2, 8), dtype=np.float32)
+    X[1, :] = -0.0
+    codes, s = O.quantize_rows(X)
+    assert np.all(s == 0)
+    assert np.all(codes[0] == 0) and np.all(codes[1] == 8)
+    tiny = np.array([[1e-45, -1e-45, 0.0, 3e-45]], dtype=np.float32)
+    codes, s = O.quantize_rows(tiny)
+    assert s[0] == np.float32(3e-45 / 6)  # rounds to 0 or the smallest subnormal
+    assert list(codes[0]) == [7, 15, 0, 7]
+
+
+# ---------------------------------------------------------------------------
+# Threshold: full sort and order-statistic invariants
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("q", [0.0, 0.5, 0.9, 0.99, 0.999, 1.0])
+def test_threshold_against_full_sort(q):
+    L = wl.make_layer("tiny")
+    A = L.A.f32
+    tau, k = O.select_threshold(A, q)
+    srt = np.sort(np.abs(A).ravel())
+    assert k == min(max(math.ceil(q * A.size) - 1, 0), A.size - 1)
+    assert tau == srt[k]
+    absA = np.abs(A)
+    assert np.count_nonzero(absA < tau) <= k < np.count_nonzero(absA <= tau)
+    perm = np.random.default_rng(1).permutation(A.size)
+    tau_p, _ = O.select_threshold(A.ravel()[perm].reshape(A.shape), q)
+    assert tau_p == tau
+
+
+def test_quantile_one_clamps_nothing():
+    L = wl.make_layer("tiny")
+    tau, _ = O.select_threshold(L.A.f32, 1.0)
+    assert tau == np.abs(L.A.f32).max()
+    _, d = O.clamp_and_residual(L.A.f32, tau)
+    assert d.nnz == 0
+
+
+def test_threshold_bf16_slice_against_sort():
+    """A slice of the 1.3B-like workload (bf16 data, many ties at tau)."""
+    L = wl.make_layer("llama1.3b_ffn_up", M=256)
+    A = L.A.f32
+    tau, k = O.select_threshold(A, 0.99)
+    assert tau == np.sort(np.abs(A).ravel())[k]
+
+
+# ---------------------------------------------------------------------------
+# Delta A: support, exact reconstruction, rounding of the stored values
+# ---------------------------------------------------------------------------
+def test_delta_support_and_exact_reconstruction():
+    L = wl.make_layer("tiny")
+    A = L.A.f32
+    tau, k = O.select_threshold(A, L.q)
+    A_c, d = O.clamp_and_residual(A, tau)
+    C = np.abs(A) > tau
+    dense = np.zeros(A.shape, dtype=bool)
+    dense[d.row, d.col] = True
+    assert np.array_equal(dense, C)                          # non-zero exactly on C
+    assert d.nnz <= A.size - 1 - k
+    order = d.row.astype(np.int64) * A.shape[1] + d.col
+    assert np.all(np.diff(order) > 0)                        # row-major, no duplicates
+    assert np.all(np.abs(A_c) <= tau)
+    # A_c + Delta A == A exactly, per entry, in rationals
+    for r, c, v in zip(d.row[:200], d.col[:200], d.val64[:200]):
+        assert Fraction(float(A_c[r, c])) + Fraction(float(v)) == Fraction(float(A[r, c]))
+        assert np.sign(v) == np.sign(A[r, c])
+    # the float32 values are the correctly rounded differences
+    for r, c, v32 in zip(d.row, d.col, d.val32):
+        a = Fraction(float(A[r, c]))
+        exact = a - (Fraction(float(tau)) if a > 0 else -Fraction(float(tau)))
+        assert v32 == _rn32_fraction(exact)
+    assert np.array_equal(np.diff(d.row_ptr), np.count_nonzero(C, axis=1))
+
+
+# ---------------------------------------------------------------------------
+# Products: closed forms
+# ---------------------------------------------------------------------------
+def _grid_exact(rng, R, L, axis):
+    """R x L matrix whose rows (axis=1) or columns (axis=0) are power-of-two
+    multiples of E2M1 grid values, each vector reaching 6*s."""
+    mags = rng.integers(0, 8, size=(R, L))
+    if axis == 1:
+        mags[:, rng.integers(0, L)] = 7
+        sc = 2.0 ** rng.integers(-6, 6, size=(R, 1))
+    else:
+        mags[rng.integers(0, R), :] = 7
+        sc = 2.0 ** rng.integers(-6, 6, size=(1, L))
+    signs = rng.choice([-1.0, 1.0], size=(R, L))
+    return (np.array(GRID)[mags] * signs * sc).astype(np.float32)
+
+
+def test_forward_equals_plain_product_on_grid_exact_inputs():
+    """q = 1 (nothing clamped) and grid-exact A rows / W columns: Y = A W exactly.
+    Non-square shapes catch a transposed operand or swapped scale axis."""
+    rng = np.random.default_rng(11)
+    M, K, N = 37, 150, 23
+    A = _grid_exact(rng, M, K, axis=1)
+    W = _grid_exact(rng, K, N, axis=0)
+    Y, ops = O.forward(A, W, 1.0)
+    assert ops.delta.nnz == 0
+    assert np.array_equal(Y, A.astype(np.float64) @ W.astype(np.float64))
+
+
+def test_integer_product_against_int64():
+    rng = np.random.default_rng(2)
+    ca = rng.integers(0, 16, size=(20, 333)).astype(np.uint8)
+    cb = rng.integers(0, 16, size=(9, 333)).astype(np.uint8)
+    twice = np.array([0, 1, 2, 3, 4, 6, 8, 12], dtype=np.int64)
+    ia = np.where(ca & 8, -1, 1) * twice[ca & 7]
+    ib = np.where(cb & 8, -1, 1) * twice[cb & 7]
+    ref = np.zeros((20, 9), dtype=np.int64)
+    for i in range(20):
+        for j in range(9):
+            ref[i, j] = int(np.sum(ia[i] * ib[j]))
+    assert np.array_equal(O.integer_product(ca, cb) * 4, ref.astype(np.float64))
+
+
+def test_compensation_equals_dense_residual():
+    """The sparse term equals (A - A_clamped) W computed densely."""
+    L = wl.make_layer("tiny")
+    A, W = L.A.f32, L.W.f32
+    Y, ops = O.forward(A, W, L.q)
+    dense = (A.astype(np.float64) - ops.A_c.astype(np.float64)) @ W.astype(np.float64)
+    sparse = O.sparse_times_dense(ops.delta, W)
+    assert O.rel_fro(sparse, dense) < 1e-13
+    quant = O.scaled_product(O.integer_product(ops.codesA, ops.codesW), ops.sA, ops.sW)
+    assert O.rel_fro(Y, quant + dense) < 1e-13
+    # the layer output approximates A W (FP4 error, outliers compensated)
+    exact = A.astype(np.float64) @ W.astype(np.float64)
+    assert O.rel_fro(Y, exact) < 0.25
+
+
+def test_dgrad_closed_form():
+    """dY rows and W rows grid-exact: Q(dY) Q(W)^T == dY W^T exactly (R9)."""
+    rng = np.random.default_rng(4)
+    M, N, K = 19, 260, 13
+    dY = _grid_exact(rng, M, N, axis=1)
+    W = _grid_exact(rng, K, N, axis=1)
+    dX, _, _ = O.dgrad(dY, W)
+    assert np.array_equal(dX, dY.astype(np.float64) @ W.astype(np.float64).T)
+
+
+# ---------------------------------------------------------------------------
+# A hand-worked example (values derived by hand from the definitions)
+# ---------------------------------------------------------------------------
+def test_hand_worked_example():
+    A = np.array([[1.0, -3.0, 0.5, 12.0],
+                  [-0.25, 2.0, -6.0, 0.0]], dtype=np.float32)
+    W = np.array([[1.0, 2.0],
+                  [0.5, -1.0],
+                  [-2.0, 0.25],
+                  [3.0, 0.0]], dtype=np.float32)
+    q = 0.75
+    # n = 8, k = ceil(6) - 1 = 5; sorted |A| = 0,.25,.5,1,2,3,6,12 -> tau = 3
+    Y, ops = O.forward(A, W, q)
+    assert ops.k == 5 and ops.tau == 3.0
+    # strict clamp: -3.0 (== tau) is not clamped; 12 -> 3 (+9), -6 -> -3 (-3)
+    assert list(ops.delta.row) == [0, 1] and list(ops.delta.col) == [3, 2]
+    assert list(ops.delta.val32) == [9.0, -3.0]
+    assert list(ops.delta.row_ptr) == [0, 1, 2]
+    # rows: amax 3 -> s = 0.5, inv = 2; y row0 = 2,6,1,6; row1 = .5,4,6,0
+    assert list(ops.sA) == [0.5, 0.5]
+    assert ops.codesA.tolist() == [[4, 15, 2, 7], [9, 6, 15, 0]]
+    # W col0 amax 3 -> y = 2,1,4,6; col1 amax 2 -> inv = 3, y = 6,3,0.75(tie->1),0
+    assert ops.sW[0] == 0.5 and ops.sW[1] == np.float32(1.0 / 3.0)
+    assert ops.codesW.tolist() == [[4, 2, 14, 7], [7, 13, 2, 0]]
+    # packing: even index in the low nibble, rows padded to 64 bytes
+    assert ops.Aq.shape == (2, 64) and ops.Wq.shape == (2, 64)
+    assert list(ops.Aq[0, :2]) == [0xF4, 0x72] and list(ops.Aq[1, :2]) == [0x69, 0x0F]
+    assert list(ops.Wq[0, :2]) == [0x24, 0x7E] and list(ops.Wq[1, :2]) == [0xD7, 0x02]
+    assert not ops.Aq[:, 2:].any() and not ops.Wq[:, 2:].any()
+    # acc = [[30, 31], [27, -21]]; Y = acc*sA*sW + dA W
+    s1 = float(np.float32(1.0 / 3.0))
+    want = np.array([[30 * 0.25 + 27.0, 31 * 0.5 * s1 + 0.0],
+                     [27 * 0.25 + 6.0, -21 * 0.5 * s1 - 0.75]])
+    assert np.array_equal(Y, want)
+    # column 0 is quantized without error, so it equals the exact product
+    assert Y[0, 0] == 34.5 and Y[1, 0] == 12.75
+
+
+def test_pack_layout():
+    codes = np.arange(16, dtype=np.uint8)[None, :].repeat(3, axis=0)
+    p = O.pack_rows(codes)
+    assert p.shape == (3, 64)
+    assert list(p[0, :8]) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    assert np.array_equal(O.unpack_rows(p, 16), codes)
+    assert O.packed_ld(1) == 64 and O.packed_ld(128) == 64 and O.packed_ld(129) == 128
+
+
+def test_quantile_rank_edges():
+    assert O.quantile_rank(8, 0.75) == 5
+    assert O.quantile_rank(8, 0.0) == 0
+    assert O.quantile_rank(8, 1.0) == 7
+    assert O.quantile_rank(1, 0.5) == 0
+    assert O.quantile_rank(100, 0.99) == 98
+    assert O.quantile_rank(131072, 0.99) == 129761
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        np.array([1.00390625, 1.01171875, -2.00781250, 3e-39, -0.0],
+                                 dtype=np.float32)])
+    ours = wl.f32_to_bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+
+
+def test_golden_tiny_fixture():
+    """The oracle still reproduces the frozen tiny-workload fixture."""
+    import hashlib
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_forward.json")
+    g = json.load(open(path))
+    L = wl.make_layer("tiny", seed=0)
+    Y, ops = O.forward(L.A.f32, L.W.f32, L.q)
+    h = lambda a: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+    assert ops.k == g["k"] and ops.delta.nnz == g["nnz"]
+    assert int(np.float32(ops.tau).view(np.uint32)) == g["tau_bits"]
+    assert h(ops.Aq) == g["Aq_sha256"] and h(ops.Wq) == g["Wq_sha256"]
+    assert h(ops.sA.astype(np.float32)) == g["sA_sha256"]
+    assert h(ops.sW.astype(np.float32)) == g["sW_sha256"]
+    assert h(ops.delta.row_ptr.astype(np.int32)) == g["row_ptr_sha256"]
+    assert h(ops.delta.val32.astype(np.float32)) == g["coo_val32_sha256"]
+    assert abs(float(np.linalg.norm(Y)) - g["Y_fro"]) <= 1e-9 * g["Y_fro"]
