@@ -1,0 +1,215 @@
+// C ABI of libfp4lin.so: argument checks, workspace layout and launches.
+// Every check runs on the host before anything is enqueued; no call allocates,
+// frees, synchronises or reads device memory.
+#include <cmath>
+#include <cstdint>
+
+#include "fp4lin.h"
+#include "internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+bool bad_dtype(fp4lin_dtype dt) { return dt != FP4LIN_F32 && dt != FP4LIN_BF16; }
+bool ok_dim(int64_t x) { return x >= 1 && x < kMaxDim; }
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+fp4lin_status launch_status(hipError_t e) { return e == hipSuccess ? FP4LIN_OK : FP4LIN_ERR_LAUNCH; }
+
+// COO entries the select can produce for rank k: #{|a| > tau} <= n - 1 - k.
+int64_t needed_capacity(int64_t n, int64_t k) { return n - 1 - k; }
+
+size_t weight_ws(int64_t N) { return round_up(fp4lin::weight_workspace_bytes(N), 256); }
+
+size_t select_ws(fp4lin_dtype dt) {
+  return round_up(fp4lin::select_workspace_bytes(dt == FP4LIN_BF16), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t fp4lin_quantile_rank(int64_t n, double q) {
+  if (n < 1 || !(q >= 0.0 && q <= 1.0)) return -1;
+  const double c = std::ceil(q * double(n));
+  int64_t k = int64_t(c) - 1;
+  if (k < 0) k = 0;
+  if (k > n - 1) k = n - 1;
+  return k;
+}
+
+int64_t fp4lin_packed_ld(int64_t L) {
+  if (L < 1) return -1;
+  return (L + 127) / 128 * 64;
+}
+
+size_t fp4lin_select_workspace_bytes(int64_t M, int64_t K, fp4lin_dtype dt) {
+  if (!ok_dim(M) || !ok_dim(K) || bad_dtype(dt)) return 0;
+  return select_ws(dt);
+}
+
+size_t fp4lin_weight_workspace_bytes(int64_t K, int64_t N) {
+  if (!ok_dim(K) || !ok_dim(N)) return 0;
+  return weight_ws(N);
+}
+
+fp4lin_status fp4lin_forward_layout(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt, double q,
+                                    fp4lin_forward_offsets* out) {
+  if (out == nullptr) return FP4LIN_ERR_NULL;
+  if (!ok_dim(M) || !ok_dim(K) || !ok_dim(N)) return FP4LIN_ERR_SHAPE;
+  if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
+  const int64_t n = M * K;
+  const int64_t k = fp4lin_quantile_rank(n, q);
+  if (k < 0) return FP4LIN_ERR_QUANTILE;
+  const int64_t cap = needed_capacity(n, k);
+  if (cap >= kMaxDim) return FP4LIN_ERR_SHAPE;
+  const size_t slots = size_t(cap > 0 ? cap : 1);
+  const size_t ldq = size_t(fp4lin_packed_ld(K));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  fp4lin_forward_offsets o{};
+  o.tau = take(4);
+  o.coo_row = take(slots * 4);
+  o.coo_col = take(slots * 4);
+  o.coo_val = take(slots * 4);
+  o.row_ptr = take(size_t(M + 1) * 4);
+  o.Aq = take(size_t(M) * ldq);
+  o.sA = take(size_t(M) * 4);
+  o.Wq = take(size_t(N) * ldq);
+  o.sW = take(size_t(N) * 4);
+  const size_t sws = select_ws(dt), wws = weight_ws(N);
+  o.scratch = take(sws > wws ? sws : wws);
+  o.capacity = cap;
+  o.total = off;
+  *out = o;
+  return FP4LIN_OK;
+}
+
+size_t fp4lin_workspace_bytes(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt, double q) {
+  fp4lin_forward_offsets o;
+  if (fp4lin_forward_layout(M, K, N, dt, q, &o) != FP4LIN_OK) return 0;
+  return o.total;
+}
+
+const char* fp4lin_status_str(fp4lin_status s) {
+  switch (s) {
+    case FP4LIN_OK: return "ok";
+    case FP4LIN_ERR_NULL: return "a required pointer is NULL";
+    case FP4LIN_ERR_SHAPE: return "invalid shape or leading dimension";
+    case FP4LIN_ERR_DTYPE: return "unsupported dtype";
+    case FP4LIN_ERR_QUANTILE: return "quantile q must be in [0, 1]";
+    case FP4LIN_ERR_CAPACITY: return "COO capacity below M*K - 1 - k";
+    case FP4LIN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FP4LIN_ERR_WORKSPACE: return "workspace too small";
+    case FP4LIN_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, int64_t K,
+                                    int64_t lda, double q, float* tau, fp4lin_coo dA, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  if (A == nullptr || tau == nullptr || dA.row == nullptr || dA.col == nullptr ||
+      dA.val == nullptr || dA.row_ptr == nullptr || ws == nullptr)
+    return FP4LIN_ERR_NULL;
+  if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
+  if (!ok_dim(M) || !ok_dim(K) || lda < K) return FP4LIN_ERR_SHAPE;
+  const int64_t n = M * K;
+  const int64_t k = fp4lin_quantile_rank(n, q);
+  if (k < 0) return FP4LIN_ERR_QUANTILE;
+  const int64_t cap = needed_capacity(n, k);
+  if (cap >= kMaxDim) return FP4LIN_ERR_SHAPE;
+  if (dA.capacity < cap) return FP4LIN_ERR_CAPACITY;
+  if (!aligned16(ws)) return FP4LIN_ERR_ALIGN;
+  if (ws_bytes < select_ws(dt)) return FP4LIN_ERR_WORKSPACE;
+  return launch_status(fp4lin::launch_outlier_select(A, dt == FP4LIN_BF16, M, K, lda, k, tau,
+                                                     dA.capacity, dA.row, dA.col, dA.val, dA.row_ptr, ws,
+                                                     stream));
+}
+
+fp4lin_status fp4lin_quantize_act(const void* X, fp4lin_dtype dt, int64_t M, int64_t K,
+                                  int64_t ldx, const float* tau, uint8_t* Xq, float* sX,
+                                  hipStream_t stream) {
+  if (X == nullptr || Xq == nullptr || sX == nullptr) return FP4LIN_ERR_NULL;
+  if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
+  if (!ok_dim(M) || !ok_dim(K) || ldx < K) return FP4LIN_ERR_SHAPE;
+  if (!aligned16(Xq)) return FP4LIN_ERR_ALIGN;
+  return launch_status(fp4lin::launch_quantize_rows(X, dt == FP4LIN_BF16, M, K, ldx, tau, Xq,
+                                                    fp4lin_packed_ld(K), sX, stream));
+}
+
+fp4lin_status fp4lin_quantize_weight(const void* W, fp4lin_dtype dt, int64_t K, int64_t N,
+                                     int64_t ldw, uint8_t* Wq, float* sW, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (W == nullptr || Wq == nullptr || sW == nullptr || ws == nullptr) return FP4LIN_ERR_NULL;
+  if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
+  if (!ok_dim(K) || !ok_dim(N) || ldw < N) return FP4LIN_ERR_SHAPE;
+  if (!aligned16(Wq) || !aligned16(ws)) return FP4LIN_ERR_ALIGN;
+  if (ws_bytes < weight_ws(N)) return FP4LIN_ERR_WORKSPACE;
+  return launch_status(fp4lin::launch_quantize_weight(W, dt == FP4LIN_BF16, K, N, ldw, Wq,
+                                                      fp4lin_packed_ld(K), sW, ws, stream));
+}
+
+fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const float* sB,
+                          int64_t M, int64_t N, int64_t K, const fp4lin_coo* dA, const void* W,
+                          fp4lin_dtype wdt, int64_t ldw, float* Y, int64_t ldy,
+                          hipStream_t stream) {
+  if (Aq == nullptr || sA == nullptr || Bq == nullptr || sB == nullptr || Y == nullptr)
+    return FP4LIN_ERR_NULL;
+  if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldy < N) return FP4LIN_ERR_SHAPE;
+  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, false, 0};
+  if (dA != nullptr) {
+    if (dA->row_ptr == nullptr || dA->col == nullptr || dA->val == nullptr || W == nullptr)
+      return FP4LIN_ERR_NULL;
+    if (bad_dtype(wdt)) return FP4LIN_ERR_DTYPE;
+    if (ldw < N) return FP4LIN_ERR_SHAPE;
+    sp = fp4lin::SparseArgs{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw};
+  }
+  if (!aligned16(Aq) || !aligned16(Bq)) return FP4LIN_ERR_ALIGN;
+  return launch_status(
+      fp4lin::launch_fp4_gemm(Aq, sA, Bq, sB, M, N, fp4lin_packed_ld(K), sp, Y, ldy, stream));
+}
+
+fp4lin_status fp4lin_forward(const void* A, const void* W, fp4lin_dtype dt, int64_t M, int64_t K,
+                             int64_t N, int64_t lda, int64_t ldw, double q, float* Y, int64_t ldy,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (A == nullptr || W == nullptr || Y == nullptr || ws == nullptr) return FP4LIN_ERR_NULL;
+  if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
+  if (!ok_dim(M) || !ok_dim(K) || !ok_dim(N) || lda < K || ldw < N || ldy < N)
+    return FP4LIN_ERR_SHAPE;
+  fp4lin_forward_offsets o;
+  const fp4lin_status ls = fp4lin_forward_layout(M, K, N, dt, q, &o);
+  if (ls != FP4LIN_OK) return ls;
+  if (!aligned16(ws)) return FP4LIN_ERR_ALIGN;
+  if (ws_bytes < o.total) return FP4LIN_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  float* tau = reinterpret_cast<float*>(base + o.tau);
+  fp4lin_coo coo;
+  coo.row = reinterpret_cast<int32_t*>(base + o.coo_row);
+  coo.col = reinterpret_cast<int32_t*>(base + o.coo_col);
+  coo.val = reinterpret_cast<float*>(base + o.coo_val);
+  coo.row_ptr = reinterpret_cast<int32_t*>(base + o.row_ptr);
+  coo.capacity = o.capacity;
+  uint8_t* Aq = reinterpret_cast<uint8_t*>(base + o.Aq);
+  float* sA = reinterpret_cast<float*>(base + o.sA);
+  uint8_t* Wq = reinterpret_cast<uint8_t*>(base + o.Wq);
+  float* sW = reinterpret_cast<float*>(base + o.sW);
+  void* scratch = base + o.scratch;
+  const size_t scratch_bytes = o.total - o.scratch;
+  fp4lin_status s =
+      fp4lin_outlier_select(A, dt, M, K, lda, q, tau, coo, scratch, scratch_bytes, stream);
+  if (s != FP4LIN_OK) return s;
+  s = fp4lin_quantize_act(A, dt, M, K, lda, tau, Aq, sA, stream);
+  if (s != FP4LIN_OK) return s;
+  s = fp4lin_quantize_weight(W, dt, K, N, ldw, Wq, sW, scratch, scratch_bytes, stream);
+  if (s != FP4LIN_OK) return s;
+  return fp4lin_gemm(Aq, sA, Wq, sW, M, N, K, &coo, W, dt, ldw, Y, ldy, stream);
+}
+
+}  // extern "C"

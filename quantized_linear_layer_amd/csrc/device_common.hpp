@@ -1,0 +1,138 @@
+// Device helpers shared by the fp4lin kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4lin {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element access. Inputs are float32 or bfloat16 (raw uint16 bits).
+// ---------------------------------------------------------------------------
+struct F32In {
+  using T = float;
+  static constexpr int kBytes = 4;
+  __device__ static inline uint32_t bits(T v) { return __float_as_uint(v); }
+  __device__ static inline float widen(T v) { return v; }
+  // |a| as an order-preserving integer key (finite inputs).
+  __device__ static inline uint32_t key(T v) { return __float_as_uint(v) & 0x7fffffffu; }
+  __device__ static inline float key_to_float(uint32_t k) { return __uint_as_float(k); }
+  __device__ static inline uint32_t sign_bit(T v) { return __float_as_uint(v) >> 31; }
+};
+
+struct BF16In {
+  using T = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ static inline uint32_t bits(T v) { return v; }
+  __device__ static inline float widen(T v) { return __uint_as_float(uint32_t(v) << 16); }
+  __device__ static inline uint32_t key(T v) { return uint32_t(v) & 0x7fffu; }
+  __device__ static inline float key_to_float(uint32_t k) { return __uint_as_float(k << 16); }
+  __device__ static inline uint32_t sign_bit(T v) { return uint32_t(v) >> 15; }
+};
+
+// Eight consecutive elements, loaded with one 16-byte (fp32: two 16-byte)
+// access when the caller has established alignment, else one by one.
+template <class In>
+struct Vec8 {
+  typename In::T v[8];
+};
+
+template <class In, bool kAligned>
+__device__ inline void load8(const typename In::T* __restrict__ p, int64_t valid,
+                             Vec8<In>& out) {
+  if (kAligned && valid >= 8) {
+    if constexpr (In::kBytes == 2) {
+      uint4 u = *reinterpret_cast<const uint4*>(p);
+      out.v[0] = uint16_t(u.x); out.v[1] = uint16_t(u.x >> 16);
+      out.v[2] = uint16_t(u.y); out.v[3] = uint16_t(u.y >> 16);
+      out.v[4] = uint16_t(u.z); out.v[5] = uint16_t(u.z >> 16);
+      out.v[6] = uint16_t(u.w); out.v[7] = uint16_t(u.w >> 16);
+    } else {
+      float4 a = *reinterpret_cast<const float4*>(p);
+      float4 b = *reinterpret_cast<const float4*>(p + 4);
+      out.v[0] = a.x; out.v[1] = a.y; out.v[2] = a.z; out.v[3] = a.w;
+      out.v[4] = b.x; out.v[5] = b.y; out.v[6] = b.z; out.v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out.v[i] = (i < valid) ? p[i] : typename In::T(0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 encoding (round to nearest, ties away from zero, saturating at 6).
+//
+// The magnitude index of y >= 0 is the number of midpoints
+// {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5} that y reaches. Multiplying by 4 (exact)
+// turns the midpoints into the integers {1, 3, 5, 7, 10, 14, 20}, so
+// "y >= t" is "floor(4y) >= 4t" and the index is a table lookup on
+// n = min(floor(4y), 20). The 21 three-bit entries live in one 64-bit constant.
+// v_cvt_u32_f32 truncates, saturates large values and +Inf to 0xffffffff and
+// turns NaN (0 * Inf when a vector's amax is 0) into 0, which the lookup maps
+// to magnitude 0, exactly as the threshold count does.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr uint64_t e2m1_lut() {
+  uint64_t lut = 0;
+  for (int n = 0; n <= 20; ++n) {
+    int idx = (n >= 1) + (n >= 3) + (n >= 5) + (n >= 7) + (n >= 10) + (n >= 14) + (n >= 20);
+    lut |= uint64_t(idx) << (3 * n);
+  }
+  return lut;
+}
+
+__device__ inline uint32_t cvt_u32_sat(float x) {
+  uint32_t r;
+  asm("v_cvt_u32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Magnitude index of y = RN32(ax * inv).
+__device__ inline uint32_t e2m1_magnitude(float ax, float inv) {
+  float y = __fmul_rn(ax, inv);
+  float y4 = __fmul_rn(y, 4.0f);
+  uint32_t n = cvt_u32_sat(y4);
+  n = n < 20u ? n : 20u;
+  return uint32_t(e2m1_lut() >> (3u * n)) & 7u;
+}
+
+// Per-vector scale and encode multiplier from the vector's amax:
+// s = RN32(amax/6), inv = RN32(6/amax). The quotients are formed in double and
+// rounded once to float; double has more than 2*24+2 bits, so the result is
+// the correctly rounded float quotient.
+__device__ inline void vector_scale(float amax, float& s, float& inv) {
+  double a = double(amax);
+  s = float(a / 6.0);
+  inv = float(6.0 / a);
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions.
+// ---------------------------------------------------------------------------
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Exclusive prefix sum across the wave.
+__device__ inline uint32_t wave_exclusive_scan(uint32_t v, uint32_t& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  total = __shfl(x, kWave - 1, kWave);
+  return x - v;
+}
+
+}  // namespace fp4lin

@@ -1,0 +1,206 @@
+"""Host-side checks of the C ABI (no GPU needed, no device work is launched).
+
+Every call here either is a pure host helper or fails argument validation,
+which the library performs before it touches the HIP runtime.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4lin.h")
+
+qll = pytest.importorskip("quantized_linear_layer_amd")
+from quantized_linear_layer_amd import _lib  # noqa: E402
+
+if not os.path.exists(_lib.LIB_PATH):
+    pytest.skip("libfp4lin.so not built (run __graft_entry__.build())", allow_module_level=True)
+
+L = _lib.load()
+P = ctypes.c_void_p
+FAKE = P(0x10000)        # 16-byte aligned, never dereferenced (validation fails first)
+MISALIGNED = P(0x10004)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4lin_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (fp4lin_\w+)", out))
+    assert set(names) <= exported
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 100, 131072, 33554432, 84 * 2 ** 20 + 3])
+@pytest.mark.parametrize("q", [0.0, 1e-9, 0.25, 0.5, 0.9, 0.99, 0.999, 0.9999999, 1.0])
+def test_quantile_rank_matches_oracle(n, q):
+    assert L.fp4lin_quantile_rank(n, q) == O.quantile_rank(n, q)
+
+
+def test_quantile_rank_invalid():
+    for n, q in [(0, 0.5), (-1, 0.5), (10, -0.01), (10, 1.01), (10, math.nan), (10, math.inf)]:
+        assert L.fp4lin_quantile_rank(n, q) == -1
+
+
+@pytest.mark.parametrize("K", [1, 2, 127, 128, 129, 512, 4095, 4096, 5120, 13824, 15360])
+def test_packed_ld_matches_oracle(K):
+    assert L.fp4lin_packed_ld(K) == O.packed_ld(K)
+    assert L.fp4lin_packed_ld(K) % 64 == 0
+
+
+def test_packed_ld_invalid():
+    assert L.fp4lin_packed_ld(0) == -1
+
+
+def test_workspace_layout_consistent():
+    for (M, K, N, dt, q) in [(256, 512, 512, 0, 0.99), (8192, 4096, 11008, 1, 0.99),
+                             (3, 5, 7, 1, 1.0), (16384, 5120, 15360, 1, 0.99)]:
+        o = _lib.ForwardOffsets()
+        assert L.fp4lin_forward_layout(M, K, N, dt, q, ctypes.byref(o)) == 0
+        k = O.quantile_rank(M * K, q)
+        assert o.capacity == M * K - 1 - k
+        ldq = O.packed_ld(K)
+        regions = sorted([
+            (o.tau, 4), (o.coo_row, 4 * max(o.capacity, 1)), (o.coo_col, 4 * max(o.capacity, 1)),
+            (o.coo_val, 4 * max(o.capacity, 1)), (o.row_ptr, 4 * (M + 1)), (o.Aq, M * ldq),
+            (o.sA, 4 * M), (o.Wq, N * ldq), (o.sW, 4 * N),
+            (o.scratch, max(L.fp4lin_select_workspace_bytes(M, K, dt),
+                            L.fp4lin_weight_workspace_bytes(K, N)))])
+        for (a, na), (b, _) in zip(regions, regions[1:]):
+            assert a + na <= b                       # no overlap
+        for off, _ in regions:
+            assert off % 256 == 0                    # every region 256-byte aligned
+        assert regions[-1][0] + regions[-1][1] <= o.total
+        assert L.fp4lin_workspace_bytes(M, K, N, dt, q) == o.total
+    assert L.fp4lin_workspace_bytes(0, 5, 7, 1, 0.5) == 0
+    assert L.fp4lin_workspace_bytes(3, 5, 7, 9, 0.5) == 0
+    assert L.fp4lin_workspace_bytes(3, 5, 7, 1, 2.0) == 0
+
+
+def test_status_strings():
+    for s in range(9):
+        assert len(L.fp4lin_status_str(s)) > 0
+    assert L.fp4lin_status_str(99) == b"unknown status"
+
+
+# ---- validation errors (nothing is launched) ---------------------------------------
+def coo(cap, null=None):
+    f = {k: FAKE.value for k in ("row", "col", "val", "row_ptr")}
+    if null:
+        f[null] = None
+    return _lib.Coo(f["row"], f["col"], f["val"], f["row_ptr"], cap)
+
+
+def select(A=FAKE, dt=1, M=4, K=8, lda=8, q=0.5, tau=FAKE, dA=None, ws=FAKE, wsb=1 << 20):
+    dA = coo(100) if dA is None else dA
+    return L.fp4lin_outlier_select(A, dt, M, K, lda, q, tau, dA, ws, wsb, None)
+
+
+def test_select_errors():
+    assert select(A=None) == _lib.ERR_NULL
+    assert select(tau=None) == _lib.ERR_NULL
+    for fld in ("row", "col", "val", "row_ptr"):
+        assert select(dA=coo(100, null=fld)) == _lib.ERR_NULL
+    assert select(ws=None) == _lib.ERR_NULL
+    assert select(dt=5) == _lib.ERR_DTYPE
+    assert select(M=0) == _lib.ERR_SHAPE
+    assert select(K=-1) == _lib.ERR_SHAPE
+    assert select(lda=7) == _lib.ERR_SHAPE
+    assert select(M=2 ** 31) == _lib.ERR_SHAPE
+    assert select(q=-0.5) == _lib.ERR_QUANTILE
+    assert select(q=float("nan")) == _lib.ERR_QUANTILE
+    # n = 32, q = 0.5 -> k = 15, capacity needed 16
+    assert select(dA=coo(15)) == _lib.ERR_CAPACITY
+    assert select(ws=MISALIGNED) == _lib.ERR_ALIGN
+    assert select(wsb=16) == _lib.ERR_WORKSPACE
+
+
+def quant_act(X=FAKE, dt=1, M=4, K=8, ldx=8, tau=None, Xq=FAKE, sX=FAKE):
+    return L.fp4lin_quantize_act(X, dt, M, K, ldx, tau, Xq, sX, None)
+
+
+def test_quantize_act_errors():
+    assert quant_act(X=None) == _lib.ERR_NULL
+    assert quant_act(Xq=None) == _lib.ERR_NULL
+    assert quant_act(sX=None) == _lib.ERR_NULL
+    assert quant_act(dt=2) == _lib.ERR_DTYPE
+    assert quant_act(M=0) == _lib.ERR_SHAPE
+    assert quant_act(ldx=7) == _lib.ERR_SHAPE
+    assert quant_act(Xq=MISALIGNED) == _lib.ERR_ALIGN
+
+
+def quant_w(W=FAKE, dt=1, K=8, N=4, ldw=4, Wq=FAKE, sW=FAKE, ws=FAKE, wsb=1 << 20):
+    return L.fp4lin_quantize_weight(W, dt, K, N, ldw, Wq, sW, ws, wsb, None)
+
+
+def test_quantize_weight_errors():
+    assert quant_w(W=None) == _lib.ERR_NULL
+    assert quant_w(ws=None) == _lib.ERR_NULL
+    assert quant_w(dt=-1) == _lib.ERR_DTYPE
+    assert quant_w(N=0) == _lib.ERR_SHAPE
+    assert quant_w(ldw=3) == _lib.ERR_SHAPE
+    assert quant_w(Wq=MISALIGNED) == _lib.ERR_ALIGN
+    assert quant_w(ws=MISALIGNED) == _lib.ERR_ALIGN
+    assert quant_w(wsb=4) == _lib.ERR_WORKSPACE
+
+
+def gemm(Aq=FAKE, sA=FAKE, Bq=FAKE, sB=FAKE, M=4, N=4, K=8, dA=None, W=None, wdt=1, ldw=4,
+         Y=FAKE, ldy=4):
+    p = ctypes.byref(dA) if dA is not None else None
+    return L.fp4lin_gemm(Aq, sA, Bq, sB, M, N, K, p, W, wdt, ldw, Y, ldy, None)
+
+
+def test_gemm_errors():
+    assert gemm(Aq=None) == _lib.ERR_NULL
+    assert gemm(sB=None) == _lib.ERR_NULL
+    assert gemm(Y=None) == _lib.ERR_NULL
+    assert gemm(dA=coo(10), W=None) == _lib.ERR_NULL
+    for fld in ("col", "val", "row_ptr"):
+        assert gemm(dA=coo(10, null=fld), W=FAKE) == _lib.ERR_NULL
+    assert gemm(dA=coo(10), W=FAKE, wdt=3) == _lib.ERR_DTYPE
+    assert gemm(dA=coo(10), W=FAKE, ldw=3) == _lib.ERR_SHAPE
+    assert gemm(K=0) == _lib.ERR_SHAPE
+    assert gemm(ldy=3) == _lib.ERR_SHAPE
+    assert gemm(Aq=MISALIGNED) == _lib.ERR_ALIGN
+    assert gemm(Bq=MISALIGNED) == _lib.ERR_ALIGN
+
+
+def forward(A=FAKE, W=FAKE, dt=1, M=4, K=8, N=4, lda=8, ldw=4, q=0.5, Y=FAKE, ldy=4, ws=FAKE,
+            wsb=1 << 30):
+    return L.fp4lin_forward(A, W, dt, M, K, N, lda, ldw, q, Y, ldy, ws, wsb, None)
+
+
+def test_forward_errors():
+    assert forward(A=None) == _lib.ERR_NULL
+    assert forward(W=None) == _lib.ERR_NULL
+    assert forward(ws=None) == _lib.ERR_NULL
+    assert forward(dt=4) == _lib.ERR_DTYPE
+    assert forward(N=0) == _lib.ERR_SHAPE
+    assert forward(lda=2) == _lib.ERR_SHAPE
+    assert forward(ldy=1) == _lib.ERR_SHAPE
+    assert forward(q=1.5) == _lib.ERR_QUANTILE
+    assert forward(ws=MISALIGNED) == _lib.ERR_ALIGN
+    need = L.fp4lin_workspace_bytes(4, 8, 4, 1, 0.5)
+    assert forward(wsb=need - 1) == _lib.ERR_WORKSPACE
+
+
+def test_python_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    A = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qll.quantize_act(A)

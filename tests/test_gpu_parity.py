@@ -1,0 +1,454 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on seeded inputs,
+small enough for the oracle to finish in seconds but spanning several tiles
+and ragged tails, plus adversarial matrices (every bfloat16 value, exact
+midpoints, zero / negative-zero / subnormal rows, ties at the threshold,
+padded and unaligned leading dimensions).
+
+Bit-exact: codes, scales, tau, COO (row, col, val, row_ptr).
+Y: relative Frobenius error <= 1e-5 (fp32 accumulation order and the
+float32 rounding of the compensation values; the exact integer GEMM core is
+checked bit-exactly with unit scales).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as wl
+from gpu_util import assert_bits_equal, host, log, padded, to_device
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def ql():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_linear_layer_amd as q
+    q.lib()
+    return q
+
+
+def torch():
+    import torch as t
+    return t
+
+
+# ---------------------------------------------------------------------------
+# input builders
+# ---------------------------------------------------------------------------
+def midpoint_rows(dtype, rows=64, K=200, seed=0):
+    """Rows whose amax is 6*2^e (inv exact) and whose entries sit on E2M1
+    midpoints, grid points and their float neighbours."""
+    rng = np.random.default_rng(seed)
+    base = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1, 1.5, 2, 3, 4, 6, 0.0],
+                    dtype=np.float32)
+    vals = rng.choice(base, size=(rows, K)).astype(np.float32)
+    if dtype == wl.F32:
+        nudge = rng.integers(-1, 2, size=(rows, K))
+        up = np.nextafter(vals, np.float32(10))
+        dn = np.nextafter(vals, np.float32(0))
+        vals = np.where(nudge > 0, up, np.where(nudge < 0, dn, vals)).astype(np.float32)
+    vals[:, 0] = 6.0
+    vals = np.minimum(vals, np.float32(6.0))
+    signs = rng.choice([-1.0, 1.0], size=(rows, K)).astype(np.float32)
+    scale = (2.0 ** rng.integers(-20, 20, size=(rows, 1))).astype(np.float32)
+    return wl.from_f32(vals * signs * scale, dtype)
+
+
+def all_bf16_scaled_rows():
+    """Every non-negative bf16 value <= 6 (and its negative) in rows of amax 6:
+    inv = 1, so y equals the value itself."""
+    b = np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    v = wl.bf16_bits_to_f32(b)
+    v = v[v <= 6.0]
+    allv = np.concatenate([v, -v])
+    K = 256
+    R = int(np.ceil(allv.size / (K - 1)))
+    out = np.zeros((R, K), dtype=np.float32)
+    flat = np.zeros(R * (K - 1), dtype=np.float32)
+    flat[: allv.size] = allv
+    out[:, 1:] = flat.reshape(R, K - 1)
+    out[:, 0] = 6.0
+    return wl.from_f32(out, wl.BF16)
+
+
+def special_rows(dtype):
+    """Zero, negative-zero, subnormal and single-value rows."""
+    K = 300
+    rows = [np.zeros(K, np.float32), np.full(K, -0.0, np.float32)]
+    sub = np.zeros(K, np.float32)
+    if dtype == wl.F32:
+        sub[::3] = np.float32(1e-45)
+        sub[1::7] = np.float32(-3e-42)
+        sub[5] = np.float32(1e-39)
+    else:
+        sub[::3] = wl.bf16_bits_to_f32(np.array([1], np.uint16))[0]       # smallest subnormal
+        sub[1::7] = -wl.bf16_bits_to_f32(np.array([0x50], np.uint16))[0]
+    rows.append(sub)
+    one = np.zeros(K, np.float32)
+    one[123] = -7.0
+    rows.append(one)
+    mixed = np.linspace(-3, 3, K).astype(np.float32)
+    mixed[::2] = -0.0
+    rows.append(mixed)
+    return wl.from_f32(np.stack(rows), dtype)
+
+
+# ---------------------------------------------------------------------------
+# quantize_act (token-wise)
+# ---------------------------------------------------------------------------
+def check_quantize_act(ql, X: wl.Matrix, tau=None, ld=None):
+    t = torch()
+    Xd = to_device(X)
+    if ld is not None:
+        Xd = padded(Xd, ld)
+    taud = None if tau is None else t.tensor([float(tau)], dtype=t.float32, device="cuda:0")
+    Xq, sX = ql.quantize_act(Xd, taud)
+    t.cuda.synchronize()
+    want_q, want_s, _ = O.quantize_act(X.f32, tau)
+    assert_bits_equal(host(sX), want_s, "scales")
+    assert_bits_equal(host(Xq), want_q, "packed codes")
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("M,K", [(1, 1), (3, 7), (5, 127), (4, 128), (9, 129), (37, 1000),
+                                 (70, 2051)])
+def test_quantize_act_shapes(ql, dtype, M, K):
+    log(f"quantize_act {dtype} {M}x{K}")
+    rng = np.random.default_rng(M * 1000 + K)
+    X = wl.random_matrix(rng, M, K, dtype, dist="t3")
+    check_quantize_act(ql, X)
+    tau, _ = O.select_threshold(X.f32, 0.9)
+    check_quantize_act(ql, X, tau)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_quantize_act_midpoints(ql, dtype):
+    check_quantize_act(ql, midpoint_rows(dtype))
+
+
+def test_quantize_act_every_bf16_value(ql):
+    check_quantize_act(ql, all_bf16_scaled_rows())
+    check_quantize_act(ql, wl.all_bf16_values_matrix(256))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_quantize_act_special_rows(ql, dtype):
+    X = special_rows(dtype)
+    check_quantize_act(ql, X)
+    check_quantize_act(ql, X, tau=np.float32(0.0))
+    check_quantize_act(ql, X, tau=np.float32(1.0))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_quantize_act_leading_dimension(ql, dtype):
+    rng = np.random.default_rng(9)
+    X = wl.random_matrix(rng, 33, 250, dtype)
+    check_quantize_act(ql, X, ld=264)   # aligned, padded
+    check_quantize_act(ql, X, ld=251)   # unaligned rows -> element loads
+
+
+def test_quantize_act_tiny_workload(ql):
+    L = wl.make_layer("tiny")
+    tau, _ = O.select_threshold(L.A.f32, L.q)
+    check_quantize_act(ql, L.A, tau)
+
+
+# ---------------------------------------------------------------------------
+# quantize_weight (channel-wise, packed N-major)
+# ---------------------------------------------------------------------------
+def check_quantize_weight(ql, W: wl.Matrix, ld=None):
+    t = torch()
+    Wd = to_device(W)
+    if ld is not None:
+        Wd = padded(Wd, ld)
+    Wq, sW = ql.quantize_weight(Wd)
+    t.cuda.synchronize()
+    want_q, want_s, _ = O.quantize_weight(W.f32)
+    assert_bits_equal(host(sW), want_s, "scales")
+    assert_bits_equal(host(Wq), want_q, "packed codes")
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("K,N", [(1, 1), (1, 1000), (129, 1), (300, 70), (512, 520),
+                                 (1000, 77)])
+def test_quantize_weight_shapes(ql, dtype, K, N):
+    log(f"quantize_weight {dtype} {K}x{N}")
+    rng = np.random.default_rng(K * 7 + N)
+    check_quantize_weight(ql, wl.random_matrix(rng, K, N, dtype, scale=0.02))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_quantize_weight_adversarial(ql, dtype):
+    X = midpoint_rows(dtype, rows=40, K=300)
+    check_quantize_weight(ql, wl.from_f32(X.f32.T.copy(), dtype))
+    S = special_rows(dtype)
+    check_quantize_weight(ql, wl.from_f32(S.f32.T.copy(), dtype))
+
+
+def test_quantize_weight_every_bf16_value(ql):
+    X = all_bf16_scaled_rows()
+    check_quantize_weight(ql, wl.from_f32(X.f32.T.copy(), wl.BF16))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_quantize_weight_leading_dimension(ql, dtype):
+    rng = np.random.default_rng(5)
+    W = wl.random_matrix(rng, 200, 90, dtype)
+    check_quantize_weight(ql, W, ld=96)
+    check_quantize_weight(ql, W, ld=91)
+
+
+# ---------------------------------------------------------------------------
+# outlier_select (tau + COO)
+# ---------------------------------------------------------------------------
+def run_select(ql, A: wl.Matrix, q, ld=None):
+    t = torch()
+    Ad = to_device(A)
+    if ld is not None:
+        Ad = padded(Ad, ld)
+    tau, coo = ql.outlier_select(Ad, q)
+    t.cuda.synchronize()
+    return tau, coo
+
+
+def check_select(ql, A: wl.Matrix, q, ld=None):
+    tau, coo = run_select(ql, A, q, ld)
+    want_tau, k = O.select_threshold(A.f32, q)
+    _, d = O.clamp_and_residual(A.f32, want_tau)
+    assert_bits_equal(host(tau)[0], want_tau, "tau")
+    rp = host(coo.row_ptr)
+    assert_bits_equal(rp, d.row_ptr.astype(np.int32), "row_ptr")
+    nnz = int(rp[-1])
+    assert nnz == d.nnz
+    assert_bits_equal(host(coo.row)[:nnz], d.row, "coo row")
+    assert_bits_equal(host(coo.col)[:nnz], d.col, "coo col")
+    assert_bits_equal(host(coo.val)[:nnz], d.val32, "coo val")
+    return tau, coo
+
+
+@pytest.mark.parametrize("q", [0.0, 0.3, 0.9, 0.99, 0.999, 1.0])
+def test_select_tiny_workload(ql, q):
+    L = wl.make_layer("tiny")
+    check_select(ql, L.A, q)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("M,K", [(1, 1), (1, 5), (3, 7), (100, 700), (257, 129)])
+def test_select_shapes(ql, dtype, M, K):
+    log(f"select {dtype} {M}x{K}")
+    rng = np.random.default_rng(M + K)
+    A = wl.random_matrix(rng, M, K, dtype, dist="t3")
+    for q in (0.5, 0.99):
+        check_select(ql, A, q)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_select_many_ties(ql, dtype):
+    """Values from a small set: many entries equal tau (strict clamp)."""
+    rng = np.random.default_rng(1)
+    vals = rng.choice(np.array([0.0, -0.0, 0.5, -1.0, 1.0, 2.0, -3.0, 3.0], np.float32),
+                      size=(150, 333))
+    A = wl.from_f32(vals, dtype)
+    for q in (0.0, 0.2, 0.5, 0.8, 0.95, 1.0):
+        check_select(ql, A, q)
+
+
+def test_select_bf16_layer_slice(ql):
+    L = wl.make_layer("llama7b_ffn_up", M=64)
+    check_select(ql, L.A, L.q)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_select_leading_dimension(ql, dtype):
+    rng = np.random.default_rng(2)
+    A = wl.random_matrix(rng, 40, 300, dtype, dist="t3")
+    check_select(ql, A, 0.95, ld=312)
+    check_select(ql, A, 0.95, ld=301)
+
+
+def test_select_deterministic(ql):
+    L = wl.make_layer("llama1.3b_ffn_up", M=512)
+    t1, c1 = run_select(ql, L.A, L.q)
+    t2, c2 = run_select(ql, L.A, L.q)
+    for a, b in ((t1, t2), (c1.row_ptr, c2.row_ptr)):
+        assert np.array_equal(host(a), host(b))
+    n = int(host(c1.row_ptr)[-1])
+    for a, b in ((c1.row, c2.row), (c1.col, c2.col), (c1.val, c2.val)):
+        assert np.array_equal(host(a)[:n], host(b)[:n])
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+def upload_u8(a):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def upload_f32(a):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(np.asarray(a, np.float32))).to("cuda:0")
+
+
+def upload_i32(a):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(np.asarray(a, np.int32))).to("cuda:0")
+
+
+def run_gemm(ql, codesA, sA, codesB, sB, K, delta=None, W=None):
+    M, N = codesA.shape[0], codesB.shape[0]
+    Aq = upload_u8(O.pack_rows(codesA))
+    Bq = upload_u8(O.pack_rows(codesB))
+    coo = None
+    Wd = None
+    if delta is not None:
+        nz = max(delta.nnz, 1)
+        pad = lambda a, dt: np.concatenate([np.asarray(a, dt), np.zeros(nz - len(a), dt)])
+        coo = ql.CooBuffers(upload_i32(pad(delta.row, np.int32)), upload_i32(pad(delta.col, np.int32)),
+                            upload_f32(pad(delta.val32, np.float32)), upload_i32(delta.row_ptr))
+        Wd = to_device(W)
+    Y = ql.gemm(Aq, upload_f32(sA), Bq, upload_f32(sB), M, N, K, coo, Wd)
+    torch().cuda.synchronize()
+    return host(Y)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (37, 300, 700), (256, 256, 256), (300, 520, 1000),
+                                   (513, 257, 4096), (64, 700, 129)])
+def test_gemm_integer_exact(ql, M, N, K):
+    """Unit scales, no compensation: Y is the exact integer-valued product."""
+    log(f"gemm exact {M}x{N}x{K}")
+    rng = np.random.default_rng(M + N + K)
+    ca = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    cb = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    Y = run_gemm(ql, ca, np.ones(M, np.float32), cb, np.ones(N, np.float32), K)
+    want = O.integer_product(ca, cb)
+    assert np.array_equal(Y.astype(np.float64), want)
+
+
+def test_gemm_one_hot_layout(ql):
+    """A[i,k] = 1 only at k = p[i]; B[j,k] = 1 only at k = r[j]: Y[i,j] = [p[i] == r[j]]."""
+    M, N, K = 96, 80, 512
+    rng = np.random.default_rng(0)
+    p = rng.integers(0, K, size=M)
+    r = rng.integers(0, K, size=N)
+    r[:M // 2 if M // 2 < N else N] = p[:min(M // 2, N)]
+    ca = np.zeros((M, K), np.uint8)
+    cb = np.zeros((N, K), np.uint8)
+    ca[np.arange(M), p] = 2   # value 1.0
+    cb[np.arange(N), r] = 2
+    Y = run_gemm(ql, ca, np.ones(M, np.float32), cb, np.ones(N, np.float32), K)
+    want = (p[:, None] == r[None, :]).astype(np.float64)
+    assert np.array_equal(Y.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("M,K,N", [(100, 300, 200), (300, 700, 520)])
+def test_gemm_scaled_with_compensation(ql, dtype, M, K, N):
+    log(f"gemm scaled {dtype} {M}x{K}x{N}")
+    rng = np.random.default_rng(M * K + N)
+    A = wl.random_matrix(rng, M, K, dtype, dist="t3")
+    W = wl.random_matrix(rng, K, N, dtype, scale=0.02)
+    ops = O.forward_operands(A.f32, W.f32, 0.97)
+    Y = run_gemm(ql, ops.codesA, ops.sA, ops.codesW, ops.sW, K, ops.delta, W)
+    want = O.forward_output(ops, W.f32)
+    err = O.rel_fro(Y, want)
+    assert err <= Y_TOL, err
+    # without compensation: the scaled product alone, tighter (no sparse sum)
+    Y0 = run_gemm(ql, ops.codesA, ops.sA, ops.codesW, ops.sW, K)
+    want0 = O.scaled_product(O.integer_product(ops.codesA, ops.codesW), ops.sA, ops.sW)
+    assert O.rel_fro(Y0, want0) <= 1e-7
+
+
+# ---------------------------------------------------------------------------
+# full forward
+# ---------------------------------------------------------------------------
+def workspace_views(ql, ws, M, K, N, dtype_code, q):
+    o = ql.forward_layout(M, K, N, dtype_code, q)
+    b = host(ws)
+    ldq = ql.packed_ld(K)
+    take = lambda off, n, dt: b[off: off + n * np.dtype(dt).itemsize].view(dt)
+    rp = take(o.row_ptr, M + 1, np.int32)
+    nnz = int(rp[-1])
+    return dict(
+        tau=take(o.tau, 1, np.float32)[0], row_ptr=rp, nnz=nnz,
+        row=take(o.coo_row, nnz, np.int32), col=take(o.coo_col, nnz, np.int32),
+        val=take(o.coo_val, nnz, np.float32),
+        Aq=take(o.Aq, M * ldq, np.uint8).reshape(M, ldq), sA=take(o.sA, M, np.float32),
+        Wq=take(o.Wq, N * ldq, np.uint8).reshape(N, ldq), sW=take(o.sW, N, np.float32))
+
+
+def check_forward(ql, L: wl.Layer, rows=None):
+    t = torch()
+    A, W = to_device(L.A), to_device(L.W)
+    Y, ws = ql.forward(A, W, L.q, return_workspace=True)
+    t.cuda.synchronize()
+    ops = O.forward_operands(L.A.f32, L.W.f32, L.q)
+    v = workspace_views(ql, ws, L.M, L.K, L.N, 0 if L.A.dtype == wl.F32 else 1, L.q)
+    assert_bits_equal(v["tau"], ops.tau, "tau")
+    assert_bits_equal(v["row_ptr"], ops.delta.row_ptr, "row_ptr")
+    assert_bits_equal(v["row"], ops.delta.row, "coo row")
+    assert_bits_equal(v["col"], ops.delta.col, "coo col")
+    assert_bits_equal(v["val"], ops.delta.val32, "coo val")
+    assert_bits_equal(v["sA"], ops.sA, "sA")
+    assert_bits_equal(v["Aq"], ops.Aq, "Aq")
+    assert_bits_equal(v["sW"], ops.sW, "sW")
+    assert_bits_equal(v["Wq"], ops.Wq, "Wq")
+    Yh = host(Y)
+    if rows is None:
+        want = O.forward_output(ops, L.W.f32)
+        got = Yh
+    else:
+        want = O.forward_output(ops, L.W.f32, rows=rows)
+        got = Yh[rows]
+    err = O.rel_fro(got, want)
+    log(f"forward {L.name} {L.M}x{L.K}x{L.N}: nnz {ops.delta.nnz} rel_fro {err:.3e}")
+    assert err <= Y_TOL, err
+
+
+def test_forward_tiny_workload(ql):
+    check_forward(ql, wl.make_layer("tiny"))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("M,K,N,q", [(1, 1, 1, 0.5), (7, 129, 3, 0.9), (300, 700, 520, 0.99),
+                                     (513, 1000, 300, 0.999)])
+def test_forward_small(ql, dtype, M, K, N, q):
+    rng = np.random.default_rng(M + 3 * K + 7 * N)
+    a = wl.draw_activation(rng, M, K, "t3", max(1, K // 200), 50.0)
+    w = wl.draw_weight(rng, K, N)
+    L = wl.Layer(f"small-{dtype}", wl.from_f32(a, dtype), wl.from_f32(w, dtype), q)
+    check_forward(ql, L)
+
+
+def test_forward_q_one_is_plain_quantized_gemm(ql):
+    """q = 1 clamps nothing; with grid-exact inputs Y = A W exactly."""
+    rng = np.random.default_rng(3)
+    M, K, N = 40, 260, 90
+    mags = rng.integers(0, 8, size=(M, K)); mags[:, 0] = 7
+    A = (np.array([0, .5, 1, 1.5, 2, 3, 4, 6])[mags] * rng.choice([-1, 1], size=(M, K))
+         * 2.0 ** rng.integers(-4, 4, size=(M, 1))).astype(np.float32)
+    mags = rng.integers(0, 8, size=(K, N)); mags[0, :] = 7
+    W = (np.array([0, .5, 1, 1.5, 2, 3, 4, 6])[mags] * rng.choice([-1, 1], size=(K, N))
+         * 2.0 ** rng.integers(-4, 4, size=(1, N))).astype(np.float32)
+    t = torch()
+    Y = ql.forward(t.from_numpy(A).cuda(), t.from_numpy(W).cuda(), 1.0)
+    t.cuda.synchronize()
+    assert np.array_equal(host(Y).astype(np.float64), A.astype(np.float64) @ W.astype(np.float64))
+
+
+def test_forward_matches_stage_calls(ql):
+    """fp4lin_forward == the four public calls in order (same bits)."""
+    t = torch()
+    L = wl.make_layer("llama1.3b_ffn_up", M=256)
+    A, W = to_device(L.A), to_device(L.W)
+    Y1 = ql.forward(A, W, L.q)
+    tau, coo = ql.outlier_select(A, L.q)
+    Aq, sA = ql.quantize_act(A, tau)
+    Wq, sW = ql.quantize_weight(W)
+    Y2 = ql.gemm(Aq, sA, Wq, sW, L.M, L.N, L.K, coo, W)
+    t.cuda.synchronize()
+    assert np.array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
