@@ -1,0 +1,259 @@
+"""Benchmark: FP4 quantized linear layer forward on one MI355X.
+
+One step = one pass of the whole forward over one batch: outlier select
+(tau + COO), token-wise quantization of A, channel-wise quantization of W, and
+the FP4 GEMM with the fused scale and sparse-compensation epilogue — the four
+public C-ABI calls that fp4lin_forward makes, issued directly so that HIP
+events can bracket each stage on the stream the kernels run on.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line. Inputs are seeded synthetic matrices (workloads module),
+already resident in HBM when the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP4 linear fwd effective TFLOP/s + % FP4 MFMA peak (7B FFN shape, 1 GPU)"
+FP4_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 MFMA
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+GEMM_SRC = os.path.join(ROOT, "quantized_linear_layer_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_llama7b_ffn_up_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama7b_ffn_up")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=4096,
+                   help="rows of A in the bounded CPU-oracle sample")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="also run a plain 1 GiB device copy (for PMC byte calibration)")
+    return p.parse_args()
+
+
+def file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+class Step:
+    """Marshals the four stage calls once; each call is then a bare C call."""
+
+    def __init__(self, ql, A, W, q, stream):
+        import torch
+        self.torch = torch
+        self.ql = ql
+        lib = ql.lib()
+        self.lib = lib
+        M, K = A.shape
+        N = W.shape[1]
+        dt = ql.BF16 if A.dtype == torch.bfloat16 else ql.F32
+        self.M, self.K, self.N, self.q = M, K, N, q
+        o = ql.forward_layout(M, K, N, dt, q)
+        self.ws = torch.empty(o.total, dtype=torch.uint8, device=A.device)
+        self.Y = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        base = self.ws.data_ptr()
+        P = ctypes.c_void_p
+        self.tau = P(base + o.tau)
+        self.coo = ql.Coo(base + o.coo_row, base + o.coo_col, base + o.coo_val,
+                          base + o.row_ptr, o.capacity)
+        self.Aq, self.sA = P(base + o.Aq), P(base + o.sA)
+        self.Wq, self.sW = P(base + o.Wq), P(base + o.sW)
+        self.scratch, self.scratch_bytes = P(base + o.scratch), o.total - o.scratch
+        self.A, self.W = P(A.data_ptr()), P(W.data_ptr())
+        self.lda, self.ldw = A.stride(0), W.stride(0)
+        self.dt = dt
+        self.stream = P(stream.cuda_stream)
+        self.offsets = o
+
+    def select(self):
+        s = self.lib.fp4lin_outlier_select(self.A, self.dt, self.M, self.K, self.lda, self.q,
+                                           self.tau, self.coo, self.scratch, self.scratch_bytes,
+                                           self.stream)
+        assert s == 0, s
+
+    def quant_a(self):
+        s = self.lib.fp4lin_quantize_act(self.A, self.dt, self.M, self.K, self.lda, self.tau,
+                                         self.Aq, self.sA, self.stream)
+        assert s == 0, s
+
+    def quant_w(self):
+        s = self.lib.fp4lin_quantize_weight(self.W, self.dt, self.K, self.N, self.ldw, self.Wq,
+                                            self.sW, self.scratch, self.scratch_bytes, self.stream)
+        assert s == 0, s
+
+    def gemm(self):
+        s = self.lib.fp4lin_gemm(self.Aq, self.sA, self.Wq, self.sW, self.M, self.N, self.K,
+                                 ctypes.byref(self.coo), self.W, self.dt, self.ldw,
+                                 ctypes.c_void_p(self.Y.data_ptr()), self.N, self.stream)
+        assert s == 0, s
+
+    def forward_call(self):
+        s = self.lib.fp4lin_forward(self.A, self.W, self.dt, self.M, self.K, self.N, self.lda,
+                                    self.ldw, self.q, ctypes.c_void_p(self.Y.data_ptr()), self.N,
+                                    ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
+                                    self.stream)
+        assert s == 0, s
+
+
+STAGES = ("select", "quant_a", "quant_w", "gemm")
+
+
+def cpu_baseline(workload, seed, rows):
+    """The oracle as it stands, on the first `rows` rows of the same workload
+    (full W), timed on the host cores."""
+    import oracle as O
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas_threads = 1
+    L = wl.make_layer(workload, seed=seed, M=rows)
+    t0 = time.perf_counter()
+    Y, _ = O.forward(L.A.f32, L.W.f32, L.q)
+    t = time.perf_counter() - t0
+    flops = 2.0 * L.M * L.N * L.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"first {rows} of {wl.spec(workload)['M']} rows of A with the full "
+                      f"{L.K}x{L.N} W, q={L.q}; whole oracle forward (tau, clamp + COO, "
+                      f"quantize A and W, float64 integer GEMM, sparse term) took {t:.2f} s; "
+                      f"host affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_linear_layer_amd as ql
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    L = wl.make_layer(args.workload, seed=args.seed)
+    A = upload(L.A, dev)
+    W = upload(L.W, dev)
+    stream = torch.cuda.current_stream()
+    st = Step(ql, A, W, L.q, stream)
+    M, K, N = L.M, L.K, L.N
+    flops = 2.0 * M * N * K
+
+    # warmup (also checks the path end to end once)
+    for _ in range(max(args.warmup, 1)):
+        st.select(); st.quant_a(); st.quant_w(); st.gemm()
+    torch.cuda.synchronize()
+    nnz = int(st.ws[st.offsets.row_ptr + 4 * M: st.offsets.row_ptr + 4 * M + 4]
+              .cpu().numpy().view(np.int32)[0])
+
+    # timed region: exactly K steps, events between the stages on the same stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        st.select(); e[1].record(stream)
+        st.quant_a(); e[2].record(stream)
+        st.quant_w(); e[3].record(stream)
+        st.gemm(); e[4].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1])
+                                     for i in range(args.steps)]))
+                for j, name in enumerate(STAGES)}
+    event_step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)]))
+
+    # cross-check: the single fp4lin_forward call over the same number of steps
+    torch.cuda.synchronize()
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(args.steps):
+        st.forward_call()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    forward_call_ms = f0.elapsed_time(f1) / args.steps
+
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    gemm_s = stage_ms["gemm"] * 1e-3
+    achieved = flops / gemm_s / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("gemm_source_sha256") == file_sha(GEMM_SRC) and tr.get("workload") == args.workload:
+            traffic = tr.get("bytes_per_launch")
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    # algorithmic HBM bytes of one forward (A read twice, W read twice, packed
+    # operands written and read once, Y written once, COO written and read)
+    alg_bytes = (2 * 2 * M * K + 2 * 2 * K * N + 2 * (M + N) * (K // 2) + 4 * M * N
+                 + 2 * 12 * nnz)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "K": K, "N": N, "q": L.q,
+                   "input_dtype": L.A.dtype, "output_dtype": "f32", "seed": args.seed,
+                   "nnz_dA": nnz},
+        "pct_fp4_peak": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
+        "pct_hbm_roofline": round(100.0 * (alg_bytes / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBS, 2),
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "event_step_ms": round(event_step_ms, 5),
+        "forward_call_ms": round(forward_call_ms, 5),
+        "roofline": {"bound": "mfma", "kernel": "fp4_gemm_kernel (with fused epilogue)",
+                     "achieved": round(achieved, 2), "peak": FP4_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.seed, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+def upload(m, dev):
+    import torch
+    import workloads as wl
+    if m.dtype == wl.F32:
+        return torch.from_numpy(np.ascontiguousarray(m.bits)).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(m.bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+if __name__ == "__main__":
+    main()

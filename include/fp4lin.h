@@ -189,6 +189,8 @@ fp4lin_status fp4lin_quantize_weight(const void* W, fp4lin_dtype dt, int64_t K, 
  *   W        device K x N (dtype wdt, leading dimension ldw), required exactly
  *            when dA is given (the unquantized weight dA multiplies)
  *   Y        device, M x N floats, leading dimension ldy (output)
+ * Packed operands are addressed with 32-bit byte offsets: (M+1)*packed_ld(K)
+ * and (N+1)*packed_ld(K) must be below 2^31 (else FP4LIN_ERR_SHAPE).
  * Errors: NULL, SHAPE, DTYPE, ALIGN, LAUNCH. */
 fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
                           const float* sB, int64_t M, int64_t N, int64_t K,

@@ -171,6 +171,9 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
     if (ldw < N) return FP4LIN_ERR_SHAPE;
     sp = fp4lin::SparseArgs{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw};
   }
+  // packed operands are addressed with 32-bit byte offsets
+  const int64_t ldq = fp4lin_packed_ld(K);
+  if ((M + 1) * ldq >= kMaxDim || (N + 1) * ldq >= kMaxDim) return FP4LIN_ERR_SHAPE;
   if (!aligned16(Aq) || !aligned16(Bq)) return FP4LIN_ERR_ALIGN;
   return launch_status(
       fp4lin::launch_fp4_gemm(Aq, sA, Bq, sB, M, N, fp4lin_packed_ld(K), sp, Y, ldy, stream));

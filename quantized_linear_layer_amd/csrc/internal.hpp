@@ -32,6 +32,10 @@ struct SparseArgs {
   int64_t ldw;
 };
 
+// Y[i, :] += sum over row i's non-zeros of val * W[col, :] (ascending col).
+hipError_t launch_sparse_add(const SparseArgs& sp, int64_t M, int64_t N, float* Y, int64_t ldy,
+                             hipStream_t stream);
+
 hipError_t launch_fp4_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const float* sB,
                            int64_t M, int64_t N, int64_t ldq, const SparseArgs& sp, float* Y,
                            int64_t ldy, hipStream_t stream);
