@@ -29,8 +29,6 @@ sys.path.insert(0, ROOT)
 METRIC = "FP4 linear fwd effective TFLOP/s + % FP4 MFMA peak (7B FFN shape, 1 GPU)"
 FP4_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 MFMA
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
-GEMM_SRC = os.path.join(ROOT, "quantized_linear_layer_amd", "csrc", "gemm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_llama7b_ffn_up_traffic.json")
 
 
 def parse():
@@ -41,8 +39,8 @@ def parse():
     p.add_argument("--workload", default="llama7b_ffn_up")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=4096,
-                   help="rows of A in the bounded CPU-oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=0,
+                   help="rows of A in the CPU-oracle sample (0 = the whole workload)")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run a plain 1 GiB device copy (for PMC byte calibration)")
     return p.parse_args()
@@ -101,8 +99,14 @@ class Step:
 
     def gemm(self):
         s = self.lib.fp4lin_gemm(self.Aq, self.sA, self.Wq, self.sW, self.M, self.N, self.K,
-                                 ctypes.byref(self.coo), self.W, self.dt, self.ldw,
-                                 ctypes.c_void_p(self.Y.data_ptr()), self.N, self.stream)
+                                 None, None, self.dt, 0, ctypes.c_void_p(self.Y.data_ptr()),
+                                 self.N, self.stream)
+        assert s == 0, s
+
+    def sparse(self):
+        s = self.lib.fp4lin_sparse_add(ctypes.byref(self.coo), self.W, self.dt, self.ldw, self.M,
+                                       self.N, ctypes.c_void_p(self.Y.data_ptr()), self.N,
+                                       self.stream)
         assert s == 0, s
 
     def forward_call(self):
@@ -113,7 +117,7 @@ class Step:
         assert s == 0, s
 
 
-STAGES = ("select", "quant_a", "quant_w", "gemm")
+STAGES = ("select", "quant_a", "quant_w", "gemm", "sparse")
 
 
 def cpu_baseline(workload, seed, rows):
@@ -127,6 +131,8 @@ def cpu_baseline(workload, seed, rows):
                             if i.get("user_api") == "blas"] or [1])
     except Exception:
         blas_threads = 1
+    full = wl.spec(workload)["M"]
+    rows = full if rows <= 0 or rows > full else rows
     L = wl.make_layer(workload, seed=seed, M=rows)
     t0 = time.perf_counter()
     Y, _ = O.forward(L.A.f32, L.W.f32, L.q)
@@ -134,10 +140,10 @@ def cpu_baseline(workload, seed, rows):
     flops = 2.0 * L.M * L.N * L.K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"first {rows} of {wl.spec(workload)['M']} rows of A with the full "
-                      f"{L.K}x{L.N} W, q={L.q}; whole oracle forward (tau, clamp + COO, "
-                      f"quantize A and W, float64 integer GEMM, sparse term) took {t:.2f} s; "
-                      f"host affinity {len(os.sched_getaffinity(0))} cpus"}
+            "sample": f"{rows} of {full} rows of A with the full {L.K}x{L.N} W, q={L.q}: "
+                      f"the whole oracle forward (tau, clamp + COO, quantize A and W, float64 "
+                      f"integer GEMM, sparse term) took {t:.2f} s; host affinity "
+                      f"{len(os.sched_getaffinity(0))} cpus, BLAS threads {blas_threads}"}
 
 
 def main():
@@ -161,7 +167,7 @@ def main():
 
     # warmup (also checks the path end to end once)
     for _ in range(max(args.warmup, 1)):
-        st.select(); st.quant_a(); st.quant_w(); st.gemm()
+        st.select(); st.quant_a(); st.quant_w(); st.gemm(); st.sparse()
     torch.cuda.synchronize()
     nnz = int(st.ws[st.offsets.row_ptr + 4 * M: st.offsets.row_ptr + 4 * M + 4]
               .cpu().numpy().view(np.int32)[0])
@@ -178,6 +184,7 @@ def main():
         st.quant_a(); e[2].record(stream)
         st.quant_w(); e[3].record(stream)
         st.gemm(); e[4].record(stream)
+        st.sparse(); e[5].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -198,25 +205,67 @@ def main():
     forward_call_ms = f0.elapsed_time(f1) / args.steps
 
     if args.copy_calib:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # plain copies of known size for PMC byte calibration: 1 GiB read and
+        # 1 GiB written, by the runtime's blit kernel and by an elementwise kernel
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(5):
+        for _ in range(3):
             dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
-    gemm_s = stage_ms["gemm"] * 1e-3
-    achieved = flops / gemm_s / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("gemm_source_sha256") == file_sha(GEMM_SRC) and tr.get("workload") == args.workload:
-            traffic = tr.get("bytes_per_launch")
     value = flops / (ms_per_step * 1e-3) / 1e12
-    # algorithmic HBM bytes of one forward (A read twice, W read twice, packed
-    # operands written and read once, Y written once, COO written and read)
-    alg_bytes = (2 * 2 * M * K + 2 * 2 * K * N + 2 * (M + N) * (K // 2) + 4 * M * N
-                 + 2 * 12 * nnz)
+    # Algorithmic work per launch of each stage (the minimum the operation
+    # needs; the roofline each stage is held against):
+    #   select  : A read twice (threshold, then compaction) + COO + row_ptr written
+    #   quant_a : A read once, packed codes + scales written
+    #   quant_w : W read once, packed codes + scales written
+    #   gemm    : 2*M*N*K FP4 MFMA flops (its HBM floor, packed operands read
+    #             once + fp32 Y written, is below the MFMA floor)
+    #   sparse  : Y read and written, COO read, each touched W row read once
+    e = 2 if L.A.dtype == wl.BF16 else 4
+    ldq = ql.packed_ld(K)
+    hbm_bytes = {
+        "select": 2 * e * M * K + 12 * nnz + 4 * (M + 1),
+        "quant_a": e * M * K + M * ldq + 4 * M,
+        "quant_w": e * K * N + N * ldq + 4 * N,
+        "gemm": (M + N) * ldq + 4 * M * N,
+        "sparse": 8 * M * N + 12 * nnz + 4 * (M + 1) + e * N * min(K, nnz),
+    }
+    kernels = {}
+    for name in STAGES:
+        t_s = stage_ms[name] * 1e-3
+        gbs = hbm_bytes[name] / t_s / 1e9
+        kernels[name] = {"ms": round(stage_ms[name], 5), "bytes": int(hbm_bytes[name]),
+                         "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    gemm_tf = flops / (stage_ms["gemm"] * 1e-3) / 1e12
+    kernels["gemm"].update({"bound": "mfma", "TFLOP/s": round(gemm_tf, 1),
+                            "mfma_frac": round(gemm_tf / FP4_PEAK_TFLOPS, 4)})
+    sp_flops = 2.0 * nnz * N
+    kernels["sparse"]["fp32_FMA_TFLOP/s"] = round(sp_flops / (stage_ms["sparse"] * 1e-3) / 1e12, 2)
+    for name in ("select", "quant_a", "quant_w", "sparse"):
+        kernels[name]["bound"] = "hbm"
+    dom = max(STAGES, key=lambda n: stage_ms[n])
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{dom}_{args.workload}.json")
+    if os.path.exists(tfile):
+        tr = json.load(open(tfile))
+        if tr.get("source_sha256") == file_sha(os.path.join(ROOT, tr["source"])):
+            traffic = tr.get("bytes_per_launch")
+    if dom == "gemm":
+        roof = {"bound": "mfma", "kernel": "fp4_gemm_kernel", "achieved": round(gemm_tf, 2),
+                "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tf / FP4_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+    else:
+        kname = {"select": "select_hist/count/compact kernels", "quant_a": "quantize_rows_kernel",
+                 "quant_w": "colmax + quantize_cols kernels", "sparse": "sparse_add_kernel"}[dom]
+        roof = {"bound": "hbm", "kernel": kname, "achieved": kernels[dom]["GB/s"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["hbm_frac"],
+                "traffic": traffic}
+    # algorithmic HBM bytes of the whole forward (A read twice, W read once,
+    # packed operands written and read once, Y written once, COO written/read)
+    alg_bytes = (2 * e * M * K + e * K * N + 2 * (M + N) * ldq + 4 * M * N + 2 * 12 * nnz)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -238,10 +287,8 @@ def main():
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "event_step_ms": round(event_step_ms, 5),
         "forward_call_ms": round(forward_call_ms, 5),
-        "roofline": {"bound": "mfma", "kernel": "fp4_gemm_kernel (with fused epilogue)",
-                     "achieved": round(achieved, 2), "peak": FP4_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4),
-                     "traffic": traffic},
+        "roofline": roof,
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.seed, args.cpu_rows)

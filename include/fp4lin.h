@@ -197,6 +197,18 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
                           const fp4lin_coo* dA, const void* W, fp4lin_dtype wdt,
                           int64_t ldw, float* Y, int64_t ldy, hipStream_t stream);
 
+/* Sparse compensation alone (compensation paragraph of the FP4 training
+ * write-up): Y[i,:] += sum over row i's non-zeros of dA, ascending k, of
+ * val * W[k,:], with fp32 fused multiply-add. fp4lin_gemm with a non-NULL dA
+ * is exactly fp4lin_gemm with dA = NULL followed by this call.
+ *   dA       host pointer to a COO descriptor (device arrays; row is not read)
+ *   W        device K x N weight (dtype wdt, leading dimension ldw)
+ *   Y        device M x N floats, leading dimension ldy (read and written)
+ * Errors: NULL, SHAPE, DTYPE, LAUNCH. */
+fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtype wdt,
+                                int64_t ldw, int64_t M, int64_t N, float* Y, int64_t ldy,
+                                hipStream_t stream);
+
 /* The whole layer forward (forward-start paragraph: W and A are quantized when
  * the layer's forward begins). Runs exactly fp4lin_outlier_select,
  * fp4lin_quantize_act (with the selected tau), fp4lin_quantize_weight and

@@ -18,7 +18,7 @@ __all__ = [
     "Fp4linError", "lib", "packed_ld", "quantile_rank", "select_workspace_bytes",
     "weight_workspace_bytes", "workspace_bytes", "forward_layout",
     "fp4lin_outlier_select", "fp4lin_quantize_act", "fp4lin_quantize_weight", "fp4lin_gemm",
-    "fp4lin_forward", "outlier_select", "quantize_act", "quantize_weight", "gemm", "forward",
+    "fp4lin_sparse_add", "fp4lin_forward", "outlier_select", "quantize_act", "quantize_weight", "gemm", "forward",
     "CooBuffers",
 ]
 
@@ -161,6 +161,16 @@ def fp4lin_gemm(Aq, sA, Bq, sB, M, N, K, coo: CooBuffers | None, W, Y, stream=No
     _check(lib().fp4lin_gemm(_dev(Aq, "Aq"), _dev(sA, "sA"), _dev(Bq, "Bq"), _dev(sB, "sB"),
                              M, N, K, cp, wp, wdt, ldw, _dev(Y, "Y"), ldy, _stream(stream)),
            "fp4lin_gemm")
+
+
+def fp4lin_sparse_add(coo: CooBuffers, W, Y, stream=None):
+    """Y += dA . W (Y must already hold the scaled FP4 product)."""
+    M, N, ldy = _matrix(Y, "Y")
+    _, _, ldw = _matrix(W, "W")
+    c = coo.struct()
+    _check(lib().fp4lin_sparse_add(ctypes.byref(c), _dev(W, "W"), _dtype_code(W), ldw, M, N,
+                                   _dev(Y, "Y"), ldy, _stream(stream)),
+           "fp4lin_sparse_add")
 
 
 def fp4lin_forward(A, W, q, Y, ws, stream=None):

@@ -179,6 +179,18 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
       fp4lin::launch_fp4_gemm(Aq, sA, Bq, sB, M, N, fp4lin_packed_ld(K), sp, Y, ldy, stream));
 }
 
+fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtype wdt,
+                                int64_t ldw, int64_t M, int64_t N, float* Y, int64_t ldy,
+                                hipStream_t stream) {
+  if (dA == nullptr || dA->row_ptr == nullptr || dA->col == nullptr || dA->val == nullptr ||
+      W == nullptr || Y == nullptr)
+    return FP4LIN_ERR_NULL;
+  if (bad_dtype(wdt)) return FP4LIN_ERR_DTYPE;
+  if (!ok_dim(M) || !ok_dim(N) || ldw < N || ldy < N) return FP4LIN_ERR_SHAPE;
+  const fp4lin::SparseArgs sp{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw};
+  return launch_status(fp4lin::launch_sparse_add(sp, M, N, Y, ldy, stream));
+}
+
 fp4lin_status fp4lin_forward(const void* A, const void* W, fp4lin_dtype dt, int64_t M, int64_t K,
                              int64_t N, int64_t lda, int64_t ldw, double q, float* Y, int64_t ldy,
                              void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -180,6 +180,23 @@ def test_gemm_errors():
     assert gemm(Bq=MISALIGNED) == _lib.ERR_ALIGN
 
 
+def sparse_add(dA=None, W=FAKE, wdt=1, ldw=4, M=4, N=4, Y=FAKE, ldy=4):
+    dA = coo(10) if dA is None else dA
+    return L.fp4lin_sparse_add(ctypes.byref(dA), W, wdt, ldw, M, N, Y, ldy, None)
+
+
+def test_sparse_add_errors():
+    assert L.fp4lin_sparse_add(None, FAKE, 1, 4, 4, 4, FAKE, 4, None) == _lib.ERR_NULL
+    for fld in ("col", "val", "row_ptr"):
+        assert sparse_add(dA=coo(10, null=fld)) == _lib.ERR_NULL
+    assert sparse_add(W=None) == _lib.ERR_NULL
+    assert sparse_add(Y=None) == _lib.ERR_NULL
+    assert sparse_add(wdt=7) == _lib.ERR_DTYPE
+    assert sparse_add(M=0) == _lib.ERR_SHAPE
+    assert sparse_add(ldw=3) == _lib.ERR_SHAPE
+    assert sparse_add(ldy=3) == _lib.ERR_SHAPE
+
+
 def forward(A=FAKE, W=FAKE, dt=1, M=4, K=8, N=4, lda=8, ldw=4, q=0.5, Y=FAKE, ldy=4, ws=FAKE,
             wsb=1 << 30):
     return L.fp4lin_forward(A, W, dt, M, K, N, lda, ldw, q, Y, ldy, ws, wsb, None)

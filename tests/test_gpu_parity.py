@@ -452,3 +452,18 @@ def test_forward_matches_stage_calls(ql):
     Y2 = ql.gemm(Aq, sA, Wq, sW, L.M, L.N, L.K, coo, W)
     t.cuda.synchronize()
     assert np.array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
+
+
+def test_gemm_equals_gemm_then_sparse_add(ql):
+    """fp4lin_gemm(dA) == fp4lin_gemm(NULL) followed by fp4lin_sparse_add (same bits)."""
+    t = torch()
+    L = wl.make_layer("llama1.3b_ffn_up", M=300)
+    A, W = to_device(L.A), to_device(L.W)
+    tau, coo = ql.outlier_select(A, L.q)
+    Aq, sA = ql.quantize_act(A, tau)
+    Wq, sW = ql.quantize_weight(W)
+    Y1 = ql.gemm(Aq, sA, Wq, sW, L.M, L.N, L.K, coo, W)
+    Y2 = ql.gemm(Aq, sA, Wq, sW, L.M, L.N, L.K)
+    ql.fp4lin_sparse_add(coo, W, Y2)
+    t.cuda.synchronize()
+    assert np.array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
