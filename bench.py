@@ -104,9 +104,9 @@ class Step:
         assert s == 0, s
 
     def sparse(self):
-        s = self.lib.fp4lin_sparse_add(ctypes.byref(self.coo), self.W, self.dt, self.ldw, self.M,
-                                       self.N, ctypes.c_void_p(self.Y.data_ptr()), self.N,
-                                       self.stream)
+        s = self.lib.fp4lin_sparse_add(ctypes.byref(self.coo), self.W, self.dt, self.K, self.ldw,
+                                       self.M, self.N, ctypes.c_void_p(self.Y.data_ptr()),
+                                       self.N, self.stream)
         assert s == 0, s
 
     def forward_call(self):

@@ -181,13 +181,15 @@ fp4lin_status fp4lin_quantize_weight(const void* W, fp4lin_dtype dt, int64_t K, 
 /* FP4 GEMM with fused epilogue (the FP4 GeMM kernel paragraph gives the role;
  * here it runs on the gfx950 FP4 matrix cores with unit block scales):
  *   acc[i,j] = sum_k v(Aq[i,k]) v(Bq[j,k])            (exact in fp32)
- *   Y[i,j]   = RN32(RN32(acc*sA[i])*sB[j]) + sum_{(i,k) in dA} val*W[k,j]
- * The sparse term is added in ascending k with fp32 fused multiply-add.
+ *   Y[i,j]   = RN32(RN32(acc*sA[i])*sB[j]) + s[i,j],
+ *   s[i,j]   = sum_{(i,k) in dA} val*W[k,j], accumulated from 0 in ascending k
+ *              with fp32 fused multiply-add, then added once to the product.
  *   Aq, sA   device, M x packed_ld(K) bytes, M floats
  *   Bq, sB   device, N x packed_ld(K) bytes (N-major), N floats
  *   dA       host pointer to a COO descriptor, or NULL for no compensation
  *   W        device K x N (dtype wdt, leading dimension ldw), required exactly
- *            when dA is given (the unquantized weight dA multiplies)
+ *            when dA is given (the unquantized weight dA multiplies);
+ *            K*ldw*sizeof(dtype) must be below 2^31
  *   Y        device, M x N floats, leading dimension ldy (output)
  * Packed operands are addressed with 32-bit byte offsets: (M+1)*packed_ld(K)
  * and (N+1)*packed_ld(K) must be below 2^31 (else FP4LIN_ERR_SHAPE).
@@ -198,16 +200,20 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
                           int64_t ldw, float* Y, int64_t ldy, hipStream_t stream);
 
 /* Sparse compensation alone (compensation paragraph of the FP4 training
- * write-up): Y[i,:] += sum over row i's non-zeros of dA, ascending k, of
- * val * W[k,:], with fp32 fused multiply-add. fp4lin_gemm with a non-NULL dA
- * is exactly fp4lin_gemm with dA = NULL followed by this call.
+ * write-up): Y[i,:] = Y[i,:] + s[i,:], where s is the sum over row i's
+ * non-zeros of dA, ascending k, of val * W[k,:], accumulated from 0 with fp32
+ * fused multiply-add. Rows without non-zeros are not touched. fp4lin_gemm with
+ * a non-NULL dA is exactly fp4lin_gemm with dA = NULL followed by this call.
  *   dA       host pointer to a COO descriptor (device arrays; row is not read)
- *   W        device K x N weight (dtype wdt, leading dimension ldw)
+ *   W        device K x N weight (dtype wdt, leading dimension ldw); column
+ *            indices of dA must be < K
  *   Y        device M x N floats, leading dimension ldy (read and written)
+ * W is addressed with 32-bit byte offsets: K*ldw*sizeof(dtype) must be below
+ * 2^31 (else FP4LIN_ERR_SHAPE).
  * Errors: NULL, SHAPE, DTYPE, LAUNCH. */
 fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtype wdt,
-                                int64_t ldw, int64_t M, int64_t N, float* Y, int64_t ldy,
-                                hipStream_t stream);
+                                int64_t K, int64_t ldw, int64_t M, int64_t N, float* Y,
+                                int64_t ldy, hipStream_t stream);
 
 /* The whole layer forward (forward-start paragraph: W and A are quantized when
  * the layer's forward begins). Runs exactly fp4lin_outlier_select,

@@ -166,9 +166,9 @@ def fp4lin_gemm(Aq, sA, Bq, sB, M, N, K, coo: CooBuffers | None, W, Y, stream=No
 def fp4lin_sparse_add(coo: CooBuffers, W, Y, stream=None):
     """Y += dA . W (Y must already hold the scaled FP4 product)."""
     M, N, ldy = _matrix(Y, "Y")
-    _, _, ldw = _matrix(W, "W")
+    K, _, ldw = _matrix(W, "W")
     c = coo.struct()
-    _check(lib().fp4lin_sparse_add(ctypes.byref(c), _dev(W, "W"), _dtype_code(W), ldw, M, N,
+    _check(lib().fp4lin_sparse_add(ctypes.byref(c), _dev(W, "W"), _dtype_code(W), K, ldw, M, N,
                                    _dev(Y, "Y"), ldy, _stream(stream)),
            "fp4lin_sparse_add")
 

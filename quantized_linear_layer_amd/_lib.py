@@ -47,8 +47,8 @@ SIGNATURES = {
                                        c_size, c_ptr]),
     "fp4lin_gemm": (c_int, [c_ptr, c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64,
                             ctypes.POINTER(Coo), c_ptr, c_int, c_i64, c_ptr, c_i64, c_ptr]),
-    "fp4lin_sparse_add": (c_int, [ctypes.POINTER(Coo), c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr,
-                                  c_i64, c_ptr]),
+    "fp4lin_sparse_add": (c_int, [ctypes.POINTER(Coo), c_ptr, c_int, c_i64, c_i64, c_i64, c_i64,
+                                  c_ptr, c_i64, c_ptr]),
     "fp4lin_forward": (c_int, [c_ptr, c_ptr, c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl,
                                c_ptr, c_i64, c_ptr, c_size, c_ptr]),
 }

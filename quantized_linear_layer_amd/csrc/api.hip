@@ -23,6 +23,11 @@ int64_t needed_capacity(int64_t n, int64_t k) { return n - 1 - k; }
 
 size_t weight_ws(int64_t N) { return round_up(fp4lin::weight_workspace_bytes(N), 256); }
 
+// The compensation kernel addresses W with 32-bit byte offsets.
+bool weight_addressable(int64_t K, int64_t ldw, fp4lin_dtype wdt) {
+  return K * ldw * (wdt == FP4LIN_BF16 ? 2 : 4) < kMaxDim;
+}
+
 size_t select_ws(fp4lin_dtype dt) {
   return round_up(fp4lin::select_workspace_bytes(dt == FP4LIN_BF16), 256);
 }
@@ -163,13 +168,13 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
   if (Aq == nullptr || sA == nullptr || Bq == nullptr || sB == nullptr || Y == nullptr)
     return FP4LIN_ERR_NULL;
   if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldy < N) return FP4LIN_ERR_SHAPE;
-  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, false, 0};
+  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, false, 0, 0};
   if (dA != nullptr) {
     if (dA->row_ptr == nullptr || dA->col == nullptr || dA->val == nullptr || W == nullptr)
       return FP4LIN_ERR_NULL;
     if (bad_dtype(wdt)) return FP4LIN_ERR_DTYPE;
-    if (ldw < N) return FP4LIN_ERR_SHAPE;
-    sp = fp4lin::SparseArgs{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw};
+    if (ldw < N || !weight_addressable(K, ldw, wdt)) return FP4LIN_ERR_SHAPE;
+    sp = fp4lin::SparseArgs{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K};
   }
   // packed operands are addressed with 32-bit byte offsets
   const int64_t ldq = fp4lin_packed_ld(K);
@@ -180,14 +185,16 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
 }
 
 fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtype wdt,
-                                int64_t ldw, int64_t M, int64_t N, float* Y, int64_t ldy,
-                                hipStream_t stream) {
+                                int64_t K, int64_t ldw, int64_t M, int64_t N, float* Y,
+                                int64_t ldy, hipStream_t stream) {
   if (dA == nullptr || dA->row_ptr == nullptr || dA->col == nullptr || dA->val == nullptr ||
       W == nullptr || Y == nullptr)
     return FP4LIN_ERR_NULL;
   if (bad_dtype(wdt)) return FP4LIN_ERR_DTYPE;
-  if (!ok_dim(M) || !ok_dim(N) || ldw < N || ldy < N) return FP4LIN_ERR_SHAPE;
-  const fp4lin::SparseArgs sp{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw};
+  if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldw < N || ldy < N ||
+      !weight_addressable(K, ldw, wdt))
+    return FP4LIN_ERR_SHAPE;
+  const fp4lin::SparseArgs sp{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K};
   return launch_status(fp4lin::launch_sparse_add(sp, M, N, Y, ldy, stream));
 }
 

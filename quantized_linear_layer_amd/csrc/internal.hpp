@@ -30,6 +30,7 @@ struct SparseArgs {
   const void* W;
   bool w_bf16;
   int64_t ldw;
+  int64_t w_rows;  // K: rows of W (W is addressed with 32-bit byte offsets)
 };
 
 // Y[i, :] += sum over row i's non-zeros of val * W[col, :] (ascending col).

@@ -6,15 +6,17 @@
 // to the FP4 product so that the outliers are not lost.
 //
 // One wave owns one (row i, 512-column strip) unit: it reads Y[i, strip] (the
-// scaled FP4 product the GEMM kernel just wrote), adds
+// scaled FP4 product the GEMM kernel wrote), adds
 //   sum over the row's non-zeros (k ascending) of val * W[k, strip]
 // with fp32 fused multiply-add, and writes it back. Each lane owns 8
-// consecutive columns, so a non-zero costs one 16-byte W load per lane. The
-// row's non-zeros are fetched 64 at a time (one per lane) and walked with
-// eight W row segments in flight. Units are ordered strip by strip, and each
-// XCD takes a contiguous run of that order, so the waves running together on
-// an XCD read the same W strip through its L2. Rows without non-zeros are
-// left untouched.
+// consecutive columns, so a non-zero costs one 16-byte (bf16) W load per lane,
+// addressed with the row offset in the scalar operand of a buffer load. The
+// row's non-zeros are fetched 64 at a time (one per lane) and consumed in
+// groups of eight W row segments, the next group requested before the current
+// one is multiplied. Units are ordered strip by strip and each XCD takes a
+// contiguous run of that order, so the waves running together on an XCD read
+// the same W strip through its L2. Rows without non-zeros are left
+// untouched.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -22,38 +24,67 @@ namespace fp4lin {
 
 namespace {
 
-constexpr int kStrip = 512;  // columns per unit (8 per lane)
-constexpr int kCPL = 8;
+constexpr int kCPL = 8;                // columns per lane
+constexpr int kStrip = 64 * kCPL;      // columns per unit
+constexpr int kGroup = 8;              // W row segments per load group (two groups in flight)
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
+
+// W words of one non-zero for this lane's 8 columns: bf16 -> one 16-byte
+// word, fp32 -> two. Converted to fp32 when consumed.
+template <bool kBf16>
+struct WRaw {
+  uint4 u[kBf16 ? 1 : 2];
+};
 
 template <bool kBf16>
-__device__ inline void load_w8(const void* __restrict__ W, int64_t off, int valid, bool vec,
-                               float w[kCPL]) {
+__device__ inline void fma_raw(float v, const WRaw<kBf16>& r, float y[kCPL]) {
   if constexpr (kBf16) {
-    const uint16_t* p = static_cast<const uint16_t*>(W) + off;
-    if (vec && valid >= kCPL) {
-      const uint4 u = *reinterpret_cast<const uint4*>(p);
-      const uint32_t d[4] = {u.x, u.y, u.z, u.w};
+    const uint32_t d[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        w[2 * q] = __uint_as_float(d[q] << 16);
-        w[2 * q + 1] = __uint_as_float(d[q] & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < kCPL; ++c) w[c] = (c < valid) ? __uint_as_float(uint32_t(p[c]) << 16) : 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      y[2 * q] = fmaf(v, __uint_as_float(d[q] << 16), y[2 * q]);
+      y[2 * q + 1] = fmaf(v, __uint_as_float(d[q] & 0xffff0000u), y[2 * q + 1]);
     }
   } else {
-    const float* p = static_cast<const float*>(W) + off;
-    if (vec && valid >= kCPL) {
-      const float4 u0 = *reinterpret_cast<const float4*>(p);
-      const float4 u1 = *reinterpret_cast<const float4*>(p + 4);
-      w[0] = u0.x; w[1] = u0.y; w[2] = u0.z; w[3] = u0.w;
-      w[4] = u1.x; w[5] = u1.y; w[6] = u1.z; w[7] = u1.w;
-    } else {
+    const uint32_t d[8] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w,
+                           r.u[1].x, r.u[1].y, r.u[1].z, r.u[1].w};
 #pragma unroll
-      for (int c = 0; c < kCPL; ++c) w[c] = (c < valid) ? p[c] : 0.0f;
-    }
+    for (int c = 0; c < kCPL; ++c) y[c] = fmaf(v, __uint_as_float(d[c]), y[c]);
   }
+}
+
+// Full-width load of W[k, col0 .. col0+3] through the buffer resource: the row
+// offset k*ldw is wave-uniform and goes in the scalar offset, the column
+// offset is the lane's constant vector offset.
+template <bool kBf16>
+__device__ inline WRaw<kBf16> load_full(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  WRaw<kBf16> r;
+  r.u[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+  if constexpr (!kBf16)
+    r.u[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, soff, 0));
+  return r;
+}
+
+// Element loads for a lane whose 4 columns run past N (last strip only).
+template <bool kBf16>
+__device__ inline WRaw<kBf16> load_part(const void* __restrict__ W, int64_t off, int valid) {
+  WRaw<kBf16> r;
+  if constexpr (kBf16) {
+    const uint16_t* p = static_cast<const uint16_t*>(W) + off;
+    uint32_t h[kCPL];
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c) h[c] = (c < valid) ? uint32_t(p[c]) : 0u;
+    r.u[0] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                        h[6] | (h[7] << 16));
+  } else {
+    const float* p = static_cast<const float*>(W) + off;
+    uint32_t h[kCPL];
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c) h[c] = (c < valid) ? __float_as_uint(p[c]) : 0u;
+    r.u[0] = make_uint4(h[0], h[1], h[2], h[3]);
+    r.u[1] = make_uint4(h[4], h[5], h[6], h[7]);
+  }
+  return r;
 }
 
 __device__ inline float readlane_f(float v, int lane) {
@@ -63,8 +94,9 @@ __device__ inline float readlane_f(float v, int lane) {
 template <bool kBf16>
 __global__ __launch_bounds__(256) void sparse_add_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-    const float* __restrict__ val, const void* __restrict__ W, int64_t ldw, int w_vec,
-    float* __restrict__ Y, int64_t ldy, int y_vec, int M, int N, int64_t units) {
+    const float* __restrict__ val, const void* __restrict__ W, int64_t ldw, int w_bytes,
+    int w_vec, float* __restrict__ Y, int64_t ldy, int y_vec, int M, int N, int64_t units) {
+  constexpr int esz = kBf16 ? 2 : 4;
   const int lane = threadIdx.x & 63;
   // XCD-contiguous unit order (workgroups go round-robin over the 8 XCDs)
   const int64_t nb = gridDim.x;
@@ -78,10 +110,16 @@ __global__ __launch_bounds__(256) void sparse_add_kernel(
   const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
   if (e0 >= e1) return;
 
-  const int64_t col0 = int64_t(strip) * kStrip + lane * kCPL;
-  const int valid = int(N - col0);
-  float y[kCPL];
+  const int col0 = strip * kStrip + lane * kCPL;
+  const int valid = N - col0;
+  const bool full = w_vec != 0 && valid >= kCPL;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W), 0, w_bytes, kBufferFlags);
+  const int voff = col0 * esz;
+  const int row_bytes = int(ldw) * esz;
+
   float* yrow = Y + int64_t(row) * ldy + col0;
+  float y[kCPL];
   if (valid > 0) {
     if (y_vec && valid >= kCPL) {
       const float4 u0 = *reinterpret_cast<const float4*>(yrow);
@@ -97,37 +135,35 @@ __global__ __launch_bounds__(256) void sparse_add_kernel(
     for (int c = 0; c < kCPL; ++c) y[c] = 0.0f;
   }
 
-  const bool vec = w_vec != 0;
   for (int base = e0; base < e1; base += 64) {
     const int n = (e1 - base) < 64 ? (e1 - base) : 64;
+    // Entries past n are zero-weight dummies on W row 0, so every group is
+    // full and the unrolled loops carry no per-entry branches.
     int mk = 0;
     float mv = 0.0f;
     if (lane < n) {
       mk = col[base + lane];
       mv = val[base + lane];
     }
-    int j = 0;
-    for (; j + 8 <= n; j += 8) {
-      float w[8][kCPL];
+    const int ng = (n + kGroup - 1) / kGroup;
+    WRaw<kBf16> gc[kGroup], gn[kGroup];
+    auto issue = [&](int j0, WRaw<kBf16>* g) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t k = __builtin_amdgcn_readlane(mk, j + u);
-        if (valid > 0) load_w8<kBf16>(W, k * ldw + col0, valid, vec, w[u]);
+      for (int u = 0; u < kGroup; ++u) {
+        const int k = __builtin_amdgcn_readlane(mk, j0 + u);
+        if (full)
+          g[u] = load_full<kBf16>(rs, voff, k * row_bytes);
+        else if (valid > 0)
+          g[u] = load_part<kBf16>(W, int64_t(k) * ldw + col0, valid);
       }
+    };
+    issue(0, gc);
+    for (int g = 0; g < ng; ++g) {
+      if (g + 1 < ng) issue((g + 1) * kGroup, gn);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float v = readlane_f(mv, j + u);
+      for (int u = 0; u < kGroup; ++u) fma_raw<kBf16>(readlane_f(mv, g * kGroup + u), gc[u], y);
 #pragma unroll
-        for (int c = 0; c < kCPL; ++c) y[c] = fmaf(v, w[u][c], y[c]);
-      }
-    }
-    for (; j < n; ++j) {
-      const int64_t k = __builtin_amdgcn_readlane(mk, j);
-      float w[kCPL];
-      if (valid > 0) load_w8<kBf16>(W, k * ldw + col0, valid, vec, w);
-      const float v = readlane_f(mv, j);
-#pragma unroll
-      for (int c = 0; c < kCPL; ++c) y[c] = fmaf(v, w[c], y[c]);
+      for (int u = 0; u < kGroup; ++u) gc[u] = gn[u];
     }
   }
 
@@ -151,18 +187,19 @@ hipError_t launch_sparse_add(const SparseArgs& sp, int64_t M, int64_t N, float* 
   const int64_t units = strips * M;
   const int64_t blocks = (units + 3) / 4;
   const int64_t esz = sp.w_bf16 ? 2 : 4;
-  // 16-byte vector access needs every row start of W and Y 16-byte aligned
-  // (column offsets are multiples of 8 elements).
+  // Vector access of a lane's 8 columns needs every row start of W 16-byte
+  // aligned and of Y 16-byte aligned (column offsets are multiples of 8).
   const bool w_vec = (reinterpret_cast<uintptr_t>(sp.W) % 16 == 0) && ((sp.ldw * esz) % 16 == 0);
-  const bool y_vec = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && ((ldy * 4) % 16 == 0);
+  const bool y_vec = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && (ldy % 4 == 0);
+  const int w_bytes = int(sp.w_rows * sp.ldw * esz);
   if (sp.w_bf16)
     sparse_add_kernel<true><<<dim3(unsigned(blocks)), 256, 0, stream>>>(
-        sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0, int(M),
-        int(N), units);
+        sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_bytes, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0,
+        int(M), int(N), units);
   else
     sparse_add_kernel<false><<<dim3(unsigned(blocks)), 256, 0, stream>>>(
-        sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0, int(M),
-        int(N), units);
+        sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_bytes, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0,
+        int(M), int(N), units);
   return hipGetLastError();
 }
 

@@ -174,19 +174,20 @@ def test_gemm_errors():
         assert gemm(dA=coo(10, null=fld), W=FAKE) == _lib.ERR_NULL
     assert gemm(dA=coo(10), W=FAKE, wdt=3) == _lib.ERR_DTYPE
     assert gemm(dA=coo(10), W=FAKE, ldw=3) == _lib.ERR_SHAPE
+    assert gemm(dA=coo(10), W=FAKE, K=2 ** 20, ldw=2 ** 11) == _lib.ERR_SHAPE
     assert gemm(K=0) == _lib.ERR_SHAPE
     assert gemm(ldy=3) == _lib.ERR_SHAPE
     assert gemm(Aq=MISALIGNED) == _lib.ERR_ALIGN
     assert gemm(Bq=MISALIGNED) == _lib.ERR_ALIGN
 
 
-def sparse_add(dA=None, W=FAKE, wdt=1, ldw=4, M=4, N=4, Y=FAKE, ldy=4):
+def sparse_add(dA=None, W=FAKE, wdt=1, K=8, ldw=4, M=4, N=4, Y=FAKE, ldy=4):
     dA = coo(10) if dA is None else dA
-    return L.fp4lin_sparse_add(ctypes.byref(dA), W, wdt, ldw, M, N, Y, ldy, None)
+    return L.fp4lin_sparse_add(ctypes.byref(dA), W, wdt, K, ldw, M, N, Y, ldy, None)
 
 
 def test_sparse_add_errors():
-    assert L.fp4lin_sparse_add(None, FAKE, 1, 4, 4, 4, FAKE, 4, None) == _lib.ERR_NULL
+    assert L.fp4lin_sparse_add(None, FAKE, 1, 8, 4, 4, 4, FAKE, 4, None) == _lib.ERR_NULL
     for fld in ("col", "val", "row_ptr"):
         assert sparse_add(dA=coo(10, null=fld)) == _lib.ERR_NULL
     assert sparse_add(W=None) == _lib.ERR_NULL
@@ -195,6 +196,8 @@ def test_sparse_add_errors():
     assert sparse_add(M=0) == _lib.ERR_SHAPE
     assert sparse_add(ldw=3) == _lib.ERR_SHAPE
     assert sparse_add(ldy=3) == _lib.ERR_SHAPE
+    assert sparse_add(K=0) == _lib.ERR_SHAPE
+    assert sparse_add(K=2 ** 20, ldw=2 ** 11) == _lib.ERR_SHAPE   # W beyond 2 GiB
 
 
 def forward(A=FAKE, W=FAKE, dt=1, M=4, K=8, N=4, lda=8, ldw=4, q=0.5, Y=FAKE, ldy=4, ws=FAKE,
