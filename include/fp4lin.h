@@ -148,6 +148,8 @@ const char* fp4lin_status_str(fp4lin_status s);
  *   tau      device, 1 float (output)
  *   dA       device arrays (outputs); dA.capacity (host) >= M*K - 1 - k
  *   ws       device workspace of >= fp4lin_select_workspace_bytes(M, K, dt)
+ * M*K must be below 2^32 (32-bit histogram counts) and M*K - 1 - k below 2^31
+ * (int32 COO positions), else FP4LIN_ERR_SHAPE.
  * Errors: NULL, SHAPE, DTYPE, QUANTILE, CAPACITY, ALIGN (ws), WORKSPACE, LAUNCH. */
 fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, int64_t K,
                                     int64_t lda, double q, float* tau, fp4lin_coo dA,

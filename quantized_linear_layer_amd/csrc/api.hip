@@ -12,6 +12,8 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 
 bool bad_dtype(fp4lin_dtype dt) { return dt != FP4LIN_F32 && dt != FP4LIN_BF16; }
+// histogram bins count in 32 bits
+constexpr int64_t kMaxCount = int64_t(1) << 32;
 bool ok_dim(int64_t x) { return x >= 1 && x < kMaxDim; }
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -66,6 +68,7 @@ fp4lin_status fp4lin_forward_layout(int64_t M, int64_t K, int64_t N, fp4lin_dtyp
   if (!ok_dim(M) || !ok_dim(K) || !ok_dim(N)) return FP4LIN_ERR_SHAPE;
   if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
   const int64_t n = M * K;
+  if (n >= kMaxCount) return FP4LIN_ERR_SHAPE;
   const int64_t k = fp4lin_quantile_rank(n, q);
   if (k < 0) return FP4LIN_ERR_QUANTILE;
   const int64_t cap = needed_capacity(n, k);
@@ -126,6 +129,7 @@ fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, i
   if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
   if (!ok_dim(M) || !ok_dim(K) || lda < K) return FP4LIN_ERR_SHAPE;
   const int64_t n = M * K;
+  if (n >= kMaxCount) return FP4LIN_ERR_SHAPE;
   const int64_t k = fp4lin_quantile_rank(n, q);
   if (k < 0) return FP4LIN_ERR_QUANTILE;
   const int64_t cap = needed_capacity(n, k);

@@ -61,6 +61,56 @@ __device__ inline void load8(const typename In::T* __restrict__ p, int64_t valid
   }
 }
 
+// Chunk c (elements c .. c+7) of a row of K elements, zero where it lies past
+// K. kFast: the row is 16-byte aligned and K % 8 == 0, so a chunk is either
+// wholly inside the row or wholly outside; the load address is clamped into
+// the row so that the vector load is unconditional and several of them can be
+// in flight before the first is used. Otherwise elements are loaded one by one.
+template <class In, bool kFast>
+__device__ inline void load_chunk(const typename In::T* __restrict__ row, int64_t c, int64_t K,
+                                  Vec8<In>& v) {
+  if constexpr (kFast) {
+    load8<In, true>(row + (c < K ? c : K - 8), 8, v);
+    if (c >= K) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v.v[i] = typename In::T(0);
+    }
+  } else {
+    load8<In, false>(row + c, K - c, v);
+  }
+}
+
+// Row streaming, one wave per row: a row is read in slabs of CH chunks per
+// lane, chunk j of lane l starting at column c0 + (j * 64 + l) * 8, so each j
+// is one coalesced 64-lane sweep and all CH loads of a slab are issued before
+// the first is used. Reductions over the row stay inside the wave.
+template <class In, bool kFast, int CH>
+__device__ inline void load_wave_slab(const typename In::T* __restrict__ row, int64_t c0,
+                                      int64_t K, Vec8<In> (&v)[CH]) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+    load_chunk<In, kFast>(row, c0 + (int64_t(j) * kWave + lane) * 8, K, v[j]);
+}
+
+// Chunks per lane that cover `cols` columns in one slab, capped at kMax.
+__host__ inline int chunks_per_lane(int64_t cols, int kMax) {
+  int ch = 1;
+  while (ch < kMax && int64_t(ch) * kWave * 8 < cols) ch *= 2;
+  return ch;
+}
+
+// Workgroups of the one-wave-per-row kernels: 4 waves each, striding over
+// rows. A wave takes about kRowsPerWave rows, so that the waves sharing a SIMD
+// drift apart and one wave's loads overlap another's arithmetic (with one row
+// per wave every wave loads, then every wave computes).
+constexpr int kRowWaves = 4;
+constexpr int kRowsPerWave = 1;
+__host__ inline unsigned row_blocks(int64_t M) {
+  const int64_t b = (M + kRowWaves * kRowsPerWave - 1) / (kRowWaves * kRowsPerWave);
+  return unsigned(b < (int64_t(1) << 20) ? b : (int64_t(1) << 20));
+}
+
 // ---------------------------------------------------------------------------
 // E2M1 encoding (round to nearest, ties away from zero, saturating at 6).
 //

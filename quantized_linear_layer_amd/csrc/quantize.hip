@@ -4,15 +4,17 @@
 // ScaleShift paragraphs — scale each vector into the FP4 range, then round to
 // the nearest FP4 value).
 //
-// Rows:    one wave per row; pass 1 finds the (clamped) row amax, pass 2
-//          re-reads the row (from cache) and writes 8 codes per lane as one
+// Rows:    one wave per row; the row (all of it, for K up to 8192 bfloat16
+//          or 4096 float32) is loaded into registers with every 16-byte load
+//          issued before the first is used, reduced to the (clamped) row amax
+//          with wave shuffles, and encoded from the registers, 8 codes per
 //          32-bit store; the zero padding up to roundup(K,128) is written too.
 // Columns: pass 1 takes per-column maxima of the K x N row-major weight with
-//          loads coalesced along N (8 columns per lane) and merges them with
-//          integer atomicMax on the float bits (non-negative floats order like
-//          their bits); pass 2 quantizes a 128 x 64 tile and transposes it
-//          through LDS so that each output row (one column of W) is written as
-//          contiguous 16-byte stores.
+//          loads coalesced along N (8 columns per lane, 8 rows in flight) and
+//          merges them with integer atomicMax on the float bits (non-negative
+//          floats order like their bits); pass 2 gives each thread 8 columns x
+//          8 consecutive rows, so the 8 codes of one column along K are one
+//          32-bit word of the column's packed (N-major) row, stored directly.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -33,40 +35,62 @@ __device__ inline uint32_t encode8(const Vec8<In>& v, int64_t valid, float tau, 
   return word;
 }
 
-template <class In, bool kAligned>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(
+// One wave per row (workgroups of 4 waves striding over rows). The row is
+// read in slabs of CH chunks per lane. When one slab covers the padded row
+// (K up to 512 * CH) it stays in registers between the amax reduction and the
+// encode, so A is read once; longer rows are read a second time for the
+// encode.
+template <class In, int CH>
+__device__ inline void encode_slab(const Vec8<In> (&v)[CH], int64_t c0, int64_t K, int64_t Kp,
+                                   float tau, float inv, uint8_t* __restrict__ qrow) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int64_t c = c0 + (int64_t(j) * kWave + lane) * 8;
+    // chunks in [K, Kp) are zero and encode to the zero padding
+    if (c < Kp) *reinterpret_cast<uint32_t*>(qrow + c / 2) = encode8<In>(v[j], K - c, tau, inv);
+  }
+}
+
+template <class In, int CH>
+__device__ inline float slab_absmax(const Vec8<In> (&v)[CH], float m) {
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(In::widen(v[j].v[i])));
+  return m;
+}
+
+template <class In, bool kFast, int CH>
+__global__ __launch_bounds__(kRowWaves * kWave) void quantize_rows_kernel(
     const typename In::T* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ tau_p, uint8_t* __restrict__ Xq, int64_t ldq,
     float* __restrict__ sX) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t r = int64_t(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (r >= M) return;
   const float tau = tau_p ? *tau_p : __builtin_huge_valf();
-  const typename In::T* row = X + r * ldx;
-  float m = 0.0f;
-  for (int64_t c = int64_t(lane) * 8; c < K; c += kWave * 8) {
-    Vec8<In> v;
-    const int64_t valid = K - c;
-    load8<In, kAligned>(row + c, valid, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(In::widen(v.v[i])));
-  }
-  m = wave_max(m);
-  const float amax = fminf(m, tau);
-  float s, inv;
-  vector_scale(amax, s, inv);
-  if (lane == 0) sX[r] = s;
-  uint8_t* qrow = Xq + r * ldq;
+  const int64_t slab = int64_t(kWave) * CH * 8;
   const int64_t Kp = ldq * 2;
-  for (int64_t c = int64_t(lane) * 8; c < Kp; c += kWave * 8) {
-    const int64_t valid = K - c;
-    uint32_t word = 0;
-    if (valid > 0) {
-      Vec8<In> v;
-      load8<In, kAligned>(row + c, valid, v);
-      word = encode8<In>(v, valid, tau, inv);
+  const int64_t stride = int64_t(gridDim.x) * kRowWaves;
+  for (int64_t r = int64_t(blockIdx.x) * kRowWaves + threadIdx.x / kWave; r < M; r += stride) {
+    const typename In::T* row = X + r * ldx;
+    uint8_t* qrow = Xq + r * ldq;
+    Vec8<In> v[CH];
+    float m = 0.0f;
+    for (int64_t c0 = 0; c0 < K; c0 += slab) {
+      load_wave_slab<In, kFast, CH>(row, c0, K, v);
+      m = slab_absmax<In, CH>(v, m);
     }
-    *reinterpret_cast<uint32_t*>(qrow + c / 2) = word;
+    const float amax = fminf(wave_max(m), tau);
+    float s, inv;
+    vector_scale(amax, s, inv);
+    if ((threadIdx.x & (kWave - 1)) == 0) sX[r] = s;
+    if (Kp <= slab) {
+      encode_slab<In, CH>(v, 0, K, Kp, tau, inv, qrow);
+    } else {
+      for (int64_t c0 = 0; c0 < Kp; c0 += slab) {
+        load_wave_slab<In, kFast, CH>(row, c0, K, v);
+        encode_slab<In, CH>(v, c0, K, Kp, tau, inv, qrow);
+      }
+    }
   }
 }
 
@@ -78,6 +102,7 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
 
 constexpr int kColStrip = 512;    // columns per workgroup (8 per lane)
 constexpr int kColRows = 64;      // rows per workgroup split
+constexpr int kColUnroll = 8;     // loads in flight per thread
 
 template <class In, bool kAligned>
 __global__ __launch_bounds__(256) void colmax_kernel(const typename In::T* __restrict__ W,
@@ -94,11 +119,23 @@ __global__ __launch_bounds__(256) void colmax_kernel(const typename In::T* __res
 #pragma unroll
   for (int i = 0; i < 8; ++i) m[i] = 0.0f;
   if (valid > 0) {
-    for (int64_t k = k0 + wave; k < k1; k += 4) {
-      Vec8<In> v;
-      load8<In, kAligned>(W + k * ldw + c, valid, v);
+    // kColUnroll rows in flight per thread; rows past k1 read as zero
+    for (int64_t kb = k0 + wave; kb < k1; kb += 4 * kColUnroll) {
+      Vec8<In> v[kColUnroll];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(In::widen(v.v[i])));
+      for (int u = 0; u < kColUnroll; ++u) {
+        const int64_t k = kb + 4 * u;
+        if (k < k1) {
+          load8<In, kAligned>(W + k * ldw + c, valid, v[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[u].v[i] = typename In::T(0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kColUnroll; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(In::widen(v[u].v[i])));
     }
   }
 #pragma unroll
@@ -114,15 +151,20 @@ __global__ __launch_bounds__(256) void colmax_kernel(const typename In::T* __res
   }
 }
 
-constexpr int kTK = 128;  // codes along K per tile (64 packed bytes)
-constexpr int kTN = 64;   // columns per tile
+// Pass 2 tile: 128 codes along K x 128 columns. Thread (kg, g) = (t % 16,
+// t / 16) owns rows k0 + 8kg .. +7 and columns n0 + 8g .. +7, so for each of its
+// columns the 8 codes along K form one 32-bit word of that column's packed row
+// (low nibble first), stored directly: a wave's store covers 64 contiguous
+// bytes of each of 4 packed rows, and its loads 64 contiguous bytes of each of
+// 16 rows of W.
+constexpr int kTK = 128;
+constexpr int kTN = 128;
 
 template <class In, bool kAligned>
 __global__ __launch_bounds__(256) void quantize_cols_kernel(
     const typename In::T* __restrict__ W, int64_t K, int64_t N, int64_t ldw,
     const uint32_t* __restrict__ colmax, uint8_t* __restrict__ Wq, int64_t ldq,
     float* __restrict__ sW) {
-  __shared__ uint8_t codes[kTN][kTK + 4];
   __shared__ float inv_s[kTN];
   const int t = threadIdx.x;
   const int64_t n0 = int64_t(blockIdx.x) * kTN;
@@ -136,46 +178,35 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(
     }
     inv_s[t] = inv;
   }
-  __syncthreads();
-  // load + encode: thread owns 8 columns x 4 rows
-  const int g = t & 7;
-  const int r0 = t >> 3;
+  const int kg = t & 15, g = t >> 4;
   const int64_t c = n0 + g * 8;
   const int64_t valid = N - c;
+  const int64_t kr = k0 + kg * 8;
+  Vec8<In> v[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kl = r0 + 32 * i;
-    const int64_t k = k0 + kl;
-    Vec8<In> v;
-    if (k < K && valid > 0) {
-      load8<In, kAligned>(W + k * ldw + c, valid, v);
+  for (int u = 0; u < 8; ++u) {
+    if (kr + u < K && valid > 0) {
+      load8<In, kAligned>(W + (kr + u) * ldw + c, valid, v[u]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v.v[j] = typename In::T(0);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float inv = inv_s[g * 8 + j];
-      const uint32_t code = e2m1_magnitude(fabsf(In::widen(v.v[j])), inv) | (In::sign_bit(v.v[j]) << 3);
-      codes[g * 8 + j][kl] = uint8_t((k < K && j < valid) ? code : 0u);
+      for (int j = 0; j < 8; ++j) v[u].v[j] = typename In::T(0);
     }
   }
   __syncthreads();
-  // transpose out: thread writes 16 bytes (32 codes) of one output row
-  const int nl = t >> 2;
-  const int part = t & 3;
-  const int64_t n = n0 + nl;
-  if (n < N) {
-    uint32_t w[4];
+  if (valid <= 0) return;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t word = 0;
+  for (int j = 0; j < 8; ++j) {
+    if (j >= valid) break;
+    const float inv = inv_s[g * 8 + j];
+    uint32_t word = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) word |= uint32_t(codes[nl][part * 32 + q * 8 + j]) << (4 * j);
-      w[q] = word;
+    for (int u = 0; u < 8; ++u) {
+      // rows past K were loaded as zero and encode to the zero padding
+      const uint32_t code =
+          e2m1_magnitude(fabsf(In::widen(v[u].v[j])), inv) | (In::sign_bit(v[u].v[j]) << 3);
+      word |= code << (4 * u);
     }
-    uint4 out = make_uint4(w[0], w[1], w[2], w[3]);
-    *reinterpret_cast<uint4*>(Wq + n * ldq + k0 / 2 + part * 16) = out;
+    *reinterpret_cast<uint32_t*>(Wq + (c + j) * ldq + kr / 2) = word;
   }
 }
 
@@ -194,28 +225,157 @@ hipError_t run_quantize_weight(const void* Wp, int64_t K, int64_t N, int64_t ldw
   return hipGetLastError();
 }
 
+// bfloat16 rows that are 16-byte aligned with K % 8 == 0 and fit one slab
+// (K <= 512 * CH): the raw 16-byte words are kept as loaded. The row amax is a
+// packed 16-bit integer max of the magnitude bits (finite bfloat16 magnitudes
+// order like their bits), and two codes are encoded per 32-bit word. When
+// 4 * inv is finite, y4 = RN32(|x| * 4inv) equals 4 * RN32(|x| * inv) wherever
+// the code can depend on it (scaling by 4 commutes with rounding in the normal
+// range, and |x| * inv <= 6 cannot overflow), so the code is the table lookup
+// at n = (uint)min(y4, 20) with no NaN to guard against; otherwise (a zero or
+// subnormal row amax) the encoder of the generic path is used.
+__device__ inline uint32_t bf16_pair_code(uint32_t w, float tau, float inv4) {
+  const float lo = fminf(fabsf(__uint_as_float(w << 16)), tau);
+  const float hi = fminf(fabsf(__uint_as_float(w & 0xffff0000u)), tau);
+  const uint32_t nlo = uint32_t(fminf(__fmul_rn(lo, inv4), 20.0f));
+  const uint32_t nhi = uint32_t(fminf(__fmul_rn(hi, inv4), 20.0f));
+  constexpr uint64_t kLut = e2m1_lut();
+  const uint32_t mlo = uint32_t(kLut >> (3u * nlo)) & 7u;
+  const uint32_t mhi = uint32_t(kLut >> (3u * nhi)) & 7u;
+  return mlo | (mhi << 4) | ((w >> 12) & 0x8u) | ((w >> 24) & 0x80u);
+}
+
+__device__ inline uint32_t bf16_pair_code_slow(uint32_t w, float tau, float inv) {
+  const float lo = fminf(fabsf(__uint_as_float(w << 16)), tau);
+  const float hi = fminf(fabsf(__uint_as_float(w & 0xffff0000u)), tau);
+  return e2m1_magnitude(lo, inv) | (e2m1_magnitude(hi, inv) << 4) | ((w >> 12) & 0x8u) |
+         ((w >> 24) & 0x80u);
+}
+
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, kWave);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+template <int CH>
+__global__ __launch_bounds__(kRowWaves * kWave) void quantize_rows_bf16_kernel(
+    const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
+    const float* __restrict__ tau_p, uint8_t* __restrict__ Xq, int64_t ldq,
+    float* __restrict__ sX) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const float tau = tau_p ? *tau_p : __builtin_huge_valf();
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t Kp = ldq * 2;
+  const int64_t stride = int64_t(gridDim.x) * kRowWaves;
+  for (int64_t r = int64_t(blockIdx.x) * kRowWaves + threadIdx.x / kWave; r < M; r += stride) {
+    const uint16_t* row = X + r * ldx;
+    uint4 w[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int64_t c = (int64_t(j) * kWave + lane) * 8;
+      w[j] = *reinterpret_cast<const uint4*>(row + (c < K ? c : K - 8));
+      if (c >= K) w[j] = make_uint4(0, 0, 0, 0);
+    }
+    u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t q[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, q[i] & 0x7fff7fffu));
+    }
+    const uint32_t mk = wave_max_u32(uint32_t(m2.x > m2.y ? m2.x : m2.y));
+    const float amax = fminf(__uint_as_float(mk << 16), tau);
+    float s, inv;
+    vector_scale(amax, s, inv);
+    if (lane == 0) sX[r] = s;
+    const float inv4 = __fmul_rn(inv, 4.0f);
+    uint8_t* qrow = Xq + r * ldq;
+    if (inv4 < __builtin_huge_valf()) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int64_t c = (int64_t(j) * kWave + lane) * 8;
+        if (c < Kp)
+          *reinterpret_cast<uint32_t*>(qrow + c / 2) =
+              bf16_pair_code(w[j].x, tau, inv4) | (bf16_pair_code(w[j].y, tau, inv4) << 8) |
+              (bf16_pair_code(w[j].z, tau, inv4) << 16) | (bf16_pair_code(w[j].w, tau, inv4) << 24);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int64_t c = (int64_t(j) * kWave + lane) * 8;
+        if (c < Kp)
+          *reinterpret_cast<uint32_t*>(qrow + c / 2) =
+              bf16_pair_code_slow(w[j].x, tau, inv) | (bf16_pair_code_slow(w[j].y, tau, inv) << 8) |
+              (bf16_pair_code_slow(w[j].z, tau, inv) << 16) |
+              (bf16_pair_code_slow(w[j].w, tau, inv) << 24);
+      }
+    }
+  }
+}
+
+template <class In, bool kFast>
+hipError_t run_quantize_rows(const void* Xp, int64_t M, int64_t K, int64_t ldx, const float* tau,
+                             uint8_t* Xq, int64_t ldq, float* sX, hipStream_t stream) {
+  const typename In::T* X = static_cast<const typename In::T*>(Xp);
+  const unsigned blocks = row_blocks(M);
+  // rows up to 512 * CH padded columns kept in registers (bfloat16: 8192, float32: 4096)
+  constexpr int kMaxCh = In::kBytes == 2 ? 16 : 8;
+  const int ch = chunks_per_lane(ldq * 2, kMaxCh);
+  if constexpr (In::kBytes == 2 && kFast) {
+    if (int64_t(ch) * kWave * 8 >= ldq * 2) {
+      switch (ch) {
+        case 1: quantize_rows_bf16_kernel<1><<<blocks, kRowWaves * kWave, 0, stream>>>(X, M, K, ldx, tau, Xq, ldq, sX); break;
+        case 2: quantize_rows_bf16_kernel<2><<<blocks, kRowWaves * kWave, 0, stream>>>(X, M, K, ldx, tau, Xq, ldq, sX); break;
+        case 4: quantize_rows_bf16_kernel<4><<<blocks, kRowWaves * kWave, 0, stream>>>(X, M, K, ldx, tau, Xq, ldq, sX); break;
+        case 8: quantize_rows_bf16_kernel<8><<<blocks, kRowWaves * kWave, 0, stream>>>(X, M, K, ldx, tau, Xq, ldq, sX); break;
+        case 16: quantize_rows_bf16_kernel<16><<<blocks, kRowWaves * kWave, 0, stream>>>(X, M, K, ldx, tau, Xq, ldq, sX); break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
+  }
+  switch (ch) {
+#define FP4LIN_QROWS(CH)                                                                      \
+  case CH:                                                                                    \
+    quantize_rows_kernel<In, kFast, CH><<<blocks, kRowWaves * kWave, 0, stream>>>(            \
+        X, M, K, ldx, tau, Xq, ldq, sX);                                                      \
+    break;
+    FP4LIN_QROWS(1)
+    FP4LIN_QROWS(2)
+    FP4LIN_QROWS(4)
+    FP4LIN_QROWS(8)
+#undef FP4LIN_QROWS
+    case 16:
+      if constexpr (kMaxCh >= 16) {
+        quantize_rows_kernel<In, kFast, 16><<<blocks, kRowWaves * kWave, 0, stream>>>(
+            X, M, K, ldx, tau, Xq, ldq, sX);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize_rows(const void* X, bool bf16, int64_t M, int64_t K, int64_t ldx,
                                 const float* tau, uint8_t* Xq, int64_t ldq, float* sX,
                                 hipStream_t stream) {
   const int esz = bf16 ? 2 : 4;
-  const bool aligned = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ((ldx * esz) % 16 == 0);
-  const unsigned blocks = unsigned((M + 3) / 4);
-  if (bf16) {
-    const uint16_t* x = static_cast<const uint16_t*>(X);
-    if (aligned)
-      quantize_rows_kernel<BF16In, true><<<blocks, 256, 0, stream>>>(x, M, K, ldx, tau, Xq, ldq, sX);
-    else
-      quantize_rows_kernel<BF16In, false><<<blocks, 256, 0, stream>>>(x, M, K, ldx, tau, Xq, ldq, sX);
-  } else {
-    const float* x = static_cast<const float*>(X);
-    if (aligned)
-      quantize_rows_kernel<F32In, true><<<blocks, 256, 0, stream>>>(x, M, K, ldx, tau, Xq, ldq, sX);
-    else
-      quantize_rows_kernel<F32In, false><<<blocks, 256, 0, stream>>>(x, M, K, ldx, tau, Xq, ldq, sX);
-  }
-  return hipGetLastError();
+  const bool fast = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && ((ldx * esz) % 16 == 0) &&
+                    (K % 8 == 0);
+  if (bf16)
+    return fast ? run_quantize_rows<BF16In, true>(X, M, K, ldx, tau, Xq, ldq, sX, stream)
+                : run_quantize_rows<BF16In, false>(X, M, K, ldx, tau, Xq, ldq, sX, stream);
+  return fast ? run_quantize_rows<F32In, true>(X, M, K, ldx, tau, Xq, ldq, sX, stream)
+              : run_quantize_rows<F32In, false>(X, M, K, ldx, tau, Xq, ldq, sX, stream);
 }
 
 size_t weight_workspace_bytes(int64_t N) { return size_t(N) * 4; }

@@ -5,10 +5,10 @@
 // only where A was clamped; its product with the unquantized weight is added
 // to the FP4 product so that the outliers are not lost.
 //
-// One wave owns one (row i, 512-column strip) unit: it reads Y[i, strip] (the
-// scaled FP4 product the GEMM kernel wrote), adds
-//   sum over the row's non-zeros (k ascending) of val * W[k, strip]
-// with fp32 fused multiply-add, and writes it back. Each lane owns 8
+// One wave owns one (row i, 512-column strip) unit: it forms
+//   s = sum over the row's non-zeros (k ascending) of val * W[k, strip]
+// from 0 with fp32 fused multiply-add, then adds s once to Y[i, strip] (the
+// scaled FP4 product the GEMM kernel wrote). Each lane owns 8
 // consecutive columns, so a non-zero costs one 16-byte (bf16) W load per lane,
 // addressed with the row offset in the scalar operand of a buffer load. The
 // row's non-zeros are fetched 64 at a time (one per lane) and consumed in
@@ -119,21 +119,9 @@ __global__ __launch_bounds__(256) void sparse_add_kernel(
   const int row_bytes = int(ldw) * esz;
 
   float* yrow = Y + int64_t(row) * ldy + col0;
-  float y[kCPL];
-  if (valid > 0) {
-    if (y_vec && valid >= kCPL) {
-      const float4 u0 = *reinterpret_cast<const float4*>(yrow);
-      const float4 u1 = *reinterpret_cast<const float4*>(yrow + 4);
-      y[0] = u0.x; y[1] = u0.y; y[2] = u0.z; y[3] = u0.w;
-      y[4] = u1.x; y[5] = u1.y; y[6] = u1.z; y[7] = u1.w;
-    } else {
+  float y[kCPL];  // the compensation sum, from 0; added to Y at the end
 #pragma unroll
-      for (int c = 0; c < kCPL; ++c) y[c] = (c < valid) ? yrow[c] : 0.0f;
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < kCPL; ++c) y[c] = 0.0f;
-  }
+  for (int c = 0; c < kCPL; ++c) y[c] = 0.0f;
 
   for (int base = e0; base < e1; base += 64) {
     const int n = (e1 - base) < 64 ? (e1 - base) : 64;
@@ -169,12 +157,16 @@ __global__ __launch_bounds__(256) void sparse_add_kernel(
 
   if (valid > 0) {
     if (y_vec && valid >= kCPL) {
-      *reinterpret_cast<float4*>(yrow) = make_float4(y[0], y[1], y[2], y[3]);
-      *reinterpret_cast<float4*>(yrow + 4) = make_float4(y[4], y[5], y[6], y[7]);
+      const float4 u0 = *reinterpret_cast<const float4*>(yrow);
+      const float4 u1 = *reinterpret_cast<const float4*>(yrow + 4);
+      *reinterpret_cast<float4*>(yrow) = make_float4(
+          __fadd_rn(u0.x, y[0]), __fadd_rn(u0.y, y[1]), __fadd_rn(u0.z, y[2]), __fadd_rn(u0.w, y[3]));
+      *reinterpret_cast<float4*>(yrow + 4) = make_float4(
+          __fadd_rn(u1.x, y[4]), __fadd_rn(u1.y, y[5]), __fadd_rn(u1.z, y[6]), __fadd_rn(u1.w, y[7]));
     } else {
 #pragma unroll
       for (int c = 0; c < kCPL; ++c)
-        if (c < valid) yrow[c] = y[c];
+        if (c < valid) yrow[c] = __fadd_rn(yrow[c], y[c]);
     }
   }
 }

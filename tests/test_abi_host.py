@@ -90,6 +90,10 @@ def test_workspace_layout_consistent():
     assert L.fp4lin_workspace_bytes(0, 5, 7, 1, 0.5) == 0
     assert L.fp4lin_workspace_bytes(3, 5, 7, 9, 0.5) == 0
     assert L.fp4lin_workspace_bytes(3, 5, 7, 1, 2.0) == 0
+    # M*K >= 2^32 is refused (32-bit histogram counts) even when the COO is small
+    o = _lib.ForwardOffsets()
+    assert L.fp4lin_forward_layout(2 ** 20, 2 ** 12, 8, 1, 1.0, ctypes.byref(o)) == _lib.ERR_SHAPE
+    assert L.fp4lin_forward_layout(2 ** 20 - 1, 2 ** 12, 8, 1, 1.0, ctypes.byref(o)) == 0
 
 
 def test_status_strings():
@@ -122,6 +126,8 @@ def test_select_errors():
     assert select(K=-1) == _lib.ERR_SHAPE
     assert select(lda=7) == _lib.ERR_SHAPE
     assert select(M=2 ** 31) == _lib.ERR_SHAPE
+    # M*K >= 2^32 overflows the 32-bit histogram counts, even with a small COO
+    assert select(M=2 ** 20, K=2 ** 12, lda=2 ** 12, q=1.0) == _lib.ERR_SHAPE
     assert select(q=-0.5) == _lib.ERR_QUANTILE
     assert select(q=float("nan")) == _lib.ERR_QUANTILE
     # n = 32, q = 0.5 -> k = 15, capacity needed 16
