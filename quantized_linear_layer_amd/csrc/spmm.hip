@@ -8,15 +8,15 @@
 // One wave owns one (row i, 512-column strip) unit: it forms
 //   s = sum over the row's non-zeros (k ascending) of val * W[k, strip]
 // from 0 with fp32 fused multiply-add, then adds s once to Y[i, strip] (the
-// scaled FP4 product the GEMM kernel wrote). Each lane owns 8
-// consecutive columns, so a non-zero costs one 16-byte (bf16) W load per lane,
-// addressed with the row offset in the scalar operand of a buffer load. The
-// row's non-zeros are fetched 64 at a time (one per lane) and consumed in
-// groups of eight W row segments, the next group requested before the current
-// one is multiplied. Units are ordered strip by strip and each XCD takes a
-// contiguous run of that order, so the waves running together on an XCD read
-// the same W strip through its L2. Rows without non-zeros are left
-// untouched.
+// scaled FP4 product the GEMM kernel wrote; its load is issued first, so that
+// it arrives while the gathers run). Each lane owns 8 consecutive columns, so
+// a non-zero costs one 16-byte (bf16) W load per lane, addressed with the row
+// offset in the scalar operand of a buffer load; the row's entries are read
+// with scalar loads. The gathers go out in small groups, the next group
+// requested before the current one is multiplied. Units are ordered strip by
+// strip and each XCD takes a contiguous run of that order, so the waves
+// running together on an XCD read the same W strip through its L2. Rows
+// without non-zeros are left untouched.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -26,7 +26,11 @@ namespace {
 
 constexpr int kCPL = 8;                // columns per lane
 constexpr int kStrip = 64 * kCPL;      // columns per unit
-constexpr int kGroup = 8;              // W row segments per load group (two groups in flight)
+// W row segments per load group (two groups in flight). Small groups keep the
+// register count low enough for 8 waves per SIMD: each wave's work is a short
+// chain (row bounds, entries, gathers, Y), so many independent waves hide the
+// latency better than deep per-wave pipelines do.
+constexpr int kGroup = 4;
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
 
 // W words of one non-zero for this lane's 8 columns: bf16 -> one 16-byte
@@ -87,10 +91,6 @@ __device__ inline WRaw<kBf16> load_part(const void* __restrict__ W, int64_t off,
   return r;
 }
 
-__device__ inline float readlane_f(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
 template <bool kBf16>
 __global__ __launch_bounds__(256) void sparse_add_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
@@ -122,51 +122,64 @@ __global__ __launch_bounds__(256) void sparse_add_kernel(
   float y[kCPL];  // the compensation sum, from 0; added to Y at the end
 #pragma unroll
   for (int c = 0; c < kCPL; ++c) y[c] = 0.0f;
-
-  for (int base = e0; base < e1; base += 64) {
-    const int n = (e1 - base) < 64 ? (e1 - base) : 64;
-    // Entries past n are zero-weight dummies on W row 0, so every group is
-    // full and the unrolled loops carry no per-entry branches.
-    int mk = 0;
-    float mv = 0.0f;
-    if (lane < n) {
-      mk = col[base + lane];
-      mv = val[base + lane];
+  // Y segment requested before the gathers so that its latency is hidden
+  float yo[kCPL];
+  if (valid > 0) {
+    if (y_vec && valid >= kCPL) {
+      const float4 u0 = *reinterpret_cast<const float4*>(yrow);
+      const float4 u1 = *reinterpret_cast<const float4*>(yrow + 4);
+      yo[0] = u0.x; yo[1] = u0.y; yo[2] = u0.z; yo[3] = u0.w;
+      yo[4] = u1.x; yo[5] = u1.y; yo[6] = u1.z; yo[7] = u1.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < kCPL; ++c) yo[c] = (c < valid) ? yrow[c] : 0.0f;
     }
-    const int ng = (n + kGroup - 1) / kGroup;
-    WRaw<kBf16> gc[kGroup], gn[kGroup];
-    auto issue = [&](int j0, WRaw<kBf16>* g) {
+  }
+
+  // The row's non-zeros are read with wave-uniform (scalar) loads, so the W
+  // row offset is a scalar operand of each buffer load and the values are
+  // scalar operands of the FMAs. Loads go out in groups of kGroup, the next
+  // group before the current one is multiplied; entries past the row's end
+  // are zero-weight dummies on W row 0, so every group is full.
+  const int n = e1 - e0;
+  const int ng = (n + kGroup - 1) / kGroup;
+  WRaw<kBf16> gc[kGroup], gn[kGroup];
+  float vc[kGroup], vn[kGroup];
+  auto issue = [&](int j0, WRaw<kBf16>* g, float* vv) {
 #pragma unroll
-      for (int u = 0; u < kGroup; ++u) {
-        const int k = __builtin_amdgcn_readlane(mk, j0 + u);
-        if (full)
-          g[u] = load_full<kBf16>(rs, voff, k * row_bytes);
-        else if (valid > 0)
-          g[u] = load_part<kBf16>(W, int64_t(k) * ldw + col0, valid);
-      }
-    };
-    issue(0, gc);
-    for (int g = 0; g < ng; ++g) {
-      if (g + 1 < ng) issue((g + 1) * kGroup, gn);
+    for (int u = 0; u < kGroup; ++u) {
+      const int e = e0 + j0 + u;
+      const bool ok = e < e1;
+      const int k = ok ? col[e] : 0;
+      vv[u] = ok ? val[e] : 0.0f;
+      if (full)
+        g[u] = load_full<kBf16>(rs, voff, k * row_bytes);
+      else if (valid > 0)
+        g[u] = load_part<kBf16>(W, int64_t(k) * ldw + col0, valid);
+    }
+  };
+  issue(0, gc, vc);
+  for (int g = 0; g < ng; ++g) {
+    if (g + 1 < ng) issue((g + 1) * kGroup, gn, vn);
 #pragma unroll
-      for (int u = 0; u < kGroup; ++u) fma_raw<kBf16>(readlane_f(mv, g * kGroup + u), gc[u], y);
+    for (int u = 0; u < kGroup; ++u) fma_raw<kBf16>(vc[u], gc[u], y);
 #pragma unroll
-      for (int u = 0; u < kGroup; ++u) gc[u] = gn[u];
+    for (int u = 0; u < kGroup; ++u) {
+      gc[u] = gn[u];
+      vc[u] = vn[u];
     }
   }
 
   if (valid > 0) {
     if (y_vec && valid >= kCPL) {
-      const float4 u0 = *reinterpret_cast<const float4*>(yrow);
-      const float4 u1 = *reinterpret_cast<const float4*>(yrow + 4);
       *reinterpret_cast<float4*>(yrow) = make_float4(
-          __fadd_rn(u0.x, y[0]), __fadd_rn(u0.y, y[1]), __fadd_rn(u0.z, y[2]), __fadd_rn(u0.w, y[3]));
+          __fadd_rn(yo[0], y[0]), __fadd_rn(yo[1], y[1]), __fadd_rn(yo[2], y[2]), __fadd_rn(yo[3], y[3]));
       *reinterpret_cast<float4*>(yrow + 4) = make_float4(
-          __fadd_rn(u1.x, y[4]), __fadd_rn(u1.y, y[5]), __fadd_rn(u1.z, y[6]), __fadd_rn(u1.w, y[7]));
+          __fadd_rn(yo[4], y[4]), __fadd_rn(yo[5], y[5]), __fadd_rn(yo[6], y[6]), __fadd_rn(yo[7], y[7]));
     } else {
 #pragma unroll
       for (int c = 0; c < kCPL; ++c)
-        if (c < valid) yrow[c] = __fadd_rn(yrow[c], y[c]);
+        if (c < valid) yrow[c] = __fadd_rn(yo[c], y[c]);
     }
   }
 }
