@@ -34,6 +34,11 @@
 //    the 8 XCDs (own L2 each; workgroups are dispatched round-robin over them)
 //    takes a contiguous run of that order, so concurrent tiles on an XCD share
 //    A rows and B columns in its L2.
+//  * The scaled tile leaves through LDS: each wave writes two 32 x 32
+//    fragments at a time into its own block of the (then idle) stage buffers
+//    and stores them back as rows, 16 bytes per lane, so Y is written with
+//    full-width stores of whole 256-byte row segments (4x fewer store
+//    instructions than storing from the MFMA layout).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -243,11 +248,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   }
 
   // ---- epilogue -------------------------------------------------------------
-  // Scales are applied in the MFMA output layout and the tile is stored
-  // straight from registers: for accumulator element r, lanes 0..31 hold 32
-  // consecutive columns of one row and lanes 32..63 the same columns four rows
-  // down, so each store instruction writes two full 128-byte row segments.
-  // All row and column scales of the lane are loaded before any is used.
+  // Scales are applied in the MFMA output layout: for accumulator element r,
+  // lanes 0..31 hold 32 consecutive columns of one row and lanes 32..63 the
+  // same columns four rows down. All row and column scales of the lane are
+  // loaded before any is used.
   const int col_l = lane & 31;
   float sb[FN];
 #pragma unroll
@@ -263,16 +267,45 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
       const int gr = m0 + wm * (FM * 32) + fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       sa[fm][r] = (gr < M) ? sA[gr] : 0.0f;
     }
+  // Output through a wave-private LDS block (the stage buffers are free after
+  // the main loop's last barrier): two 32x32 fragments at a time are written
+  // in the MFMA layout, read back as rows and stored 16 bytes per lane.
+  constexpr int kER = 72;  // padded row of a 32 x 64 chunk (floats)
+  static_assert((NT / kWave) * 32 * kER * 4 <= 2 * C::kStageBytes,
+                "epilogue chunks fit the stage buffers");
+  static_assert(FN % 2 == 0, "fragments are staged in pairs");
+  float* eb = reinterpret_cast<float*>(lds) + wave * (32 * kER);
+  const bool y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy & 3) == 0);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int gc = n0 + wn * (FN * 32) + fn * 32 + col_l;
+    for (int fp = 0; fp < FN; fp += 2) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gr = m0 + wm * (FM * 32) + fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (gr < M && gc < N)
-          Y[int64_t(gr) * ldy + gc] = __fmul_rn(__fmul_rn(acc[fm][fn][r], sa[fm][r]), sb[fn]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          eb[rl * kER + h * 32 + col_l] = __fmul_rn(__fmul_rn(acc[fm][fp + h][r], sa[fm][r]), sb[fp + h]);
+        }
+      const int row_base = m0 + wm * (FM * 32) + fm * 32;
+      const int col_base = n0 + wn * (FN * 32) + fp * 32;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rl = it * 4 + (lane >> 4);
+        const int cl = (lane & 15) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(eb + rl * kER + cl);
+        const int gr = row_base + rl, gc = col_base + cl;
+        if (gr < M) {
+          float* dst = Y + int64_t(gr) * ldy + gc;
+          if (y_vec && gc + 4 <= N) {
+            *reinterpret_cast<float4*>(dst) = v;
+          } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (gc + c < N) dst[c] = vv[c];
+          }
+        }
       }
     }
 }
