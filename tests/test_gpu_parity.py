@@ -467,3 +467,50 @@ def test_gemm_equals_gemm_then_sparse_add(ql):
     ql.fp4lin_sparse_add(coo, W, Y2)
     t.cuda.synchronize()
     assert np.array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# output and weight layouts: padded / unaligned leading dimensions, ragged N
+# ---------------------------------------------------------------------------
+def upload_coo(ql, delta):
+    nz = max(delta.nnz, 1)
+    pad = lambda a, dt: np.concatenate([np.asarray(a, dt), np.zeros(nz - len(a), dt)])
+    return ql.CooBuffers(upload_i32(pad(delta.row, np.int32)), upload_i32(pad(delta.col, np.int32)),
+                         upload_f32(pad(delta.val32, np.float32)), upload_i32(delta.row_ptr))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("N,ldy_pad,ldw_pad", [(203, 5, 3), (256, 4, 0), (130, 2, 1),
+                                               (517, 3, 8), (8, 0, 5)])
+def test_gemm_compensation_padded_layouts(ql, dtype, N, ldy_pad, ldw_pad):
+    """fp4lin_gemm with dA into a padded (possibly unaligned) Y, with a padded
+    (possibly unaligned) W: the element paths of the epilogue and of the
+    compensation run, the result matches the oracle, and no padding column of
+    Y is written."""
+    t = torch()
+    M, K = 150, 300
+    log(f"gemm layouts {dtype} N={N} ldy=N+{ldy_pad} ldw=N+{ldw_pad}")
+    rng = np.random.default_rng(N * 7 + ldy_pad * 3 + ldw_pad)
+    A = wl.random_matrix(rng, M, K, dtype, dist="t3")
+    W = wl.random_matrix(rng, K, N, dtype, scale=0.02)
+    ops = O.forward_operands(A.f32, W.f32, 0.97)
+    Aq, Bq = upload_u8(O.pack_rows(ops.codesA)), upload_u8(O.pack_rows(ops.codesW))
+    coo = upload_coo(ql, ops.delta)
+    Wd = padded(to_device(W), N + ldw_pad)
+    sentinel = float("nan")
+    Ybuf = t.full((M, N + ldy_pad), sentinel, dtype=t.float32, device="cuda:0")
+    Y = Ybuf[:, :N]
+    ql.fp4lin_gemm(Aq, upload_f32(ops.sA), Bq, upload_f32(ops.sW), M, N, K, coo, Wd, Y)
+    t.cuda.synchronize()
+    full = host(Ybuf)
+    if ldy_pad:
+        assert np.isnan(full[:, N:]).all(), "a padding column of Y was written"
+    err = O.rel_fro(full[:, :N], O.forward_output(ops, W.f32))
+    assert err <= Y_TOL, err
+    # the same through fp4lin_gemm (no dA) + fp4lin_sparse_add: same bits
+    Ybuf2 = t.full((M, N + ldy_pad), sentinel, dtype=t.float32, device="cuda:0")
+    Y2 = Ybuf2[:, :N]
+    ql.fp4lin_gemm(Aq, upload_f32(ops.sA), Bq, upload_f32(ops.sW), M, N, K, None, None, Y2)
+    ql.fp4lin_sparse_add(coo, Wd, Y2)
+    t.cuda.synchronize()
+    assert np.array_equal(host(Ybuf2).view(np.uint32), full.view(np.uint32))
