@@ -5,18 +5,21 @@
 // only where A was clamped; its product with the unquantized weight is added
 // to the FP4 product so that the outliers are not lost.
 //
-// One wave owns one (row i, 512-column strip) unit: it forms
+// One single-wave workgroup owns one (row i, 512-column strip) unit: it forms
 //   s = sum over the row's non-zeros (k ascending) of val * W[k, strip]
 // from 0 with fp32 fused multiply-add, then adds s once to Y[i, strip] (the
 // scaled FP4 product the GEMM kernel wrote; its load is issued first, so that
 // it arrives while the gathers run). Each lane owns 8 consecutive columns, so
 // a non-zero costs one 16-byte (bf16) W load per lane, addressed with the row
 // offset in the scalar operand of a buffer load; the row's entries are read
-// with scalar loads. The gathers go out in small groups, the next group
-// requested before the current one is multiplied. Units are ordered strip by
-// strip and each XCD takes a contiguous run of that order, so the waves
-// running together on an XCD read the same W strip through its L2. Rows
-// without non-zeros are left untouched.
+// with scalar loads. The gathers go out in groups of four, software-pipelined:
+// the entries of group g+2 are requested while the W rows of group g+1 are in
+// flight and group g is multiplied. Y is read and written with non-temporal
+// accesses, so the stream of Y lines does not evict the W strip from L2.
+// Units are ordered strip by strip and each XCD takes a contiguous run of that
+// order, so the waves running together on an XCD read the same W strip
+// through its L2. Single-wave workgroups free their slot as soon as their own
+// row is done. Rows without non-zeros are left untouched.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -91,19 +94,30 @@ __device__ inline WRaw<kBf16> load_part(const void* __restrict__ W, int64_t off,
   return r;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Y is streamed once per unit: non-temporal accesses keep it from evicting the
+// W strip that the gathers reuse from L2.
+__device__ inline f32x4 load_y4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ inline void store_y4(f32x4 v, float* p) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
 template <bool kBf16>
-__global__ __launch_bounds__(256) void sparse_add_kernel(
+__global__ __launch_bounds__(64) void sparse_add_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
     const float* __restrict__ val, const void* __restrict__ W, int64_t ldw, int w_bytes,
-    int w_vec, float* __restrict__ Y, int64_t ldy, int y_vec, int M, int N, int64_t units) {
+    int w_vec, float* __restrict__ Y, int64_t ldy, int y_vec, int M, int N, int64_t unit_base,
+    int64_t units) {
   constexpr int esz = kBf16 ? 2 : 4;
   const int lane = threadIdx.x & 63;
   // XCD-contiguous unit order (workgroups go round-robin over the 8 XCDs)
   const int64_t nb = gridDim.x;
   const int64_t xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
   const int64_t base_b = nb >> 3, rem = nb & 7;
-  const int64_t blk = xcd * base_b + (xcd < rem ? xcd : rem) + idx;
-  const int64_t unit = blk * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t unit = unit_base + xcd * base_b + (xcd < rem ? xcd : rem) + idx;
   if (unit >= units) return;
   const int strip = int(unit / M);
   const int row = int(unit - int64_t(strip) * M);
@@ -112,70 +126,127 @@ __global__ __launch_bounds__(256) void sparse_add_kernel(
 
   const int col0 = strip * kStrip + lane * kCPL;
   const int valid = N - col0;
-  const bool full = w_vec != 0 && valid >= kCPL;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W), 0, w_bytes, kBufferFlags);
   const int voff = col0 * esz;
   const int row_bytes = int(ldw) * esz;
+  const bool y_full = y_vec && valid >= kCPL;
 
   float* yrow = Y + int64_t(row) * ldy + col0;
-  float y[kCPL];  // the compensation sum, from 0; added to Y at the end
-#pragma unroll
-  for (int c = 0; c < kCPL; ++c) y[c] = 0.0f;
   // Y segment requested before the gathers so that its latency is hidden
   float yo[kCPL];
   if (valid > 0) {
-    if (y_vec && valid >= kCPL) {
-      const float4 u0 = *reinterpret_cast<const float4*>(yrow);
-      const float4 u1 = *reinterpret_cast<const float4*>(yrow + 4);
-      yo[0] = u0.x; yo[1] = u0.y; yo[2] = u0.z; yo[3] = u0.w;
-      yo[4] = u1.x; yo[5] = u1.y; yo[6] = u1.z; yo[7] = u1.w;
+    if (y_full) {
+      const f32x4 u0 = load_y4(yrow), u1 = load_y4(yrow + 4);
+      yo[0] = u0[0]; yo[1] = u0[1]; yo[2] = u0[2]; yo[3] = u0[3];
+      yo[4] = u1[0]; yo[5] = u1[1]; yo[6] = u1[2]; yo[7] = u1[3];
     } else {
 #pragma unroll
       for (int c = 0; c < kCPL; ++c) yo[c] = (c < valid) ? yrow[c] : 0.0f;
     }
   }
 
-  // The row's non-zeros are read with wave-uniform (scalar) loads, so the W
-  // row offset is a scalar operand of each buffer load and the values are
-  // scalar operands of the FMAs. Loads go out in groups of kGroup, the next
-  // group before the current one is multiplied; entries past the row's end
-  // are zero-weight dummies on W row 0, so every group is full.
+  float y[kCPL];  // the compensation sum, from 0; added to Y at the end
+#pragma unroll
+  for (int c = 0; c < kCPL; ++c) y[c] = 0.0f;
+
   const int n = e1 - e0;
   const int ng = (n + kGroup - 1) / kGroup;
-  WRaw<kBf16> gc[kGroup], gn[kGroup];
-  float vc[kGroup], vn[kGroup];
-  auto issue = [&](int j0, WRaw<kBf16>* g, float* vv) {
+  const int32_t* __restrict__ cp = col + e0;
+  const float* __restrict__ vp = val + e0;
+  // Entries of group g (wave-uniform, scalar loads). In the row's last group
+  // the indexes are clamped to its last entry and the extra slots get weight
+  // 0 (an integer mask, so the selection stays scalar), so every group is
+  // full and every read stays inside the row.
+  auto entries = [&](int g, int (&kk)[kGroup], float (&vv)[kGroup]) {
+    const int j0 = g * kGroup;
+    if (j0 + kGroup <= n) {
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-      const int e = e0 + j0 + u;
-      const bool ok = e < e1;
-      const int k = ok ? col[e] : 0;
-      vv[u] = ok ? val[e] : 0.0f;
-      if (full)
-        g[u] = load_full<kBf16>(rs, voff, k * row_bytes);
-      else if (valid > 0)
-        g[u] = load_part<kBf16>(W, int64_t(k) * ldw + col0, valid);
+      for (int u = 0; u < kGroup; ++u) {
+        kk[u] = cp[j0 + u];
+        vv[u] = vp[j0 + u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        const int j = min(j0 + u, n - 1);
+        kk[u] = cp[j];
+        const uint32_t keep = (j0 + u < n) ? 0xffffffffu : 0u;
+        vv[u] = __uint_as_float(__float_as_uint(vp[j]) & keep);
+      }
     }
   };
-  issue(0, gc, vc);
-  for (int g = 0; g < ng; ++g) {
-    if (g + 1 < ng) issue((g + 1) * kGroup, gn, vn);
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) fma_raw<kBf16>(vc[u], gc[u], y);
+  auto gather = [&](const int (&kk)[kGroup], WRaw<kBf16> (&w)[kGroup]) {
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
-      gc[u] = gn[u];
-      vc[u] = vn[u];
+      w[u] = load_full<kBf16>(rs, voff, kk[u] * row_bytes);
+    }
+  };
+  auto multiply = [&](const float (&vv)[kGroup], const WRaw<kBf16> (&w)[kGroup]) {
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) fma_raw<kBf16>(vv[u], w[u], y);
+  };
+
+  // Every lane holds 8 columns or none (no lane straddles N), and W rows are
+  // 16-byte aligned: one 16-byte buffer load per entry and lane. Lanes past N
+  // load harmlessly (inside the buffer, or zero past its end) and store nothing.
+  const bool vec_path = w_vec != 0 && ((N % kCPL) == 0 || (strip + 1) * kStrip <= N);
+  if (vec_path) {
+    // Software pipeline over groups, two W buffers used in turn: the entries
+    // of group g+2 are requested while the W rows of group g+1 are in flight
+    // and group g is multiplied.
+    int kA[kGroup], kB[kGroup];
+    float vA[kGroup], vB[kGroup];
+    WRaw<kBf16> wA[kGroup], wB[kGroup];
+    entries(0, kA, vA);
+    gather(kA, wA);
+    if (ng > 1) entries(1, kB, vB);
+    for (int g = 0; g < ng; g += 2) {
+      int k2[kGroup];
+      float v2[kGroup];
+      if (g + 1 < ng) gather(kB, wB);
+      if (g + 2 < ng) entries(g + 2, k2, v2);
+      multiply(vA, wA);
+      if (g + 1 >= ng) break;
+      if (g + 2 < ng) gather(k2, wA);
+      if (g + 3 < ng) entries(g + 3, kA, vA);  // kA/vA are free: group g is done
+      multiply(vB, wB);
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        kB[u] = kA[u];  // group g+3 entries
+        vB[u] = vA[u];
+        vA[u] = v2[u];  // group g+2 values (its W rows are in wA)
+      }
+    }
+  } else {
+    // Unaligned W or a ragged last strip: per-lane element loads where a lane
+    // straddles N, one group of entries at a time.
+    const bool full = w_vec != 0 && valid >= kCPL;
+    for (int g = 0; g < ng; ++g) {
+      int kk[kGroup];
+      float vv[kGroup];
+      entries(g, kk, vv);
+      WRaw<kBf16> w[kGroup];
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        if (full)
+          w[u] = load_full<kBf16>(rs, voff, kk[u] * row_bytes);
+        else if (valid > 0)
+          w[u] = load_part<kBf16>(W, int64_t(kk[u]) * ldw + col0, valid);
+        else
+          w[u] = WRaw<kBf16>{};
+      }
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) fma_raw<kBf16>(vv[u], w[u], y);
     }
   }
 
   if (valid > 0) {
-    if (y_vec && valid >= kCPL) {
-      *reinterpret_cast<float4*>(yrow) = make_float4(
-          __fadd_rn(yo[0], y[0]), __fadd_rn(yo[1], y[1]), __fadd_rn(yo[2], y[2]), __fadd_rn(yo[3], y[3]));
-      *reinterpret_cast<float4*>(yrow + 4) = make_float4(
-          __fadd_rn(yo[4], y[4]), __fadd_rn(yo[5], y[5]), __fadd_rn(yo[6], y[6]), __fadd_rn(yo[7], y[7]));
+    if (y_full) {
+      store_y4(f32x4{__fadd_rn(yo[0], y[0]), __fadd_rn(yo[1], y[1]), __fadd_rn(yo[2], y[2]),
+                     __fadd_rn(yo[3], y[3])}, yrow);
+      store_y4(f32x4{__fadd_rn(yo[4], y[4]), __fadd_rn(yo[5], y[5]), __fadd_rn(yo[6], y[6]),
+                     __fadd_rn(yo[7], y[7])}, yrow + 4);
     } else {
 #pragma unroll
       for (int c = 0; c < kCPL; ++c)
@@ -190,21 +261,26 @@ hipError_t launch_sparse_add(const SparseArgs& sp, int64_t M, int64_t N, float* 
                              hipStream_t stream) {
   const int64_t strips = (N + kStrip - 1) / kStrip;
   const int64_t units = strips * M;
-  const int64_t blocks = (units + 3) / 4;
   const int64_t esz = sp.w_bf16 ? 2 : 4;
   // Vector access of a lane's 8 columns needs every row start of W 16-byte
   // aligned and of Y 16-byte aligned (column offsets are multiples of 8).
   const bool w_vec = (reinterpret_cast<uintptr_t>(sp.W) % 16 == 0) && ((sp.ldw * esz) % 16 == 0);
   const bool y_vec = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && (ldy % 4 == 0);
   const int w_bytes = int(sp.w_rows * sp.ldw * esz);
-  if (sp.w_bf16)
-    sparse_add_kernel<true><<<dim3(unsigned(blocks)), 256, 0, stream>>>(
-        sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_bytes, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0,
-        int(M), int(N), units);
-  else
-    sparse_add_kernel<false><<<dim3(unsigned(blocks)), 256, 0, stream>>>(
-        sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_bytes, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0,
-        int(M), int(N), units);
+  // One single-wave workgroup per unit, launched in chunks that keep the
+  // thread count of one launch below 2^32.
+  constexpr int64_t kChunk = int64_t(1) << 24;
+  for (int64_t base = 0; base < units; base += kChunk) {
+    const int64_t blocks = units - base < kChunk ? units - base : kChunk;
+    if (sp.w_bf16)
+      sparse_add_kernel<true><<<dim3(unsigned(blocks)), 64, 0, stream>>>(
+          sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_bytes, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0,
+          int(M), int(N), base, base + blocks);
+    else
+      sparse_add_kernel<false><<<dim3(unsigned(blocks)), 64, 0, stream>>>(
+          sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_bytes, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0,
+          int(M), int(N), base, base + blocks);
+  }
   return hipGetLastError();
 }
 
