@@ -38,7 +38,9 @@
 //    fragments at a time into its own block of the (then idle) stage buffers
 //    and stores them back as rows, 16 bytes per lane, so Y is written with
 //    full-width stores of whole 256-byte row segments (4x fewer store
-//    instructions than storing from the MFMA layout).
+//    instructions than storing from the MFMA layout). The stores are
+//    non-temporal: the output stream is not kept in L2 at the expense of the
+//    operand tiles that concurrent workgroups re-read.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -48,6 +50,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
 // no swizzle); with stride 0 the bounds check is offset < num_records.
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
         if (gr < M) {
           float* dst = Y + int64_t(gr) * ldy + gc;
           if (y_vec && gc + 4 <= N) {
-            *reinterpret_cast<float4*>(dst) = v;
+            __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(dst));
           } else {
             const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
