@@ -19,10 +19,15 @@
 // Layout and schedule:
 //  * A is M x ldq bytes and B is N x ldq bytes, K-contiguous packed rows.
 //  * A workgroup of 4 waves (2 x 2 grid, each wave 64 x 128 outputs) owns a
-//    128 x 256 output tile and walks K in 128-code (64-byte) steps through a
-//    double-buffered LDS stage (48 KiB). Operand loads are buffer loads held in
-//    registers and issued two K steps before they are stored to LDS. Two
-//    workgroups share a CU, so one's stores overlap the other's MFMA loop.
+//    128 x 256 output tile and walks K in 128-code (64-byte) steps through
+//    three LDS stages of 24 KiB. Operand tiles go from global memory straight
+//    into LDS (buffer loads with an LDS destination, no register staging),
+//    issued three steps ahead into the stage the previous step finished.
+//    Each step issues its first 64-code sub-step of MFMAs, then waits for its
+//    own loads of the next stage and meets the other waves at the barrier
+//    while the matrix core works through the queued MFMAs, then issues the
+//    next loads, the second sub-step of MFMAs and the next step's first
+//    fragment reads. Two workgroups share a CU.
 //  * Each 16-byte chunk of a staged row is stored at a chunk index XOR-ed with
 //    row bits, so that the lanes reading one chunk column of consecutive rows
 //    hit distinct banks.
@@ -56,35 +61,37 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // no swizzle); with stride 0 the bounds check is offset < num_records.
 constexpr int kBufferFlags = 0x00020000;
 
-template <int BM_, int BN_, int WM_, int WN_, int BKB_, int MINB_, int STAGES_>
+template <int BM_, int BN_, int WM_, int WN_, int BKB_, int MINB_>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BKB = BKB_;
   static constexpr int kMinBlocks = MINB_;  // workgroups per CU the register budget targets
-  static constexpr int kStages = STAGES_;   // K steps of operand loads in flight (registers)
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int FM = BM / WM / 32;
   static constexpr int FN = BN / WN / 32;
   static constexpr int CPR = BKB / 16;            // 16-byte chunks per staged row
   static constexpr int kSub = BKB / 32;            // 64-code MFMA steps per K step
-  static constexpr int kAChunks = BM * CPR / kThreads;
-  static constexpr int kBChunks = BN * CPR / kThreads;
   static constexpr int kStageBytes = (BM + BN) * BKB;
   static_assert(FM >= 1 && FN >= 1, "tile too small for the wave grid");
-  static_assert(kAChunks >= 1 && kBChunks >= 1, "tile too small for the thread count");
-  static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "uneven tile load");
   static_assert(CPR == 4 || CPR == 8, "swizzle assumes 64- or 128-byte staged rows");
 };
 
-// Physical 16-byte chunk of logical chunk c in staged row r. A 128-bit LDS
-// read of 32 consecutive rows at one logical chunk must not put two lanes of
-// the same bank group on one bank; the mapping below spreads every aligned
-// group of 16 consecutive rows over 256 distinct bytes (64 banks) and every
-// aligned group of 8 rows over 128 distinct bytes (32 banks):
-//   64-byte rows:  chunk ^ (((r >> 1) ^ (r >> 3)) & 3)
+// s_waitcnt immediate of gfx9-family parts: vmcnt in bits 3:0 (and 15:14),
+// expcnt in 6:4 (7: do not wait), lgkmcnt in 11:8.
+constexpr int waitcnt_vm_lgkm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+// Physical 16-byte chunk of logical chunk c in staged row r. A fragment read
+// is a 128-bit LDS read of 32 consecutive rows at one logical chunk (lanes
+// 32..63 at the next chunk). On gfx950 such a read takes 4 LDS cycles when
+// every 16 consecutive lanes cover 64 distinct 4-byte banks, the rate of a
+// contiguous 1 KiB read; measured on the device, the mapping below reaches
+// it for 64-byte rows, while an unswizzled layout takes 16 cycles:
+//   64-byte rows:  chunk ^ ((r >> 2) & 3)
 //   128-byte rows: chunk ^ ((r ^ (r >> 3)) & 7)
 template <int CPR>
 __device__ inline int swz(int r, int c) {
-  if constexpr (CPR == 4) return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+  if constexpr (CPR == 4) return c ^ ((r >> 2) & 3);
   return c ^ ((r ^ (r >> 3)) & 7);
 }
 
@@ -106,6 +113,17 @@ __device__ inline void tile_coords(int bid, int nblocks, int tiles_m, int& tm, i
   tn = within / gsize;
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// dst + 16 * l (dst wave-uniform).
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff,
+                                           0, 0, 0);
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across;
+// the caller waits for the counters it needs first.
+__device__ inline void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <class C>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
     const uint8_t* __restrict__ Aq, const float* __restrict__ sA,
@@ -113,7 +131,12 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
     int tiles_m, float* __restrict__ Y, int64_t ldy) {
   constexpr int BM = C::BM, BN = C::BN, WN = C::WN, BKB = C::BKB, CPR = C::CPR;
   constexpr int FM = C::FM, FN = C::FN, NT = C::kThreads;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::kStageBytes];
+  constexpr int SB = C::kStageBytes;
+  // Three LDS stages, separate objects so that the compiler can tell the
+  // direct-to-LDS loads into one stage from the fragment reads of another.
+  __shared__ __attribute__((aligned(16))) uint8_t st0[SB];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[SB];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[SB];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -125,59 +148,39 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
   const int nkt = (ldq + BKB - 1) / BKB;
 
-  // Operand tiles are fetched with buffer loads: the resource descriptor holds
-  // the base and the byte size of the packed matrix, and the hardware returns
-  // zeros for any offset past the end, so rows past M (or N) read as zero
-  // codes. Each thread keeps one 32-bit offset per 16-byte chunk (the K step is
-  // added to it, inside the checked offset). Chunk c of a thread is fixed (the
-  // thread count is a multiple of the chunks per row). The host keeps
-  // (rows + 1) * ldq below 2^31.
-  const int tc = t % CPR;
+  // Operand tiles go straight from global memory to LDS (buffer loads with
+  // the LDS destination): one instruction moves 1 KiB, lane l landing at byte
+  // 16*l of the block, so the XOR swizzle is applied to the source address.
+  // The resource holds the packed matrix size, so rows past M (or N) read as
+  // zero codes. A stage is (BM + BN) rows of BKB bytes in 1 KiB blocks (A rows
+  // first); wave w moves blocks w, w + W, w + 2W, ...
+  static_assert(BKB == 64, "one 1 KiB block is 16 rows of 64 bytes");
+  constexpr int kBlocks = SB / 1024;
+  constexpr int kWaves = NT / kWave;
+  constexpr int kPer = kBlocks / kWaves;
+  static_assert(kBlocks % kWaves == 0 && BM % 16 == 0, "even block split");
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(Aq), 0, int(int64_t(M) * ldq), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsB =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(Bq), 0, int(int64_t(N) * ldq), kBufferFlags);
-  int a_off[C::kAChunks], b_off[C::kBChunks];
+  int src_off[kPer];
 #pragma unroll
-  for (int i = 0; i < C::kAChunks; ++i) {
-    const int row = (t + i * NT) / CPR;
-    a_off[i] = (m0 + row < M) ? (m0 + row) * ldq + tc * 16 : int(int64_t(M) * ldq);
+  for (int j = 0; j < kPer; ++j) {
+    const int b = wave + j * kWaves;
+    const bool is_a = b < BM / 16;
+    const int r = (is_a ? b * 16 : (b - BM / 16) * 16) + (lane >> 2);
+    const int c = (lane & 3) ^ (swz<CPR>(r, 0));  // logical chunk stored at physical lane & 3
+    if (is_a)
+      src_off[j] = (m0 + r < M) ? (m0 + r) * ldq + c * 16 : int(int64_t(M) * ldq);
+    else
+      src_off[j] = (n0 + r < N) ? (n0 + r) * ldq + c * 16 : int(int64_t(N) * ldq);
   }
-#pragma unroll
-  for (int i = 0; i < C::kBChunks; ++i) {
-    const int row = (t + i * NT) / CPR;
-    b_off[i] = (n0 + row < N) ? (n0 + row) * ldq + tc * 16 : int(int64_t(N) * ldq);
-  }
-
-  constexpr int S = C::kStages;
-  uint4 ra[S][C::kAChunks], rb[S][C::kBChunks];
-  // K tail: a chunk past the packed row length would read the next row, so it
-  // is replaced by zero codes (the load itself stays in bounds).
-  auto gload = [&](int kt, int slot) {
+  auto dma = [&](int kt, uint8_t* stage) {
     const int kb = kt * BKB;
-    const bool ok = kb + tc * 16 < ldq;
 #pragma unroll
-    for (int i = 0; i < C::kAChunks; ++i) {
-      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i] + kb, 0, 0));
-      ra[slot][i] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int i = 0; i < C::kBChunks; ++i) {
-      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsB, b_off[i] + kb, 0, 0));
-      rb[slot][i] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto lstore = [&](int buf, int slot) {
-    uint8_t* base = lds + buf * C::kStageBytes;
-#pragma unroll
-    for (int i = 0; i < C::kAChunks; ++i) {
-      const int row = (t + i * NT) / CPR;
-      *reinterpret_cast<uint4*>(base + row * BKB + (swz<CPR>(row, tc) << 4)) = ra[slot][i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::kBChunks; ++i) {
-      const int row = (t + i * NT) / CPR;
-      *reinterpret_cast<uint4*>(base + BM * BKB + row * BKB + (swz<CPR>(row, tc) << 4)) = rb[slot][i];
+    for (int j = 0; j < kPer; ++j) {
+      const int b = wave + j * kWaves;
+      load_lds16(b < BM / 16 ? rsA : rsB, stage + b * 1024, src_off[j] + kb);
     }
   };
 
@@ -187,68 +190,97 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-  // fragment source offsets inside a stage (row part; chunk added per step)
   int a_row[FM], b_row[FN];
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) a_row[fm] = wm * (FM * 32) + fm * 32 + (lane & 31);
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) b_row[fn] = wn * (FN * 32) + fn * 32 + (lane & 31);
 
-  // Pipeline: LDS stage kt & 1 holds step kt; register slot (j % S) holds the
-  // loads of step j in flight, issued S steps before they are stored to LDS.
-  gload(0, 0);
-  lstore(0, 0);
-#pragma unroll
-  for (int j = 1; j <= S; ++j)
-    if (j < nkt) gload(j, j % S);
-  __syncthreads();
-  for (int kt0 = 0; kt0 < nkt; kt0 += S) {
-#pragma unroll
-  for (int sub = 0; sub < S; ++sub) {
-    const int kt = kt0 + sub;
-    if (kt >= nkt) break;
-    const int cur = kt & 1;
-    // slot of step kt+1 (and of step kt+1+S, loaded after it is stored)
-    const int nslot = (sub + 1) % S;
-    const uint8_t* As = lds + cur * C::kStageBytes;
+  static_assert(C::kSub == 2, "two 64-code MFMA sub-steps per K step");
+  // fragments of one sub-step (kk) of a stage
+  auto read_frags = [&](const uint8_t* As, int kk, v8i* af, v8i* bf) {
     const uint8_t* Bs = As + BM * BKB;
-    // Fragments of sub-step kk+1 are read from LDS before the MFMAs of sub-step
-    // kk are issued (two fragment sets live); the scheduling barriers keep the
-    // compiler from hoisting every sub-step's reads to the top of the step.
-    v8i a[2][FM], b[2][FN];
-    auto read_frags = [&](int kk, v8i* af, v8i* bf) {
-      const int c = kk * 2 + (lane >> 5);
+    const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int r = a_row[fm];
-        const uint4 u = *reinterpret_cast<const uint4*>(As + r * BKB + (swz<CPR>(r, c) << 4));
-        af[fm] = v8i{int(u.x), int(u.y), int(u.z), int(u.w), 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int r = b_row[fn];
-        const uint4 u = *reinterpret_cast<const uint4*>(Bs + r * BKB + (swz<CPR>(r, c) << 4));
-        bf[fn] = v8i{int(u.x), int(u.y), int(u.z), int(u.w), 0, 0, 0, 0};
-      }
-    };
-    read_frags(0, a[0], b[0]);
-#pragma unroll
-    for (int kk = 0; kk < C::kSub; ++kk) {
-      if (kk + 1 < C::kSub) read_frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              a[kk & 1][fm], b[kk & 1][fn], acc[fm][fn], 4, 4, 0, 127, 0, 127);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int fm = 0; fm < FM; ++fm) {
+      const int r = a_row[fm];
+      const uint4 u = *reinterpret_cast<const uint4*>(As + r * BKB + (swz<CPR>(r, c) << 4));
+      af[fm] = v8i{int(u.x), int(u.y), int(u.z), int(u.w), 0, 0, 0, 0};
     }
-    if (kt + 1 < nkt) lstore(cur ^ 1, nslot);
-    if (kt + 1 + S < nkt) gload(kt + 1 + S, nslot);
-    __syncthreads();
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int r = b_row[fn];
+      const uint4 u = *reinterpret_cast<const uint4*>(Bs + r * BKB + (swz<CPR>(r, c) << 4));
+      bf[fn] = v8i{int(u.x), int(u.y), int(u.z), int(u.w), 0, 0, 0, 0};
+    }
+  };
+  auto mfmas = [&](const v8i* af, const v8i* bf) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf[fn], acc[fm][fn], 4, 4,
+                                                                      0, 127, 0, 127);
+  };
+
+  // Pipeline over K steps (stage of step s: s mod 3). On entry to step kt the
+  // first sub-step's fragments of stage kt are in registers. The step reads
+  // its second sub-step's fragments, issues the first sub-step's MFMAs, then
+  // waits for its own loads of stage kt+1 (those of kt+2 stay in flight) and
+  // for its fragment reads, and meets the other waves at a barrier while the
+  // matrix core works through the queued MFMAs. After the barrier stage kt+1
+  // is complete and nobody reads stage kt any more, so the loads of step kt+3
+  // go there; then the second sub-step's MFMAs and the next step's first
+  // fragment reads. Every wave issues kPer loads per step on every path
+  // (past the last step they repeat it into a stage that is not read).
+  constexpr int kWaitCnt = waitcnt_vm_lgkm(kPer, 0);
+  static_assert(2 * kPer < 64, "vmcnt immediate");
+  v8i a0[FM], b0[FN], a1[FM], b1[FN];
+  // a full step inside the main loop (steps kt, kt+1 and kt+2 all exist)
+  auto step = [&](int kt, const uint8_t* cur, const uint8_t* nxt, uint8_t* ldst) {
+    read_frags(cur, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitCnt);
+    raw_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    dma(kt + 3 < nkt ? kt + 3 : nkt - 1, ldst);
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(nxt, 0, a0, b0);
+  };
+  // one of the last (up to two) steps: no more loads are issued
+  auto tail_step = [&](const uint8_t* cur, const uint8_t* nxt, bool has_next) {
+    read_frags(cur, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, 0));
+    raw_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_next) read_frags(nxt, 0, a0, b0);
+  };
+  dma(0, st0);
+  dma(nkt > 1 ? 1 : nkt - 1, st1);
+  dma(nkt > 2 ? 2 : nkt - 1, st2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(2 * kPer, 0));  // step 0 landed
+  raw_barrier();
+  read_frags(st0, 0, a0, b0);
+  int kt0 = 0;
+  for (; kt0 + 3 <= nkt; kt0 += 3) {
+    step(kt0, st0, st1, st0);
+    step(kt0 + 1, st1, st2, st1);
+    step(kt0 + 2, st2, st0, st2);
   }
-  }
+  if (kt0 < nkt) tail_step(st0, st1, kt0 + 1 < nkt);
+  if (kt0 + 1 < nkt) tail_step(st1, st2, false);
+  // every load has landed and every wave is done with the stages before they
+  // are reused for the output
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, 0));
+  raw_barrier();
 
   // ---- epilogue -------------------------------------------------------------
   // Scales are applied in the MFMA output layout: for accumulator element r,
@@ -274,10 +306,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   // the main loop's last barrier): two 32x32 fragments at a time are written
   // in the MFMA layout, read back as rows and stored 16 bytes per lane.
   constexpr int kER = 72;  // padded row of a 32 x 64 chunk (floats)
-  static_assert((NT / kWave) * 32 * kER * 4 <= 2 * C::kStageBytes,
-                "epilogue chunks fit the stage buffers");
+  static_assert(2 * 32 * kER * 4 <= C::kStageBytes && NT / kWave == 4,
+                "two waves' epilogue chunks fit one stage buffer");
   static_assert(FN % 2 == 0, "fragments are staged in pairs");
-  float* eb = reinterpret_cast<float*>(lds) + wave * (32 * kER);
+  float* eb = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * (32 * kER);
   const bool y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy & 3) == 0);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
@@ -313,7 +345,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
     }
 }
 
-using GemmTile = GemmCfg<128, 256, 2, 2, 64, 2, 2>;
+using GemmTile = GemmCfg<128, 256, 2, 2, 64, 2>;
 
 }  // namespace
 
@@ -321,6 +353,9 @@ hipError_t launch_fp4_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq
                            int64_t M, int64_t N, int64_t ldq, const SparseArgs& sp, float* Y,
                            int64_t ldy, hipStream_t stream) {
   using C = GemmTile;
+  // K steps are whole 64-byte chunks of the packed rows (the packed row length
+  // is a multiple of 64 bytes), so no step reads past a row.
+  if (ldq % C::BKB != 0) return hipErrorInvalidValue;
   const int tiles_m = int((M + C::BM - 1) / C::BM);
   const int tiles_n = int((N + C::BN - 1) / C::BN);
   fp4_gemm_kernel<C><<<dim3(unsigned(tiles_m * tiles_n)), C::kThreads, 0, stream>>>(
