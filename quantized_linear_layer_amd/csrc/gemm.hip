@@ -306,10 +306,12 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   // the main loop's last barrier): two 32x32 fragments at a time are written
   // in the MFMA layout, read back as rows and stored 16 bytes per lane.
   constexpr int kER = 72;  // padded row of a 32 x 64 chunk (floats)
-  static_assert(2 * 32 * kER * 4 <= C::kStageBytes && NT / kWave == 4,
-                "two waves' epilogue chunks fit one stage buffer");
+  // each stage buffer holds the blocks of kEpiPer waves
+  constexpr int kEpiPer = C::kStageBytes / (32 * kER * 4);
+  static_assert(kEpiPer >= 1 && 3 * kEpiPer >= NT / kWave, "epilogue blocks fit the stages");
   static_assert(FN % 2 == 0, "fragments are staged in pairs");
-  float* eb = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * (32 * kER);
+  uint8_t* const ebs = wave < kEpiPer ? st0 : (wave < 2 * kEpiPer ? st1 : st2);
+  float* eb = reinterpret_cast<float*>(ebs) + (wave % kEpiPer) * (32 * kER);
   const bool y_vec = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy & 3) == 0);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
