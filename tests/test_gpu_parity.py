@@ -316,8 +316,11 @@ def run_gemm(ql, codesA, sA, codesB, sB, K, delta=None, W=None):
     return host(Y)
 
 
+# K steps of 128 codes: 1, 6, 2, 8, 32, 2 and (added) 3, 4, 13, so that every
+# count below three and every residue modulo the three LDS stages is covered.
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (37, 300, 700), (256, 256, 256), (300, 520, 1000),
-                                   (513, 257, 4096), (64, 700, 129)])
+                                   (513, 257, 4096), (64, 700, 129), (64, 300, 384),
+                                   (130, 270, 512), (96, 260, 1664)])
 def test_gemm_integer_exact(ql, M, N, K):
     """Unit scales, no compensation: Y is the exact integer-valued product."""
     log(f"gemm exact {M}x{N}x{K}")
