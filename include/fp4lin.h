@@ -44,7 +44,9 @@
  * Conventions for every call:
  *   - Pointers are device pointers owned by the caller unless marked "host".
  *     The library never allocates, frees or keeps a pointer after return, holds
- *     no global state and is safe to call from several host threads.
+ *     no global state (apart from each host thread's record of its last HIP
+ *     launch result, see fp4lin_last_hip_error) and is safe to call from
+ *     several host threads.
  *   - All device work is enqueued asynchronously, in order, on `stream`
  *     (0 = the null stream). Nothing is read back and there is no host
  *     synchronisation: results are valid once the caller synchronises the
@@ -136,6 +138,12 @@ fp4lin_status fp4lin_forward_layout(int64_t M, int64_t K, int64_t N, fp4lin_dtyp
 
 /* Static description of a status code. */
 const char* fp4lin_status_str(fp4lin_status s);
+
+/* The hipError_t value (as int) of the calling thread's most recent launch
+ * check, and its name: after FP4LIN_ERR_LAUNCH they say what the HIP runtime
+ * reported. hipSuccess (0) before any launch on the thread. */
+int fp4lin_last_hip_error(void);
+const char* fp4lin_last_hip_error_name(void);
 
 /* ---- device operations ---------------------------------------------------- */
 

@@ -26,6 +26,8 @@ __all__ = [
 class Fp4linError(RuntimeError):
     def __init__(self, status: int, where: str):
         msg = lib().fp4lin_status_str(status).decode()
+        if status == _lib.ERR_LAUNCH:
+            msg += f": {lib().fp4lin_last_hip_error_name().decode()}"
         super().__init__(f"{where}: status {status} ({msg})")
         self.status = status
 

@@ -39,6 +39,8 @@ SIGNATURES = {
     "fp4lin_forward_layout": (c_int, [c_i64, c_i64, c_i64, c_int, c_dbl,
                                       ctypes.POINTER(ForwardOffsets)]),
     "fp4lin_status_str": (ctypes.c_char_p, [c_int]),
+    "fp4lin_last_hip_error": (c_int, []),
+    "fp4lin_last_hip_error_name": (ctypes.c_char_p, []),
     "fp4lin_outlier_select": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_dbl, c_ptr, Coo,
                                       c_ptr, c_size, c_ptr]),
     "fp4lin_quantize_act": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr, c_ptr,
@@ -65,6 +67,15 @@ def load():
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m quantized_linear_layer_amd.build` "
             "(there is no fallback implementation)")
+    # PyTorch-ROCm ships its own HIP runtime with the same soname as the
+    # system one the library is linked against. Loading torch first makes the
+    # library bind to the runtime torch already holds, so both share one HIP
+    # context; loaded the other way round, the process ends up with two
+    # runtimes and the library's launches fail with hipErrorNoDevice.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

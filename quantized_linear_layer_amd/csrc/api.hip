@@ -18,7 +18,14 @@ bool ok_dim(int64_t x) { return x >= 1 && x < kMaxDim; }
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-fp4lin_status launch_status(hipError_t e) { return e == hipSuccess ? FP4LIN_OK : FP4LIN_ERR_LAUNCH; }
+// HIP error behind the calling thread's last launch check (for
+// fp4lin_last_hip_error).
+thread_local hipError_t t_last_hip = hipSuccess;
+
+fp4lin_status launch_status(hipError_t e) {
+  t_last_hip = e;
+  return e == hipSuccess ? FP4LIN_OK : FP4LIN_ERR_LAUNCH;
+}
 
 // COO entries the select can produce for rank k: #{|a| > tau} <= n - 1 - k.
 int64_t needed_capacity(int64_t n, int64_t k) { return n - 1 - k; }
@@ -104,6 +111,10 @@ size_t fp4lin_workspace_bytes(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt, 
   if (fp4lin_forward_layout(M, K, N, dt, q, &o) != FP4LIN_OK) return 0;
   return o.total;
 }
+
+int fp4lin_last_hip_error(void) { return int(t_last_hip); }
+
+const char* fp4lin_last_hip_error_name(void) { return hipGetErrorName(t_last_hip); }
 
 const char* fp4lin_status_str(fp4lin_status s) {
   switch (s) {

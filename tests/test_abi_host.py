@@ -230,3 +230,12 @@ def test_python_binding_refuses_cpu_tensors():
     A = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         qll.quantize_act(A)
+
+
+def test_one_hip_runtime_in_process():
+    """The library binds to the HIP runtime PyTorch loaded, so the process holds
+    one runtime (two copies of it do not share a device context)."""
+    pytest.importorskip("torch")
+    maps = open("/proc/self/maps").read()
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, sorted(hip)
