@@ -60,7 +60,7 @@ __device__ inline void fma_raw(float v, const WRaw<kBf16>& r, float y[kCPL]) {
   }
 }
 
-// Full-width load of W[k, col0 .. col0+3] through the buffer resource: the row
+// Full-width load of W[k, col0 .. col0+7] through the buffer resource: the row
 // offset k*ldw is wave-uniform and goes in the scalar offset, the column
 // offset is the lane's constant vector offset.
 template <bool kBf16>
@@ -72,7 +72,7 @@ __device__ inline WRaw<kBf16> load_full(__amdgpu_buffer_rsrc_t rs, int voff, int
   return r;
 }
 
-// Element loads for a lane whose 4 columns run past N (last strip only).
+// Element loads for a lane whose 8 columns run past N (last strip only).
 template <bool kBf16>
 __device__ inline WRaw<kBf16> load_part(const void* __restrict__ W, int64_t off, int valid) {
   WRaw<kBf16> r;
