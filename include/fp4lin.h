@@ -120,7 +120,8 @@ int64_t fp4lin_quantile_rank(int64_t n, double q);
 int64_t fp4lin_packed_ld(int64_t L);
 
 /* Workspace bytes fp4lin_outlier_select needs for an M x K input of dtype dt
- * (radix histograms and selection state). 0 on invalid arguments. */
+ * (radix histograms, selection state, per-row counts: grows with M).
+ * 0 on invalid arguments. */
 size_t fp4lin_select_workspace_bytes(int64_t M, int64_t K, fp4lin_dtype dt);
 
 /* Workspace bytes fp4lin_quantize_weight needs for a K x N weight (per-column

@@ -37,8 +37,8 @@ bool weight_addressable(int64_t K, int64_t ldw, fp4lin_dtype wdt) {
   return K * ldw * (wdt == FP4LIN_BF16 ? 2 : 4) < kMaxDim;
 }
 
-size_t select_ws(fp4lin_dtype dt) {
-  return round_up(fp4lin::select_workspace_bytes(dt == FP4LIN_BF16), 256);
+size_t select_ws(int64_t M, fp4lin_dtype dt) {
+  return round_up(fp4lin::select_workspace_bytes(dt == FP4LIN_BF16, M), 256);
 }
 
 }  // namespace
@@ -61,7 +61,7 @@ int64_t fp4lin_packed_ld(int64_t L) {
 
 size_t fp4lin_select_workspace_bytes(int64_t M, int64_t K, fp4lin_dtype dt) {
   if (!ok_dim(M) || !ok_dim(K) || bad_dtype(dt)) return 0;
-  return select_ws(dt);
+  return select_ws(M, dt);
 }
 
 size_t fp4lin_weight_workspace_bytes(int64_t K, int64_t N) {
@@ -98,7 +98,7 @@ fp4lin_status fp4lin_forward_layout(int64_t M, int64_t K, int64_t N, fp4lin_dtyp
   o.sA = take(size_t(M) * 4);
   o.Wq = take(size_t(N) * ldq);
   o.sW = take(size_t(N) * 4);
-  const size_t sws = select_ws(dt), wws = weight_ws(N);
+  const size_t sws = select_ws(M, dt), wws = weight_ws(N);
   o.scratch = take(sws > wws ? sws : wws);
   o.capacity = cap;
   o.total = off;
@@ -147,7 +147,7 @@ fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, i
   if (cap >= kMaxDim) return FP4LIN_ERR_SHAPE;
   if (dA.capacity < cap) return FP4LIN_ERR_CAPACITY;
   if (!aligned16(ws)) return FP4LIN_ERR_ALIGN;
-  if (ws_bytes < select_ws(dt)) return FP4LIN_ERR_WORKSPACE;
+  if (ws_bytes < select_ws(M, dt)) return FP4LIN_ERR_WORKSPACE;
   return launch_status(fp4lin::launch_outlier_select(A, dt == FP4LIN_BF16, M, K, lda, k, tau,
                                                      dA.capacity, dA.row, dA.col, dA.val, dA.row_ptr, ws,
                                                      stream));

@@ -7,7 +7,7 @@
 
 namespace fp4lin {
 
-size_t select_workspace_bytes(bool bf16);
+size_t select_workspace_bytes(bool bf16, int64_t M);
 size_t weight_workspace_bytes(int64_t N);
 
 hipError_t launch_outlier_select(const void* A, bool bf16, int64_t M, int64_t K, int64_t lda,

@@ -9,21 +9,27 @@
 // |a| of a finite float is ordered like its bit pattern with the sign cleared,
 // so the k-th smallest |a| is the k-th smallest integer key, found digit by
 // digit from the top: each pass histograms one digit of the keys whose higher
-// digits equal the prefix found so far, and a one-workgroup pick kernel finds
-// the digit that holds the remaining rank. Everything stays on the device; the
-// host never reads a histogram.
+// digits equal the prefix found so far, and the digit that holds the remaining
+// rank is appended to the prefix. Everything stays on the device; the host
+// never reads a histogram.
 //
 // bfloat16 keys (15 bits) take two passes over A. Pass 1 builds a full
 // 32768-bin histogram per workgroup in LDS (one 16-wave workgroup per CU),
 // which spreads the densely populated magnitudes over many bins so that few
-// lanes of an LDS atomic meet on one address, but merges only its 128 coarse
-// sums (256 keys each) into global memory: merging every non-zero fine bin with
-// device-wide atomics costs several times the pass itself. Pass 2 histograms
-// the 256 keys of the chosen coarse bin. float32 keys (31 bits) take three
-// passes of 11, 11 and 9 bits with a 2048-bin histogram.
+// lanes of an LDS atomic meet on one address, and writes only its 128 coarse
+// sums (256 keys each), one row of partial sums per workgroup: merging every
+// non-zero fine bin with device-wide atomics costs several times the pass
+// itself. Pass 2 adds the partial rows up in every workgroup, finds the coarse
+// bin that holds rank k, and histograms the 256 keys of that bin. The row count
+// that follows finds tau's key from that histogram in every wave. No kernel
+// needs a cleared buffer on entry, so no launch is spent on set-up.
+// float32 keys (31 bits) take three passes of 11, 11 and 9 bits with a
+// 2048-bin histogram and a one-workgroup pick kernel after each.
 //
-// Then the entries with |a| > tau are counted per row, the counts scanned into
-// row_ptr, and the entries written in row-major order.
+// Then the entries with |a| > tau are counted per row, with one total per
+// workgroup of rows; the compaction adds up the totals of the workgroups before
+// its own, which gives row_ptr and the row-major positions without a separate
+// scan.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -37,9 +43,9 @@ struct SelState {
   int64_t krem;      // rank still to find inside the current prefix
 };
 
-// Find the digit whose cumulative count passes the remaining rank and append
-// it to the prefix; after the last pass the prefix is the key of tau, whose
-// float bits are key << key_shift. One workgroup of 256 threads.
+// float32 passes: find the digit whose cumulative count passes the remaining
+// rank and append it to the prefix; after the last pass the prefix is the key
+// of tau, whose float bits are key << key_shift. One workgroup of 256 threads.
 __global__ __launch_bounds__(256) void select_pick_kernel(SelState* st,
                                                           const uint32_t* __restrict__ hist,
                                                           int width, int last, int key_shift,
@@ -169,30 +175,89 @@ constexpr int kCoarseBins = 1 << kCoarseBits;
 constexpr int kFineBins = 1 << kFineBits;
 constexpr int kH16Threads = 1024;
 constexpr int kH16Waves = kH16Threads / kWave;
+constexpr int kMaxH16Groups = 256;  // workgroups of the bfloat16 passes (one per CU)
+
+// The coarse bin (key >> 8) that holds rank k. Thread t adds, for the four
+// bins 4q .. 4q+3 (q = t % 32), the partial rows s, s+32, ... (s = t / 32);
+// wave 0 adds the 32 sets up, two bins per lane, scans the 128 totals, and
+// the lane whose range holds k names the bin. Workgroup 0 records the bin and
+// the rank left inside it for the row count. All kH16Threads threads call it.
+__device__ inline uint32_t coarse_pick(const uint32_t* __restrict__ part, int nparts,
+                                       uint32_t k, SelState* __restrict__ st) {
+  constexpr int kQuads = kCoarseBins / 4;
+  constexpr int kSets = kH16Threads / kQuads;
+  __shared__ uint4 red[kSets][kQuads];
+  __shared__ uint32_t pick;
+  const int t = threadIdx.x;
+  const int q = t % kQuads, s = t / kQuads;
+  if (t == 0) pick = 0u;
+  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+  for (int p = s; p < nparts; p += kSets) {
+    const uint4 x = reinterpret_cast<const uint4*>(part)[p * kQuads + q];
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  red[s][q] = acc;
+  __syncthreads();
+  if (t < kWave) {
+    const uint32_t* r = reinterpret_cast<const uint32_t*>(&red[0][0]);
+    uint32_t a = 0, b = 0;
+    for (int y = 0; y < kSets; ++y) {
+      a += r[y * kCoarseBins + 2 * t];
+      b += r[y * kCoarseBins + 2 * t + 1];
+    }
+    // totals and ranks are below M*K < 2^32
+    uint32_t total;
+    const uint32_t ex = wave_exclusive_scan(a + b, total);
+    if (k >= ex && k - ex < a + b) {
+      const bool lo = k - ex < a;
+      const uint32_t bin = uint32_t(2 * t) + (lo ? 0u : 1u);
+      pick = bin;
+      if (blockIdx.x == 0) {
+        st->prefix = bin;
+        st->krem = int64_t(lo ? k - ex : k - ex - a);
+      }
+    }
+  }
+  __syncthreads();
+  return uint32_t(__builtin_amdgcn_readfirstlane(int(pick)));
+}
 
 // Both bfloat16 passes. Each workgroup (16 waves sharing one LDS histogram)
 // takes a contiguous range of rows, one wave per row as in the row kernels
 // below (CH chunks per lane issued together).
-//   kFine = false: every key into a 32768-bin LDS histogram; the merge adds
-//                  each group of 256 bins to coarse[key >> 8].
-//   kFine = true:  keys with key >> 8 == prefix into a 256-bin LDS histogram,
-//                  merged bin by bin into fine[].
+//   kFine = false: every key into a 32768-bin LDS histogram; workgroup b
+//                  writes the sums of its 128 groups of 256 bins to
+//                  part[b][0 .. 128), and workgroup 0 clears fine[].
+//   kFine = true:  the workgroup finds the coarse bin from the nparts partial
+//                  rows, then histograms the keys of that bin (key >> 8 equal
+//                  to it) in a 256-bin LDS histogram, merged bin by bin into
+//                  fine[].
 template <bool kFast, bool kFine, int CH>
 __global__ __launch_bounds__(kH16Threads) void select_hist16_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rows_per_wg,
-    const SelState* __restrict__ st, uint32_t* __restrict__ out) {
+    uint32_t* __restrict__ part, int nparts, uint32_t k, SelState* __restrict__ st,
+    uint32_t* __restrict__ fine) {
   constexpr int kBins = kFine ? kFineBins : kKeyBins16;
   __shared__ uint32_t h[kBins];
   const int t = threadIdx.x;
   for (int i = t; i < kBins / 4; i += kH16Threads)
     reinterpret_cast<uint4*>(h)[i] = make_uint4(0, 0, 0, 0);
+  uint32_t prefix = 0u;
+  if constexpr (kFine) {
+    prefix = coarse_pick(part, nparts, k, st);
+  } else {
+    if (blockIdx.x == 0)
+      for (int i = t; i < kFineBins; i += kH16Threads) fine[i] = 0u;
+  }
   __syncthreads();
-  const uint32_t prefix = kFine ? st->prefix : 0u;
   const int lane = t & (kWave - 1);
   const int64_t slab = int64_t(kWave) * CH * 8;
   const int64_t r0 = int64_t(blockIdx.x) * rows_per_wg;
   const int64_t r1 = (r0 + rows_per_wg < M) ? r0 + rows_per_wg : M;
-  for (int64_t r = r0 + t / kWave; r < r1; r += kH16Waves) {
+  for (int64_t r = r0 + __builtin_amdgcn_readfirstlane(t / kWave); r < r1; r += kH16Waves) {
     const uint16_t* row = A + r * lda;
     for (int64_t c0 = 0; c0 < K; c0 += slab) {
       Vec8<BF16In> v[CH];
@@ -221,31 +286,70 @@ __global__ __launch_bounds__(kH16Threads) void select_hist16_kernel(
   if constexpr (kFine) {
     for (int b = t; b < kFineBins; b += kH16Threads) {
       const uint32_t x = h[b];
-      if (x) atomicAdd(&out[b], x);
+      if (x) atomicAdd(&fine[b], x);
     }
   } else {
     // Thread t sums bins [32t, 32t + 32), reading 16-byte words in a rotated
     // order to spread LDS banks; the 8 threads of one coarse bin are adjacent
-    // lanes and reduce with shuffles before one atomic.
+    // lanes and reduce with shuffles before one store.
     constexpr int kPer = kKeyBins16 / kH16Threads;
     static_assert((kPer * 8) == kFineBins, "8 threads per coarse bin");
-    uint32_t part = 0;
+    uint32_t sum = 0;
 #pragma unroll
     for (int i = 0; i < kPer / 4; ++i) {
       const int q4 = (i + t) & (kPer / 4 - 1);
       const uint4 x = *reinterpret_cast<const uint4*>(&h[t * kPer + q4 * 4]);
-      part += x.x + x.y + x.z + x.w;
+      sum += x.x + x.y + x.z + x.w;
     }
-    part += __shfl_xor(part, 1, kWave);
-    part += __shfl_xor(part, 2, kWave);
-    part += __shfl_xor(part, 4, kWave);
-    if ((t & 7) == 0 && part) atomicAdd(&out[t >> 3], part);
+    sum += __shfl_xor(sum, 1, kWave);
+    sum += __shfl_xor(sum, 2, kWave);
+    sum += __shfl_xor(sum, 4, kWave);
+    if ((t & 7) == 0) part[size_t(blockIdx.x) * kCoarseBins + (t >> 3)] = sum;
   }
 }
 
+// tau's key in every wave: the coarse bin recorded in st followed by the fine
+// bin that holds the rank left inside it. Lane l owns fine bins 4l .. 4l+3.
+__device__ inline uint32_t fine_pick(const SelState* st, const uint32_t* __restrict__ fine) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint4 h = reinterpret_cast<const uint4*>(fine)[lane];
+  const uint32_t s = h.x + h.y + h.z + h.w;
+  uint32_t total;
+  const uint32_t ex = wave_exclusive_scan(s, total);
+  const uint32_t krem = uint32_t(st->krem);
+  const uint32_t prefix = st->prefix;
+  const uint32_t r = krem - ex;  // meaningful in the lane that holds krem
+  uint32_t j = 3;
+  if (r < h.x)
+    j = 0;
+  else if (r - h.x < h.y)
+    j = 1;
+  else if (r - h.x - h.y < h.z)
+    j = 2;
+  const uint64_t mine = __ballot(krem >= ex && r < s);
+  const int src = mine ? __builtin_ctzll(mine) : 0;
+  const uint32_t key = (prefix << kFineBits) | (uint32_t(4 * lane) + j);
+  // uniform: kept in a scalar register for the compares
+  return uint32_t(__builtin_amdgcn_readfirstlane(__shfl(int(key), src, kWave)));
+}
+
 // ---------------------------------------------------------------------------
-// Rows: count, scan, compact. One wave per row.
+// Rows: count, compact. One wave per row. Workgroup g owns the rows
+// [g*R, min(M, (g+1)*R)), R = kRowWaves * rpw; wave w takes rows
+// g*R + w + kRowWaves*i, so the workgroup walks its range in batches of
+// kRowWaves consecutive rows.
 // ---------------------------------------------------------------------------
+constexpr int64_t kMaxRowGroups = 2048;
+
+__host__ inline int64_t rows_per_wave(int64_t M) {
+  return (M + kRowWaves * kMaxRowGroups - 1) / (kRowWaves * kMaxRowGroups);
+}
+
+__host__ inline int64_t row_groups(int64_t M) {
+  const int64_t R = kRowWaves * rows_per_wave(M);
+  return (M + R - 1) / R;
+}
+
 template <class In, int CH>
 __device__ inline uint32_t count_above(const Vec8<In> (&v)[CH], uint32_t tkey) {
   // chunks past K are zero and a zero key never exceeds tkey
@@ -257,133 +361,163 @@ __device__ inline uint32_t count_above(const Vec8<In> (&v)[CH], uint32_t tkey) {
   return cnt;
 }
 
-// Per-row count of |a| > tau, written to row_ptr[i+1].
-template <class In, bool kFast, int CH>
+// Per-row count of |a| > tau into cnt[r], and the workgroup's total into
+// gsum[blockIdx.x]. kPick (bfloat16): tau's key comes from the fine histogram
+// and workgroup 0 records it in st and tau; otherwise it is read from st. The
+// first row's loads are issued before the key is known.
+template <class In, bool kFast, int CH, bool kPick>
 __global__ __launch_bounds__(kRowWaves * kWave) void count_rows_kernel(
-    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda,
-    const SelState* __restrict__ st, int32_t* __restrict__ row_ptr) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
-  const uint32_t tkey = st->tau_key;
+    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+    SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
+    uint32_t* __restrict__ cnt, uint32_t* __restrict__ gsum) {
+  __shared__ uint32_t wsum[kRowWaves];
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);  // wave-uniform
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t R = int64_t(kRowWaves) * rpw;
+  const int64_t r0 = int64_t(blockIdx.x) * R;
+  const int64_t r1 = (r0 + R < M) ? r0 + R : M;
   const int64_t slab = int64_t(kWave) * CH * 8;
-  const int64_t stride = int64_t(gridDim.x) * kRowWaves;
-  for (int64_t r = int64_t(blockIdx.x) * kRowWaves + threadIdx.x / kWave; r < M; r += stride) {
+  uint32_t tkey;
+  if constexpr (kPick) {
+    tkey = fine_pick(st, fine);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      st->tau_key = tkey;
+      *tau = In::key_to_float(tkey);
+    }
+  } else {
+    tkey = st->tau_key;
+  }
+  uint32_t total = 0;
+  for (int64_t r = r0 + w; r < r1; r += kRowWaves) {
     const typename In::T* row = A + r * lda;
-    uint32_t cnt = 0;
+    uint32_t c = 0;
     for (int64_t c0 = 0; c0 < K; c0 += slab) {
       Vec8<In> v[CH];
       load_wave_slab<In, kFast, CH>(row, c0, K, v);
-      cnt += count_above<In, CH>(v, tkey);
+      c += count_above<In, CH>(v, tkey);
     }
-    cnt = wave_sum_u32(cnt);
-    if ((threadIdx.x & (kWave - 1)) == 0) row_ptr[r + 1] = int32_t(cnt);
+    c = wave_sum_u32(c);
+    total += c;
+    if (lane == 0) cnt[r] = c;
+  }
+  if (lane == 0) wsum[w] = total;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < kRowWaves; ++i) s += wsum[i];
+    gsum[blockIdx.x] = s;
   }
 }
 
-// In-place inclusive scan of row_ptr[1..M] by one workgroup of 1024 threads,
-// in tiles of kScanPer * 1024 rows: thread t owns rows kScanPer*t .. +kScanPer-1
-// of a tile (loaded together, scanned serially), the thread totals are scanned
-// across the wave with shuffles and across the 16 waves through LDS, and the
-// carry of earlier tiles is added.
-constexpr int kScanThreads = 1024;
-constexpr int kScanPer = 8;
-
-__global__ __launch_bounds__(kScanThreads) void scan_rows_kernel(int32_t* __restrict__ row_ptr,
-                                                                 int64_t M) {
-  constexpr int kW = kScanThreads / kWave;
-  __shared__ uint32_t wsum[kW];
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), w = t / kWave;
-  int32_t* v = row_ptr + 1;
-  uint32_t carry = 0;
-  for (int64_t base = 0; base < M; base += int64_t(kScanPer) * kScanThreads) {
-    const int64_t i0 = base + int64_t(t) * kScanPer;
-    uint32_t x[kScanPer];
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) x[j] = (i0 + j < M) ? uint32_t(v[i0 + j]) : 0u;
-#pragma unroll
-    for (int j = 1; j < kScanPer; ++j) x[j] += x[j - 1];
-    uint32_t wtot;
-    const uint32_t wex = wave_exclusive_scan(x[kScanPer - 1], wtot);
-    if (lane == 0) wsum[w] = wtot;
-    __syncthreads();
-    uint32_t before = carry + wex, all = 0;
-    for (int y = 0; y < kW; ++y) {
-      const uint32_t s = wsum[y];
-      before += (y < w) ? s : 0u;
-      all += s;
-    }
-    carry += all;
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j)
-      if (i0 + j < M) v[i0 + j] = int32_t(before + x[j]);
-    __syncthreads();  // wsum is rewritten by the next tile
-  }
-}
-
-// Write every |a| > tau entry of a row, ascending column, at row_ptr[i] + rank.
+// Write every |a| > tau entry of a row, ascending column, from position pos.
 // The entries of chunk (j, lane) follow those of all chunks (j', *) with
 // j' < j and (j, lane') with lane' < lane; per element position i of a chunk
 // a wave ballot of the predicate gives, through mbcnt, how many entries the
 // lower lanes hold at that position, so the rank needs no LDS and no barrier.
-template <class In, bool kFast, int CH>
-__global__ __launch_bounds__(kRowWaves * kWave) void compact_rows_kernel(
-    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda,
-    const SelState* __restrict__ st, const float* __restrict__ tau_p,
-    const int32_t* __restrict__ row_ptr, int64_t capacity, int32_t* __restrict__ out_row,
-    int32_t* __restrict__ out_col, float* __restrict__ out_val) {
-  const uint32_t tkey = st->tau_key;
-  const float tau = *tau_p;
+template <class In, int CH>
+__device__ inline void compact_slab(const Vec8<In> (&v)[CH], int64_t c0, int64_t r, uint32_t tkey,
+                                    float tau, uint32_t& pos, uint32_t cap,
+                                    int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
+                                    float* __restrict__ out_val) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int cap = int(capacity < INT32_MAX ? capacity : INT32_MAX);
-  const int64_t slab = int64_t(kWave) * CH * 8;
-  const int64_t stride = int64_t(gridDim.x) * kRowWaves;
-  for (int64_t r = int64_t(blockIdx.x) * kRowWaves + threadIdx.x / kWave; r < M; r += stride) {
-    const typename In::T* row = A + r * lda;
-    int pos = row_ptr[r];
-    for (int64_t c0 = 0; c0 < K; c0 += slab) {
-      Vec8<In> v[CH];
-      load_wave_slab<In, kFast, CH>(row, c0, K, v);
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        uint32_t lower = 0, total = 0, mine = 0;
+  for (int j = 0; j < CH; ++j) {
+    uint32_t lower = 0, total = 0, mine = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bool p = In::key(v[j].v[i]) > tkey;
-          const uint64_t b = __ballot(p);
-          lower = __builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32),
-                                            __builtin_amdgcn_mbcnt_lo(uint32_t(b), lower));
-          total += uint32_t(__popcll(b));
-          mine |= uint32_t(p) << i;
+    for (int i = 0; i < 8; ++i) {
+      const bool p = In::key(v[j].v[i]) > tkey;
+      const uint64_t b = __ballot(p);
+      lower = __builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32),
+                                        __builtin_amdgcn_mbcnt_lo(uint32_t(b), lower));
+      total += uint32_t(__popcll(b));
+      mine |= uint32_t(p) << i;
+    }
+    if (mine) {
+      // positions are below capacity < 2^31 and columns below K < 2^31
+      uint32_t p = pos + lower;
+      const int c = int(c0) + (j * kWave + lane) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // p < cap always holds when tau is the true order statistic
+        // (nnz <= n-1-k); the test only keeps a wrong tau from writing out of bounds.
+        if (((mine >> i) & 1u) && p < cap) {
+          const float a = In::widen(v[j].v[i]);
+          out_row[p] = int32_t(r);
+          out_col[p] = c + i;
+          out_val[p] = __fsub_rn(a, copysignf(tau, a));
+          ++p;
         }
-        if (mine) {
-          // positions and columns fit 32 bits (capacity < 2^31, K < 2^31)
-          int p = pos + int(lower);
-          const int c = int(c0) + (j * kWave + lane) * 8;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            // p < capacity always holds when tau is the true order statistic
-            // (nnz <= n-1-k); the test only keeps a wrong tau from writing out of bounds.
-            if (((mine >> i) & 1u) && p < cap) {
-              const float a = In::widen(v[j].v[i]);
-              out_row[p] = int32_t(r);
-              out_col[p] = c + i;
-              out_val[p] = __fsub_rn(a, copysignf(tau, a));
-              ++p;
-            }
-          }
-        }
-        pos += int(total);
       }
     }
+    pos += total;
   }
 }
 
-// Histogram words after the 256-byte state: bfloat16 128 coarse + 256 fine
-// bins; float32 one 2048-bin histogram per pass.
+// Row-major COO and row_ptr. The workgroup's first position is the sum of the
+// totals of the workgroups before it; within a batch of kRowWaves rows a wave
+// adds the counts of the lower rows of the batch, so waves need no barrier
+// after the first.
+template <class In, bool kFast, int CH>
+__global__ __launch_bounds__(kRowWaves * kWave) void compact_rows_kernel(
+    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+    const SelState* __restrict__ st, const float* __restrict__ tau_p,
+    const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
+    int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
+    float* __restrict__ out_val) {
+  __shared__ uint32_t wsum[kRowWaves];
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);  // wave-uniform
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t R = int64_t(kRowWaves) * rpw;
+  const int64_t r0 = int64_t(blockIdx.x) * R;
+  const int64_t r1 = (r0 + R < M) ? r0 + R : M;
+  const int64_t slab = int64_t(kWave) * CH * 8;
+  const uint32_t tkey = st->tau_key;
+  const float tau = *tau_p;
+  const uint32_t cap = uint32_t(capacity < INT32_MAX ? capacity : INT32_MAX);
+  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
+  // entries of the workgroups before this one
+  uint32_t base = 0;
+  {
+    uint32_t s = 0;
+    for (int64_t g = threadIdx.x; g < int64_t(blockIdx.x); g += kRowWaves * kWave) s += gsum[g];
+    s = wave_sum_u32(s);
+    if (lane == 0) wsum[w] = s;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kRowWaves; ++i) base += wsum[i];
+  }
+  for (int64_t rb = r0; rb < r1; rb += kRowWaves) {
+    const int64_t r = rb + w;
+    uint32_t before = 0, all = 0, own = 0;
+#pragma unroll
+    for (int j = 0; j < kRowWaves; ++j) {
+      const uint32_t cj = (rb + j < r1) ? cnt[rb + j] : 0u;
+      before += (j < w) ? cj : 0u;
+      own = (j == w) ? cj : own;
+      all += cj;
+    }
+    if (r < r1) {
+      const typename In::T* row = A + r * lda;
+      uint32_t pos = base + before;
+      for (int64_t c0 = 0; c0 < K; c0 += slab) {
+        Vec8<In> v[CH];
+        load_wave_slab<In, kFast, CH>(row, c0, K, v);
+        compact_slab<In, CH>(v, c0, r, tkey, tau, pos, cap, out_row, out_col, out_val);
+      }
+      if (lane == 0) row_ptr[r + 1] = int32_t(base + before + own);
+    }
+    base += all;
+  }
+}
+
+// Words after the 256-byte state: bfloat16 has the coarse partial rows and the
+// fine histogram, float32 one 2048-bin histogram per pass; both then hold the
+// row-group totals and the per-row counts.
 template <class In>
 constexpr size_t hist_words() {
   if constexpr (In::kBytes == 2)
-    return size_t(kCoarseBins + kFineBins);
+    return size_t(kMaxH16Groups) * kCoarseBins + kFineBins;
   else
     return size_t(F32Digits::kPasses) * kHistBins;
 }
@@ -399,16 +533,47 @@ __global__ void select_init_kernel(SelState* st, uint32_t* hist, int64_t nwords,
   }
 }
 
-template <class In, bool kFast, int CH>
+template <class In, bool kFast, int CH, bool kPick>
 void launch_rows(const typename In::T* A, int64_t M, int64_t K, int64_t lda, SelState* st,
-                 const float* tau, int64_t capacity, int32_t* row, int32_t* col, float* val,
-                 int32_t* row_ptr, hipStream_t stream) {
-  const unsigned blocks = row_blocks(M);
-  count_rows_kernel<In, kFast, CH><<<blocks, kRowWaves * kWave, 0, stream>>>(A, M, K, lda, st,
-                                                                            row_ptr);
-  scan_rows_kernel<<<1, kScanThreads, 0, stream>>>(row_ptr, M);
-  compact_rows_kernel<In, kFast, CH><<<blocks, kRowWaves * kWave, 0, stream>>>(
-      A, M, K, lda, st, tau, row_ptr, capacity, row, col, val);
+                 const uint32_t* fine, float* tau, uint32_t* gsum, uint32_t* cnt,
+                 int64_t capacity, int32_t* row, int32_t* col, float* val, int32_t* row_ptr,
+                 hipStream_t stream) {
+  const int64_t rpw = rows_per_wave(M);
+  const dim3 g(static_cast<unsigned>(row_groups(M)));
+  count_rows_kernel<In, kFast, CH, kPick><<<g, kRowWaves * kWave, 0, stream>>>(
+      A, M, K, lda, rpw, st, fine, tau, cnt, gsum);
+  compact_rows_kernel<In, kFast, CH><<<g, kRowWaves * kWave, 0, stream>>>(
+      A, M, K, lda, rpw, st, tau, cnt, gsum, capacity, row_ptr, row, col, val);
+}
+
+template <class In, bool kFast, bool kPick>
+hipError_t rows_dispatch(const typename In::T* A, int64_t M, int64_t K, int64_t lda,
+                         SelState* st, const uint32_t* fine, float* tau, uint32_t* gsum,
+                         uint32_t* cnt, int64_t capacity, int32_t* row, int32_t* col, float* val,
+                         int32_t* row_ptr, hipStream_t stream) {
+  // rows up to 512 * CH columns in one slab (bfloat16: 8192, float32: 4096)
+  constexpr int kMaxCh = In::kBytes == 2 ? 16 : 8;
+  switch (chunks_per_lane(K, kMaxCh)) {
+#define FP4LIN_ROWS(CH)                                                                          \
+  case CH:                                                                                       \
+    launch_rows<In, kFast, CH, kPick>(A, M, K, lda, st, fine, tau, gsum, cnt, capacity, row,    \
+                                      col, val, row_ptr, stream);                                \
+    return hipSuccess;
+    FP4LIN_ROWS(1)
+    FP4LIN_ROWS(2)
+    FP4LIN_ROWS(4)
+    FP4LIN_ROWS(8)
+#undef FP4LIN_ROWS
+    case 16:
+      if constexpr (kMaxCh >= 16) {
+        launch_rows<In, kFast, 16, kPick>(A, M, K, lda, st, fine, tau, gsum, cnt, capacity, row,
+                                          col, val, row_ptr, stream);
+        return hipSuccess;
+      }
+      return hipErrorInvalidValue;
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 template <class In, bool kFast>
@@ -419,25 +584,26 @@ hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t
   const T* A = static_cast<const T*>(Ap);
   SelState* st = static_cast<SelState*>(ws);
   uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 256);
-  const int64_t nwords = int64_t(hist_words<In>());
-  select_init_kernel<<<1, 256, 0, stream>>>(st, hist, nwords, k);
+  uint32_t* gsum = hist + hist_words<In>();
+  uint32_t* cnt = gsum + kMaxRowGroups;
+  hipError_t e = hipSuccess;
   if constexpr (In::kBytes == 2) {
     // one workgroup per CU (MI355X: 256), at least one row per wave
     int64_t wgs = (M + kH16Waves - 1) / kH16Waves;
-    wgs = wgs < 256 ? wgs : 256;
+    wgs = wgs < kMaxH16Groups ? wgs : kMaxH16Groups;
     const int64_t per = (M + wgs - 1) / wgs;
-    uint32_t* coarse = hist;
-    uint32_t* fine = hist + kCoarseBins;
+    uint32_t* part = hist;
+    uint32_t* fine = hist + size_t(kMaxH16Groups) * kCoarseBins;
     const dim3 g(static_cast<unsigned>(wgs));
+    // k < M*K < 2^32
+    const uint32_t k32 = uint32_t(k);
     switch (chunks_per_lane(K, 16)) {
-#define FP4LIN_H16(CH)                                                                            \
-  case CH:                                                                                        \
-    select_hist16_kernel<kFast, false, CH><<<g, kH16Threads, 0, stream>>>(A, M, K, lda, per, st,  \
-                                                                         coarse);                 \
-    select_pick_kernel<<<1, 256, 0, stream>>>(st, coarse, kCoarseBits, 0, 16, tau);               \
-    select_hist16_kernel<kFast, true, CH><<<g, kH16Threads, 0, stream>>>(A, M, K, lda, per, st,   \
-                                                                        fine);                    \
-    select_pick_kernel<<<1, 256, 0, stream>>>(st, fine, kFineBits, 1, 16, tau);                   \
+#define FP4LIN_H16(CH)                                                                           \
+  case CH:                                                                                       \
+    select_hist16_kernel<kFast, false, CH><<<g, kH16Threads, 0, stream>>>(A, M, K, lda, per,     \
+                                                                         part, 0, 0u, st, fine); \
+    select_hist16_kernel<kFast, true, CH><<<g, kH16Threads, 0, stream>>>(                        \
+        A, M, K, lda, per, part, int(wgs), k32, st, fine);                                       \
     break;
       FP4LIN_H16(1)
       FP4LIN_H16(2)
@@ -448,7 +614,10 @@ hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t
       default:
         return hipErrorInvalidValue;
     }
+    e = rows_dispatch<In, kFast, true>(A, M, K, lda, st, fine, tau, gsum, cnt, capacity, row,
+                                       col, val, row_ptr, stream);
   } else {
+    select_init_kernel<<<1, 256, 0, stream>>>(st, hist, int64_t(hist_words<In>()), k);
     // Enough workgroups to fill the chip, each with several slabs so that the
     // per-group histogram merge stays small.
     const int64_t slab = int64_t(kHistThreads) * kHistCh * 8;
@@ -464,30 +633,18 @@ hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t
       select_pick_kernel<<<1, 256, 0, stream>>>(st, hist + size_t(p) * kHistBins, width,
                                                  p == F32Digits::kPasses - 1 ? 1 : 0, 0, tau);
     }
+    e = rows_dispatch<In, kFast, false>(A, M, K, lda, st, nullptr, tau, gsum, cnt, capacity, row,
+                                        col, val, row_ptr, stream);
   }
-  // rows up to 512 * CH columns in one slab (bfloat16: 8192, float32: 4096)
-  constexpr int kMaxCh = In::kBytes == 2 ? 16 : 8;
-  switch (chunks_per_lane(K, kMaxCh)) {
-    case 1: launch_rows<In, kFast, 1>(A, M, K, lda, st, tau, capacity, row, col, val, row_ptr, stream); break;
-    case 2: launch_rows<In, kFast, 2>(A, M, K, lda, st, tau, capacity, row, col, val, row_ptr, stream); break;
-    case 4: launch_rows<In, kFast, 4>(A, M, K, lda, st, tau, capacity, row, col, val, row_ptr, stream); break;
-    case 8: launch_rows<In, kFast, 8>(A, M, K, lda, st, tau, capacity, row, col, val, row_ptr, stream); break;
-    case 16:
-      if constexpr (kMaxCh >= 16) {
-        launch_rows<In, kFast, 16>(A, M, K, lda, st, tau, capacity, row, col, val, row_ptr, stream);
-        break;
-      }
-      return hipErrorInvalidValue;
-    default:
-      return hipErrorInvalidValue;
-  }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t select_workspace_bytes(bool bf16) {
-  const size_t words = bf16 ? hist_words<BF16In>() : hist_words<F32In>();
+size_t select_workspace_bytes(bool bf16, int64_t M) {
+  const size_t words = (bf16 ? hist_words<BF16In>() : hist_words<F32In>()) +
+                       size_t(kMaxRowGroups) + size_t(M);
   return 256 + words * 4;
 }
 

@@ -237,7 +237,11 @@ def test_select_tiny_workload(ql, q):
 
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
-@pytest.mark.parametrize("M,K", [(1, 1), (1, 5), (3, 7), (100, 700), (257, 129)])
+@pytest.mark.parametrize("M,K", [(1, 1), (1, 5), (3, 7), (100, 700), (257, 129),
+                                 # 4097 rows: the last bfloat16 histogram workgroups get no rows
+                                 (4097, 16),
+                                 # over 8192 rows: 2 and 3 rows per wave, the last row group short
+                                 (9000, 3), (16389, 24)])
 def test_select_shapes(ql, dtype, M, K):
     log(f"select {dtype} {M}x{K}")
     rng = np.random.default_rng(M + K)
