@@ -433,22 +433,26 @@ __device__ inline void compact_slab(const Vec8<In> (&v)[CH], int64_t c0, int64_t
       total += uint32_t(__popcll(b));
       mine |= uint32_t(p) << i;
     }
-    if (mine) {
-      // positions are below capacity < 2^31 and columns below K < 2^31
-      uint32_t p = pos + lower;
-      const int c = int(c0) + (j * kWave + lane) * 8;
+    // One store per array for each set bit of the lane, lowest first: a lane
+    // rarely holds more than one entry of a chunk, so the wave usually
+    // stores once instead of once per element position.
+    uint32_t p = pos + lower;  // positions below capacity < 2^31, columns below K < 2^31
+    const int c = int(c0) + (j * kWave + lane) * 8;
+    while (mine) {
+      const int i = __builtin_ctz(mine);
+      mine &= mine - 1u;
+      typename In::T x = v[j].v[0];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // p < cap always holds when tau is the true order statistic
-        // (nnz <= n-1-k); the test only keeps a wrong tau from writing out of bounds.
-        if (((mine >> i) & 1u) && p < cap) {
-          const float a = In::widen(v[j].v[i]);
-          out_row[p] = int32_t(r);
-          out_col[p] = c + i;
-          out_val[p] = __fsub_rn(a, copysignf(tau, a));
-          ++p;
-        }
+      for (int q = 1; q < 8; ++q) x = (i == q) ? v[j].v[q] : x;
+      // p < cap always holds when tau is the true order statistic
+      // (nnz <= n-1-k); the test only keeps a wrong tau from writing out of bounds.
+      if (p < cap) {
+        const float a = In::widen(x);
+        out_row[p] = int32_t(r);
+        out_col[p] = c + i;
+        out_val[p] = __fsub_rn(a, copysignf(tau, a));
       }
+      ++p;
     }
     pos += total;
   }

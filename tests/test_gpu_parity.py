@@ -192,6 +192,31 @@ def test_quantize_weight_adversarial(ql, dtype):
 def test_quantize_weight_every_bf16_value(ql):
     X = all_bf16_scaled_rows()
     check_quantize_weight(ql, wl.from_f32(X.f32.T.copy(), wl.BF16))
+    # 128 and 136 columns: every 8-column group of the column kernels full
+    check_quantize_weight(ql, wl.from_f32(X.f32[:128].T.copy(), wl.BF16))
+    pad = np.zeros((136, X.f32.shape[1]), np.float32)
+    pad[:X.f32.shape[0]] = X.f32[:136]
+    check_quantize_weight(ql, wl.from_f32(pad.T.copy(), wl.BF16))
+
+
+# N % 8 == 0 with aligned bfloat16 rows: whole 8-column groups, the last
+# 128-column tile ragged.
+@pytest.mark.parametrize("K,N", [(1, 8), (7, 16), (129, 64), (300, 136), (4101, 72),
+                                 (2, 1032)])
+def test_quantize_weight_bf16_full_groups(ql, K, N):
+    log(f"quantize_weight bf16 {K}x{N}")
+    rng = np.random.default_rng(K * 13 + N)
+    check_quantize_weight(ql, wl.random_matrix(rng, K, N, wl.BF16, scale=0.02))
+
+
+def test_quantize_weight_bf16_special_columns(ql):
+    """Zero, negative-zero, subnormal and one-value columns inside a tile that
+    also holds ordinary columns (the tile then takes the generic encoder)."""
+    S = special_rows(wl.BF16).f32.T            # 300 x 5
+    rng = np.random.default_rng(11)
+    R = wl.random_matrix(rng, S.shape[0], 11, wl.BF16, scale=0.02).f32
+    check_quantize_weight(ql, wl.from_f32(np.concatenate([S, R], axis=1), wl.BF16))
+    check_quantize_weight(ql, wl.from_f32(np.tile(S[:, 3:], (1, 4)), wl.BF16))
 
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
