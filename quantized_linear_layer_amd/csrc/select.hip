@@ -230,16 +230,27 @@ __device__ inline uint32_t coarse_pick(const uint32_t* __restrict__ part, int np
 // below (CH chunks per lane issued together).
 //   kFine = false: every key into a 32768-bin LDS histogram; workgroup b
 //                  writes the sums of its 128 groups of 256 bins to
-//                  part[b][0 .. 128), and workgroup 0 clears fine[].
+//                  part[b][0 .. 128), and workgroup 0 clears fine[]. The
+//                  workgroup also estimates the coarse bin of rank k from its
+//                  own rows (the bin where its cumulative count passes
+//                  k * n_b / (M*K)) and saves the exact fine counts of that
+//                  bin and its two neighbours: win[b] = first of the three,
+//                  fwin[b][0 .. 768) = their 256-bin histograms.
 //   kFine = true:  the workgroup finds the coarse bin from the nparts partial
-//                  rows, then histograms the keys of that bin (key >> 8 equal
-//                  to it) in a 256-bin LDS histogram, merged bin by bin into
-//                  fine[].
+//                  rows. If every coarse workgroup saved that bin or has no
+//                  key in it, the saved counts add up to its whole fine
+//                  histogram: workgroup 0 writes that sum to fine[] and A is
+//                  not read again. Otherwise every workgroup histograms the
+//                  keys of that bin (key >> 8 equal to it) in a 256-bin LDS
+//                  histogram, merged bin by bin into fine[].
+constexpr int kWinBins = 3;                     // coarse bins saved per workgroup
+constexpr int kWinWords = kWinBins * kFineBins;
+
 template <bool kFast, bool kFine, int CH>
 __global__ __launch_bounds__(kH16Threads) void select_hist16_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rows_per_wg,
     uint32_t* __restrict__ part, int nparts, uint32_t k, SelState* __restrict__ st,
-    uint32_t* __restrict__ fine) {
+    uint32_t* __restrict__ fine, uint32_t* __restrict__ win, uint32_t* __restrict__ fwin) {
   constexpr int kBins = kFine ? kFineBins : kKeyBins16;
   __shared__ uint32_t h[kBins];
   const int t = threadIdx.x;
@@ -248,6 +259,33 @@ __global__ __launch_bounds__(kH16Threads) void select_hist16_kernel(
   uint32_t prefix = 0u;
   if constexpr (kFine) {
     prefix = coarse_pick(part, nparts, k, st);
+    int miss = 0;
+    for (int w = t; w < nparts; w += kH16Threads)
+      if (prefix - win[w] >= uint32_t(kWinBins) && part[size_t(w) * kCoarseBins + prefix] != 0u)
+        miss = 1;
+    if (!__syncthreads_or(miss)) {
+      // fine[i] = sum over the coarse workgroups of their saved counts of
+      // key (prefix << 8) | i; workgroup b forms bins b, b + gridDim.x, ...
+      // and thread t reads coarse workgroup t's count.
+      static_assert(kMaxH16Groups <= kH16Threads, "one coarse workgroup per thread");
+      __shared__ uint32_t wred[kH16Waves];
+      const uint32_t d = (t < nparts) ? prefix - win[t] : uint32_t(kWinBins);
+      const int lane = t & (kWave - 1);
+      for (int i = blockIdx.x; i < kFineBins; i += gridDim.x) {
+        uint32_t x = (d < uint32_t(kWinBins)) ? fwin[size_t(t) * kWinWords + d * kFineBins + i] : 0u;
+        x = wave_sum_u32(x);
+        if (lane == 0) wred[t / kWave] = x;
+        __syncthreads();
+        if (t == 0) {
+          uint32_t y = 0;
+#pragma unroll
+          for (int w = 0; w < kH16Waves; ++w) y += wred[w];
+          fine[i] = y;
+        }
+        __syncthreads();
+      }
+      return;
+    }
   } else {
     if (blockIdx.x == 0)
       for (int i = t; i < kFineBins; i += kH16Threads) fine[i] = 0u;
@@ -304,7 +342,39 @@ __global__ __launch_bounds__(kH16Threads) void select_hist16_kernel(
     sum += __shfl_xor(sum, 1, kWave);
     sum += __shfl_xor(sum, 2, kWave);
     sum += __shfl_xor(sum, 4, kWave);
-    if ((t & 7) == 0) part[size_t(blockIdx.x) * kCoarseBins + (t >> 3)] = sum;
+    __shared__ uint32_t csum[kCoarseBins];
+    __shared__ uint32_t wbase;
+    if ((t & 7) == 0) {
+      part[size_t(blockIdx.x) * kCoarseBins + (t >> 3)] = sum;
+      csum[t >> 3] = sum;
+    }
+    __syncthreads();
+    if (t < kWave) {
+      // this workgroup's estimate of the coarse bin of rank k (lane t owns
+      // bins 2t and 2t+1); its counts are below M*K < 2^32
+      const uint32_t a = csum[2 * t], b = csum[2 * t + 1];
+      uint32_t nb;
+      const uint32_t ex = wave_exclusive_scan(a + b, nb);
+      const uint32_t target = uint32_t(uint64_t(k) * nb / uint64_t(M * K));
+      const uint64_t hit = __ballot(target >= ex && target - ex < a + b);
+      uint32_t bin = 0u;
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        const uint32_t exl = uint32_t(__shfl(int(ex), l, kWave));
+        const uint32_t al = uint32_t(__shfl(int(a), l, kWave));
+        bin = uint32_t(2 * l) + (target - exl < al ? 0u : 1u);
+      }
+      const uint32_t first =
+          bin < 1u ? 0u : (bin + kWinBins - 1 > kCoarseBins ? kCoarseBins - kWinBins : bin - 1u);
+      if (t == 0) {
+        wbase = first;
+        win[blockIdx.x] = first;
+      }
+    }
+    __syncthreads();
+    const uint32_t first = wbase;
+    for (int i = t; i < kWinWords; i += kH16Threads)
+      fwin[size_t(blockIdx.x) * kWinWords + i] = h[first * kFineBins + i];
   }
 }
 
@@ -521,7 +591,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void compact_rows_kernel(
 template <class In>
 constexpr size_t hist_words() {
   if constexpr (In::kBytes == 2)
-    return size_t(kMaxH16Groups) * kCoarseBins + kFineBins;
+    return size_t(kMaxH16Groups) * (kCoarseBins + 1 + kWinWords) + kFineBins;
   else
     return size_t(F32Digits::kPasses) * kHistBins;
 }
@@ -597,17 +667,19 @@ hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t
     wgs = wgs < kMaxH16Groups ? wgs : kMaxH16Groups;
     const int64_t per = (M + wgs - 1) / wgs;
     uint32_t* part = hist;
-    uint32_t* fine = hist + size_t(kMaxH16Groups) * kCoarseBins;
+    uint32_t* fine = part + size_t(kMaxH16Groups) * kCoarseBins;
+    uint32_t* win = fine + kFineBins;
+    uint32_t* fwin = win + kMaxH16Groups;
     const dim3 g(static_cast<unsigned>(wgs));
     // k < M*K < 2^32
     const uint32_t k32 = uint32_t(k);
     switch (chunks_per_lane(K, 16)) {
 #define FP4LIN_H16(CH)                                                                           \
   case CH:                                                                                       \
-    select_hist16_kernel<kFast, false, CH><<<g, kH16Threads, 0, stream>>>(A, M, K, lda, per,     \
-                                                                         part, 0, 0u, st, fine); \
+    select_hist16_kernel<kFast, false, CH><<<g, kH16Threads, 0, stream>>>(                       \
+        A, M, K, lda, per, part, 0, k32, st, fine, win, fwin);                                   \
     select_hist16_kernel<kFast, true, CH><<<g, kH16Threads, 0, stream>>>(                        \
-        A, M, K, lda, per, part, int(wgs), k32, st, fine);                                       \
+        A, M, K, lda, per, part, int(wgs), k32, st, fine, win, fwin);                            \
     break;
       FP4LIN_H16(1)
       FP4LIN_H16(2)

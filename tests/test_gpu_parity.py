@@ -286,6 +286,25 @@ def test_select_many_ties(ql, dtype):
         check_select(ql, A, q)
 
 
+def test_select_bf16_uneven_row_blocks(ql):
+    """bfloat16 select where the first 16 rows (one histogram workgroup) are
+    tiny apart from a few entries near the global 0.99 quantile: that
+    workgroup's own quantile estimate lies far below the global one while it
+    still holds keys in the global quantile's coarse bin, so the second pass
+    over A is needed. Also the mirror case: a block of huge values."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((64, 1000)).astype(np.float32)
+    x[:16] *= np.float32(1e-3)
+    pos = rng.choice(16 * 1000, size=48, replace=False)
+    x[:16].reshape(-1)[pos] = np.float32(2.6) * rng.choice([-1.0, 1.0], size=48).astype(np.float32)
+    for q in (0.99, 0.995, 0.9):
+        check_select(ql, wl.from_f32(x, wl.BF16), q)
+    y = rng.standard_normal((64, 1000)).astype(np.float32)
+    y[32:48] *= np.float32(1e4)
+    for q in (0.5, 0.74, 0.75, 0.76, 0.99):
+        check_select(ql, wl.from_f32(y, wl.BF16), q)
+
+
 def test_select_bf16_layer_slice(ql):
     L = wl.make_layer("llama7b_ffn_up", M=64)
     check_select(ql, L.A, L.q)
