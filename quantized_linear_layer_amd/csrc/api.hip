@@ -131,9 +131,16 @@ const char* fp4lin_status_str(fp4lin_status s) {
   return "unknown status";
 }
 
-fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, int64_t K,
-                                    int64_t lda, double q, float* tau, fp4lin_coo dA, void* ws,
-                                    size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// fp4lin_outlier_select; with quantized set, the forward path's token-wise
+// quantization of A (Xq, sX) is done by the same kernels where the rows allow
+// it, and *quantized says whether it was.
+fp4lin_status select_impl(const void* A, fp4lin_dtype dt, int64_t M, int64_t K, int64_t lda,
+                          double q, float* tau, fp4lin_coo dA, void* ws, size_t ws_bytes,
+                          hipStream_t stream, uint8_t* Xq, float* sX, bool* quantized) {
   if (A == nullptr || tau == nullptr || dA.row == nullptr || dA.col == nullptr ||
       dA.val == nullptr || dA.row_ptr == nullptr || ws == nullptr)
     return FP4LIN_ERR_NULL;
@@ -148,9 +155,20 @@ fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, i
   if (dA.capacity < cap) return FP4LIN_ERR_CAPACITY;
   if (!aligned16(ws)) return FP4LIN_ERR_ALIGN;
   if (ws_bytes < select_ws(M, dt)) return FP4LIN_ERR_WORKSPACE;
-  return launch_status(fp4lin::launch_outlier_select(A, dt == FP4LIN_BF16, M, K, lda, k, tau,
-                                                     dA.capacity, dA.row, dA.col, dA.val, dA.row_ptr, ws,
-                                                     stream));
+  return launch_status(fp4lin::launch_outlier_select(
+      A, dt == FP4LIN_BF16, M, K, lda, k, tau, dA.capacity, dA.row, dA.col, dA.val, dA.row_ptr,
+      ws, stream, Xq, fp4lin_packed_ld(K), sX, quantized));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, int64_t K,
+                                    int64_t lda, double q, float* tau, fp4lin_coo dA, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  return select_impl(A, dt, M, K, lda, q, tau, dA, ws, ws_bytes, stream, nullptr, nullptr,
+                     nullptr);
 }
 
 fp4lin_status fp4lin_quantize_act(const void* X, fp4lin_dtype dt, int64_t M, int64_t K,
@@ -239,11 +257,16 @@ fp4lin_status fp4lin_forward(const void* A, const void* W, fp4lin_dtype dt, int6
   float* sW = reinterpret_cast<float*>(base + o.sW);
   void* scratch = base + o.scratch;
   const size_t scratch_bytes = o.total - o.scratch;
-  fp4lin_status s =
-      fp4lin_outlier_select(A, dt, M, K, lda, q, tau, coo, scratch, scratch_bytes, stream);
+  // bfloat16 rows that fit one slab are quantized by the select's compaction,
+  // which reads A anyway
+  bool a_done = false;
+  fp4lin_status s = select_impl(A, dt, M, K, lda, q, tau, coo, scratch, scratch_bytes, stream, Aq,
+                                sA, &a_done);
   if (s != FP4LIN_OK) return s;
-  s = fp4lin_quantize_act(A, dt, M, K, lda, tau, Aq, sA, stream);
-  if (s != FP4LIN_OK) return s;
+  if (!a_done) {
+    s = fp4lin_quantize_act(A, dt, M, K, lda, tau, Aq, sA, stream);
+    if (s != FP4LIN_OK) return s;
+  }
   s = fp4lin_quantize_weight(W, dt, K, N, ldw, Wq, sW, scratch, scratch_bytes, stream);
   if (s != FP4LIN_OK) return s;
   return fp4lin_gemm(Aq, sA, Wq, sW, M, N, K, &coo, W, dt, ldw, Y, ldy, stream);

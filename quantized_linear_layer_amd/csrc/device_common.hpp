@@ -185,4 +185,87 @@ __device__ inline uint32_t wave_exclusive_scan(uint32_t v, uint32_t& total) {
   return x - v;
 }
 
+// ---------------------------------------------------------------------------
+// Token-wise quantization of one bfloat16 row held in registers as raw 16-byte
+// words (16-byte aligned rows with K % 8 == 0 that fit one slab). The row amax
+// is a packed 16-bit integer max of the magnitude bits (finite bfloat16 magnitudes
+// order like their bits), and two codes are encoded per 32-bit word. When
+// 4 * inv is finite, y4 = RN32(|x| * 4inv) equals 4 * RN32(|x| * inv) wherever
+// the code can depend on it (scaling by 4 commutes with rounding in the normal
+// range, and |x| * inv <= 6 cannot overflow), so the code is the table lookup
+// at n = (uint)min(y4, 20) with no NaN to guard against; otherwise (a zero or
+// subnormal row amax) the encoder of the generic path is used.
+__device__ inline uint32_t bf16_pair_code(uint32_t w, float tau, float inv4) {
+  const float lo = fminf(fabsf(__uint_as_float(w << 16)), tau);
+  const float hi = fminf(fabsf(__uint_as_float(w & 0xffff0000u)), tau);
+  const uint32_t nlo = uint32_t(fminf(__fmul_rn(lo, inv4), 20.0f));
+  const uint32_t nhi = uint32_t(fminf(__fmul_rn(hi, inv4), 20.0f));
+  constexpr uint64_t kLut = e2m1_lut();
+  const uint32_t mlo = uint32_t(kLut >> (3u * nlo)) & 7u;
+  const uint32_t mhi = uint32_t(kLut >> (3u * nhi)) & 7u;
+  return mlo | (mhi << 4) | ((w >> 12) & 0x8u) | ((w >> 24) & 0x80u);
+}
+
+__device__ inline uint32_t bf16_pair_code_slow(uint32_t w, float tau, float inv) {
+  const float lo = fminf(fabsf(__uint_as_float(w << 16)), tau);
+  const float hi = fminf(fabsf(__uint_as_float(w & 0xffff0000u)), tau);
+  return e2m1_magnitude(lo, inv) | (e2m1_magnitude(hi, inv) << 4) | ((w >> 12) & 0x8u) |
+         ((w >> 24) & 0x80u);
+}
+
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, kWave);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+
+// Row amax (clamped to tau), scale and codes of a bfloat16 row whose words
+// w[j] (chunk j of lane l: columns (64j + l) * 8 .. +7, zero past K) the wave
+// holds: the codes of the columns below Kp (zero padding included) go to
+// qrow, 8 per 32-bit store, and lane 0 writes the scale to *s_out.
+template <int CH>
+__device__ inline void quantize_bf16_row(const uint4 (&w)[CH], int64_t Kp, float tau,
+                                         uint8_t* __restrict__ qrow, float* __restrict__ s_out) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & (kWave - 1);
+  u16x2 m2 = {0, 0};
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const uint32_t q[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, q[i] & 0x7fff7fffu));
+  }
+  const uint32_t mk = wave_max_u32(uint32_t(m2.x > m2.y ? m2.x : m2.y));
+  const float amax = fminf(__uint_as_float(mk << 16), tau);
+  float s, inv;
+  vector_scale(amax, s, inv);
+  if (lane == 0) *s_out = s;
+  const float inv4 = __fmul_rn(inv, 4.0f);
+  if (inv4 < __builtin_huge_valf()) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int64_t c = (int64_t(j) * kWave + lane) * 8;
+      if (c < Kp)
+        *reinterpret_cast<uint32_t*>(qrow + c / 2) =
+            bf16_pair_code(w[j].x, tau, inv4) | (bf16_pair_code(w[j].y, tau, inv4) << 8) |
+            (bf16_pair_code(w[j].z, tau, inv4) << 16) | (bf16_pair_code(w[j].w, tau, inv4) << 24);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int64_t c = (int64_t(j) * kWave + lane) * 8;
+      if (c < Kp)
+        *reinterpret_cast<uint32_t*>(qrow + c / 2) =
+            bf16_pair_code_slow(w[j].x, tau, inv) | (bf16_pair_code_slow(w[j].y, tau, inv) << 8) |
+            (bf16_pair_code_slow(w[j].z, tau, inv) << 16) |
+            (bf16_pair_code_slow(w[j].w, tau, inv) << 24);
+    }
+  }
+}
+
 }  // namespace fp4lin

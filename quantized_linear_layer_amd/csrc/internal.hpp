@@ -10,10 +10,14 @@ namespace fp4lin {
 size_t select_workspace_bytes(bool bf16, int64_t M);
 size_t weight_workspace_bytes(int64_t N);
 
+// With quantized set, rows that allow it are also quantized token-wise (Xq
+// with row stride ldq, scales sX, clamped to tau) by the compaction, and
+// *quantized says whether that happened; with quantized null, Xq is ignored.
 hipError_t launch_outlier_select(const void* A, bool bf16, int64_t M, int64_t K, int64_t lda,
                                  int64_t k, float* tau, int64_t capacity, int32_t* row,
                                  int32_t* col, float* val, int32_t* row_ptr, void* ws,
-                                 hipStream_t stream);
+                                 hipStream_t stream, uint8_t* Xq = nullptr, int64_t ldq = 0,
+                                 float* sX = nullptr, bool* quantized = nullptr);
 
 hipError_t launch_quantize_rows(const void* X, bool bf16, int64_t M, int64_t K, int64_t ldx,
                                 const float* tau, uint8_t* Xq, int64_t ldq, float* sX,

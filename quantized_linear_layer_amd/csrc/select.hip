@@ -585,6 +585,108 @@ __global__ __launch_bounds__(kRowWaves * kWave) void compact_rows_kernel(
   }
 }
 
+// Compaction from a bfloat16 row held as raw 16-byte words (element i of a
+// chunk is the low half of word i / 2 for even i, the high half for odd i),
+// ranked as in compact_slab.
+template <int CH>
+__device__ inline void compact_words(const uint4 (&wv)[CH], int64_t r, uint32_t tkey, float tau,
+                                     uint32_t& pos, uint32_t cap, int32_t* __restrict__ out_row,
+                                     int32_t* __restrict__ out_col, float* __restrict__ out_val) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const uint32_t q[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+    uint32_t lower = 0, total = 0, mine = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t key = ((i & 1) ? (q[i >> 1] >> 16) : q[i >> 1]) & 0x7fffu;
+      const bool p = key > tkey;
+      const uint64_t b = __ballot(p);
+      lower = __builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32),
+                                        __builtin_amdgcn_mbcnt_lo(uint32_t(b), lower));
+      total += uint32_t(__popcll(b));
+      mine |= uint32_t(p) << i;
+    }
+    uint32_t p = pos + lower;  // positions below capacity < 2^31, columns below K < 2^31
+    const int c = (j * kWave + lane) * 8;
+    while (mine) {
+      const int i = __builtin_ctz(mine);
+      mine &= mine - 1u;
+      const int h = i >> 1;
+      const uint32_t word = h == 0 ? q[0] : (h == 1 ? q[1] : (h == 2 ? q[2] : q[3]));
+      // p < cap always holds when tau is the true order statistic
+      if (p < cap) {
+        const float a = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
+        out_row[p] = int32_t(r);
+        out_col[p] = c + i;
+        out_val[p] = __fsub_rn(a, copysignf(tau, a));
+      }
+      ++p;
+    }
+    pos += total;
+  }
+}
+
+// Forward path, 16-byte aligned bfloat16 rows with K % 8 == 0 whose padded
+// length fits one slab: the compaction of compact_rows_kernel and the
+// token-wise quantization of the row clamped to tau (quantize_bf16_row) from
+// one read of A.
+template <int CH>
+__global__ __launch_bounds__(kRowWaves * kWave) void compact_quantize_rows_kernel(
+    const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+    const SelState* __restrict__ st, const float* __restrict__ tau_p,
+    const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
+    int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
+    float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX) {
+  __shared__ uint32_t wsum[kRowWaves];
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);  // wave-uniform
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t R = int64_t(kRowWaves) * rpw;
+  const int64_t r0 = int64_t(blockIdx.x) * R;
+  const int64_t r1 = (r0 + R < M) ? r0 + R : M;
+  const uint32_t tkey = st->tau_key;
+  const float tau = *tau_p;
+  const uint32_t cap = uint32_t(capacity < INT32_MAX ? capacity : INT32_MAX);
+  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
+  // entries of the workgroups before this one
+  uint32_t base = 0;
+  {
+    uint32_t s = 0;
+    for (int64_t g = threadIdx.x; g < int64_t(blockIdx.x); g += kRowWaves * kWave) s += gsum[g];
+    s = wave_sum_u32(s);
+    if (lane == 0) wsum[w] = s;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kRowWaves; ++i) base += wsum[i];
+  }
+  for (int64_t rb = r0; rb < r1; rb += kRowWaves) {
+    const int64_t r = rb + w;
+    uint32_t before = 0, all = 0, own = 0;
+#pragma unroll
+    for (int j = 0; j < kRowWaves; ++j) {
+      const uint32_t cj = (rb + j < r1) ? cnt[rb + j] : 0u;
+      before += (j < w) ? cj : 0u;
+      own = (j == w) ? cj : own;
+      all += cj;
+    }
+    if (r < r1) {
+      const uint16_t* row = A + r * lda;
+      uint4 wv[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int64_t c = (int64_t(j) * kWave + lane) * 8;
+        wv[j] = *reinterpret_cast<const uint4*>(row + (c < K ? c : K - 8));
+        if (c >= K) wv[j] = make_uint4(0, 0, 0, 0);
+      }
+      uint32_t pos = base + before;
+      compact_words<CH>(wv, r, tkey, tau, pos, cap, out_row, out_col, out_val);
+      quantize_bf16_row<CH>(wv, ldq * 2, tau, Xq + r * ldq, sX + r);
+      if (lane == 0) row_ptr[r + 1] = int32_t(base + before + own);
+    }
+    base += all;
+  }
+}
+
 // Words after the 256-byte state: bfloat16 has the coarse partial rows and the
 // fine histogram, float32 one 2048-bin histogram per pass; both then hold the
 // row-group totals and the per-row counts.
@@ -607,15 +709,47 @@ __global__ void select_init_kernel(SelState* st, uint32_t* hist, int64_t nwords,
   }
 }
 
+// Quantization outputs of the forward path: when Xq is set and the rows
+// qualify, the compaction also quantizes A and sets *done.
+struct RowQuant {
+  uint8_t* Xq;
+  int64_t ldq;
+  float* sX;
+  bool* done;
+};
+
 template <class In, bool kFast, int CH, bool kPick>
 void launch_rows(const typename In::T* A, int64_t M, int64_t K, int64_t lda, SelState* st,
                  const uint32_t* fine, float* tau, uint32_t* gsum, uint32_t* cnt,
                  int64_t capacity, int32_t* row, int32_t* col, float* val, int32_t* row_ptr,
-                 hipStream_t stream) {
+                 const RowQuant& rq, hipStream_t stream) {
   const int64_t rpw = rows_per_wave(M);
   const dim3 g(static_cast<unsigned>(row_groups(M)));
   count_rows_kernel<In, kFast, CH, kPick><<<g, kRowWaves * kWave, 0, stream>>>(
       A, M, K, lda, rpw, st, fine, tau, cnt, gsum);
+  if constexpr (In::kBytes == 2 && kFast) {
+    // padded row length within one slab of 16 chunks per lane
+    if (rq.Xq != nullptr && rq.ldq * 2 <= int64_t(kWave) * 16 * 8) {
+      const uint16_t* A16 = reinterpret_cast<const uint16_t*>(A);
+      switch (chunks_per_lane(rq.ldq * 2, 16)) {
+#define FP4LIN_CQ(CQ)                                                                            \
+  case CQ:                                                                                       \
+    compact_quantize_rows_kernel<CQ><<<g, kRowWaves * kWave, 0, stream>>>(                       \
+        A16, M, K, lda, rpw, st, tau, cnt, gsum, capacity, row_ptr, row, col, val, rq.Xq,        \
+        rq.ldq, rq.sX);                                                                          \
+    *rq.done = true;                                                                             \
+    return;
+        FP4LIN_CQ(1)
+        FP4LIN_CQ(2)
+        FP4LIN_CQ(4)
+        FP4LIN_CQ(8)
+        FP4LIN_CQ(16)
+#undef FP4LIN_CQ
+        default:
+          break;
+      }
+    }
+  }
   compact_rows_kernel<In, kFast, CH><<<g, kRowWaves * kWave, 0, stream>>>(
       A, M, K, lda, rpw, st, tau, cnt, gsum, capacity, row_ptr, row, col, val);
 }
@@ -624,14 +758,14 @@ template <class In, bool kFast, bool kPick>
 hipError_t rows_dispatch(const typename In::T* A, int64_t M, int64_t K, int64_t lda,
                          SelState* st, const uint32_t* fine, float* tau, uint32_t* gsum,
                          uint32_t* cnt, int64_t capacity, int32_t* row, int32_t* col, float* val,
-                         int32_t* row_ptr, hipStream_t stream) {
+                         int32_t* row_ptr, const RowQuant& rq, hipStream_t stream) {
   // rows up to 512 * CH columns in one slab (bfloat16: 8192, float32: 4096)
   constexpr int kMaxCh = In::kBytes == 2 ? 16 : 8;
   switch (chunks_per_lane(K, kMaxCh)) {
 #define FP4LIN_ROWS(CH)                                                                          \
   case CH:                                                                                       \
     launch_rows<In, kFast, CH, kPick>(A, M, K, lda, st, fine, tau, gsum, cnt, capacity, row,    \
-                                      col, val, row_ptr, stream);                                \
+                                      col, val, row_ptr, rq, stream);                            \
     return hipSuccess;
     FP4LIN_ROWS(1)
     FP4LIN_ROWS(2)
@@ -641,7 +775,7 @@ hipError_t rows_dispatch(const typename In::T* A, int64_t M, int64_t K, int64_t 
     case 16:
       if constexpr (kMaxCh >= 16) {
         launch_rows<In, kFast, 16, kPick>(A, M, K, lda, st, fine, tau, gsum, cnt, capacity, row,
-                                          col, val, row_ptr, stream);
+                                          col, val, row_ptr, rq, stream);
         return hipSuccess;
       }
       return hipErrorInvalidValue;
@@ -653,7 +787,7 @@ hipError_t rows_dispatch(const typename In::T* A, int64_t M, int64_t K, int64_t 
 template <class In, bool kFast>
 hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t k, float* tau,
                       int64_t capacity, int32_t* row, int32_t* col, float* val,
-                      int32_t* row_ptr, void* ws, hipStream_t stream) {
+                      int32_t* row_ptr, void* ws, const RowQuant& rq, hipStream_t stream) {
   using T = typename In::T;
   const T* A = static_cast<const T*>(Ap);
   SelState* st = static_cast<SelState*>(ws);
@@ -691,7 +825,7 @@ hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t
         return hipErrorInvalidValue;
     }
     e = rows_dispatch<In, kFast, true>(A, M, K, lda, st, fine, tau, gsum, cnt, capacity, row,
-                                       col, val, row_ptr, stream);
+                                       col, val, row_ptr, rq, stream);
   } else {
     select_init_kernel<<<1, 256, 0, stream>>>(st, hist, int64_t(hist_words<In>()), k);
     // Enough workgroups to fill the chip, each with several slabs so that the
@@ -710,7 +844,7 @@ hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t
                                                  p == F32Digits::kPasses - 1 ? 1 : 0, 0, tau);
     }
     e = rows_dispatch<In, kFast, false>(A, M, K, lda, st, nullptr, tau, gsum, cnt, capacity, row,
-                                        col, val, row_ptr, stream);
+                                        col, val, row_ptr, rq, stream);
   }
   if (e != hipSuccess) return e;
   return hipGetLastError();
@@ -727,15 +861,22 @@ size_t select_workspace_bytes(bool bf16, int64_t M) {
 hipError_t launch_outlier_select(const void* A, bool bf16, int64_t M, int64_t K, int64_t lda,
                                  int64_t k, float* tau, int64_t capacity, int32_t* row,
                                  int32_t* col, float* val, int32_t* row_ptr, void* ws,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, uint8_t* Xq, int64_t ldq, float* sX,
+                                 bool* quantized) {
+  bool done = false;
+  const RowQuant rq{quantized != nullptr ? Xq : nullptr, ldq, sX, &done};
   const int esz = bf16 ? 2 : 4;
   const bool fast = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && ((lda * esz) % 16 == 0) &&
                     (K % 8 == 0);
+  hipError_t e;
   if (bf16)
-    return fast ? run_select<BF16In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, stream)
-                : run_select<BF16In, false>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, stream);
-  return fast ? run_select<F32In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, stream)
-              : run_select<F32In, false>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, stream);
+    e = fast ? run_select<BF16In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, rq, stream)
+             : run_select<BF16In, false>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, rq, stream);
+  else
+    e = fast ? run_select<F32In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, rq, stream)
+             : run_select<F32In, false>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, rq, stream);
+  if (quantized != nullptr) *quantized = done && e == hipSuccess;
+  return e;
 }
 
 }  // namespace fp4lin
