@@ -432,9 +432,11 @@ def workspace_views(ql, ws, M, K, N, dtype_code, q):
         Wq=take(o.Wq, N * ldq, np.uint8).reshape(N, ldq), sW=take(o.sW, N, np.float32))
 
 
-def check_forward(ql, L: wl.Layer, rows=None):
+def check_forward(ql, L: wl.Layer, rows=None, lda=None):
     t = torch()
     A, W = to_device(L.A), to_device(L.W)
+    if lda is not None:
+        A = padded(A, lda)
     Y, ws = ql.forward(A, W, L.q, return_workspace=True)
     t.cuda.synchronize()
     ops = O.forward_operands(L.A.f32, L.W.f32, L.q)
@@ -475,6 +477,25 @@ def test_forward_small(ql, dtype, M, K, N, q):
     check_forward(ql, L)
 
 
+# bfloat16 rows inside fp4lin_forward: 16-byte aligned rows of up to 8192
+# columns are compacted and quantized by one kernel, the others by the separate
+# select and quantize_act kernels.
+@pytest.mark.parametrize("M,K,N,lda", [
+    (24, 8192, 64, None),   # 16 chunks per lane, one slab: one kernel
+    (20, 8200, 72, None),   # two slabs: separate kernels
+    (40, 300, 80, 301),     # rows not 16-byte aligned: separate kernels
+    (40, 304, 80, 312),     # aligned rows with lda != K: one kernel
+    (9, 1024, 24, None),    # fewer rows than one workgroup of each select kernel
+])
+def test_forward_bf16_row_paths(ql, M, K, N, lda):
+    log(f"forward bf16 row paths {M}x{K}x{N} lda={lda}")
+    rng = np.random.default_rng(M * 31 + K + N)
+    a = wl.draw_activation(rng, M, K, "t3", max(1, K // 200), 50.0)
+    w = wl.draw_weight(rng, K, N)
+    L = wl.Layer("bf16-rows", wl.from_f32(a, wl.BF16), wl.from_f32(w, wl.BF16), 0.99)
+    check_forward(ql, L, lda=lda)
+
+
 def test_forward_q_one_is_plain_quantized_gemm(ql):
     """q = 1 clamps nothing; with grid-exact inputs Y = A W exactly."""
     rng = np.random.default_rng(3)
@@ -496,13 +517,24 @@ def test_forward_matches_stage_calls(ql):
     t = torch()
     L = wl.make_layer("llama1.3b_ffn_up", M=256)
     A, W = to_device(L.A), to_device(L.W)
-    Y1 = ql.forward(A, W, L.q)
+    Y1, ws = ql.forward(A, W, L.q, return_workspace=True)
     tau, coo = ql.outlier_select(A, L.q)
     Aq, sA = ql.quantize_act(A, tau)
     Wq, sW = ql.quantize_weight(W)
     Y2 = ql.gemm(Aq, sA, Wq, sW, L.M, L.N, L.K, coo, W)
     t.cuda.synchronize()
     assert np.array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
+    # the forward compacts and quantizes A in one kernel; the separate calls
+    # must give the same intermediates
+    v = workspace_views(ql, ws, L.M, L.K, L.N, 1, L.q)
+    nnz = v["nnz"]
+    assert_bits_equal(v["tau"], host(tau)[0], "tau")
+    assert_bits_equal(v["row_ptr"], host(coo.row_ptr), "row_ptr")
+    assert_bits_equal(v["row"], host(coo.row)[:nnz], "coo row")
+    assert_bits_equal(v["col"], host(coo.col)[:nnz], "coo col")
+    assert_bits_equal(v["val"], host(coo.val)[:nnz], "coo val")
+    assert_bits_equal(v["Aq"], host(Aq), "Aq")
+    assert_bits_equal(v["sA"], host(sA), "sA")
 
 
 def test_gemm_equals_gemm_then_sparse_add(ql):
