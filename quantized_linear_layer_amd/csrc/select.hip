@@ -13,23 +13,28 @@
 // rank is appended to the prefix. Everything stays on the device; the host
 // never reads a histogram.
 //
-// bfloat16 keys (15 bits) take two passes over A. Pass 1 builds a full
-// 32768-bin histogram per workgroup in LDS (one 16-wave workgroup per CU),
-// which spreads the densely populated magnitudes over many bins so that few
-// lanes of an LDS atomic meet on one address, and writes only its 128 coarse
-// sums (256 keys each), one row of partial sums per workgroup: merging every
-// non-zero fine bin with device-wide atomics costs several times the pass
-// itself. Pass 2 adds the partial rows up in every workgroup, finds the coarse
-// bin that holds rank k, and histograms the 256 keys of that bin. The row count
-// that follows finds tau's key from that histogram in every wave. No kernel
-// needs a cleared buffer on entry, so no launch is spent on set-up.
+// bfloat16 keys (15 bits): pass 1 builds a full 32768-bin histogram per
+// workgroup in LDS (one 16-wave workgroup per CU), which spreads the densely
+// populated magnitudes over many bins so that few lanes of an LDS atomic meet
+// on one address, and writes only its 128 coarse sums (256 keys each), one row
+// of partial sums per workgroup: merging every non-zero fine bin with
+// device-wide atomics costs several times the pass itself. From its own rows
+// the workgroup also estimates the coarse bin of rank k and saves the exact
+// fine counts of that bin and its two neighbours. Pass 2 adds the partial rows
+// up in every workgroup and finds the coarse bin that holds rank k. When every
+// workgroup saved that bin or has no key in it, the fine histogram is the sum
+// of the saved counts and A is not read again; otherwise pass 2 histograms the
+// 256 keys of that bin from A. The row count that follows finds tau's key from
+// the fine histogram in every wave. No kernel needs a cleared buffer on entry,
+// so no launch is spent on set-up.
 // float32 keys (31 bits) take three passes of 11, 11 and 9 bits with a
 // 2048-bin histogram and a one-workgroup pick kernel after each.
 //
 // Then the entries with |a| > tau are counted per row, with one total per
 // workgroup of rows; the compaction adds up the totals of the workgroups before
 // its own, which gives row_ptr and the row-major positions without a separate
-// scan.
+// scan. In the whole-layer forward, bfloat16 rows that fit one slab are also
+// quantized token-wise by the compaction kernel, from the same registers.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -687,8 +692,9 @@ __global__ __launch_bounds__(kRowWaves * kWave) void compact_quantize_rows_kerne
   }
 }
 
-// Words after the 256-byte state: bfloat16 has the coarse partial rows and the
-// fine histogram, float32 one 2048-bin histogram per pass; both then hold the
+// Words after the 256-byte state: bfloat16 has the coarse partial rows, the
+// fine histogram, and per coarse workgroup its first saved bin and its saved
+// fine counts; float32 one 2048-bin histogram per pass. Both then hold the
 // row-group totals and the per-row counts.
 template <class In>
 constexpr size_t hist_words() {
