@@ -50,6 +50,9 @@ Readings where the pages are silent (each is listed in the design notes):
       every step in float64 and compares by relative Frobenius error.
   R9  dgrad dX = Q(dY) Q(W)^T: dY quantized per row over N (no clamp), W
       re-quantized per row over N so that its scale leaves the reduction.
+  R10 wgrad dW = Q(A)^T Q(dY): A and dY both quantized per column over M (the
+      reduction), with no clamp and no compensation term, so that both scales
+      leave the reduction; the channel-wise quantizer of W applied to A and dY.
 """
 from __future__ import annotations
 
@@ -310,6 +313,21 @@ def dgrad(dY32: np.ndarray, W32: np.ndarray, rows=None):
         rows = np.arange(c_dy.shape[0])
     acc = integer_product(c_dy[rows], c_w2)
     return scaled_product(acc, s_dy[rows], s_w2), (dYq, s_dy, c_dy), (Wq2, s_w2, c_w2)
+
+
+def wgrad(A32: np.ndarray, dY32: np.ndarray, rows=None):
+    """dW = Q(A)^T Q(dY) with A (M x K) and dY (M x N) quantized per column over
+    M (reading R10): the weight quantizer applied to A and to dY gives both
+    operands packed along M, one packed row per column of A or dY.
+
+    Returns (dW float64 K x N, or its listed rows, (Aq', s_A', codes_A' K x M),
+    (dYq', s_dY', codes_dY' N x M))."""
+    Aq2, s_a2, c_a2 = quantize_weight(A32)
+    dYq2, s_dy2, c_dy2 = quantize_weight(dY32)
+    if rows is None:
+        rows = np.arange(c_a2.shape[0])
+    acc = integer_product(c_a2[rows], c_dy2)
+    return scaled_product(acc, s_a2[rows], s_dy2), (Aq2, s_a2, c_a2), (dYq2, s_dy2, c_dy2)
 
 
 def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:

@@ -278,6 +278,57 @@ def test_dgrad_closed_form():
     assert np.array_equal(dX, dY.astype(np.float64) @ W.astype(np.float64).T)
 
 
+def test_wgrad_closed_form():
+    """A and dY columns grid-exact over M: Q(A)^T Q(dY) == A^T dY exactly (R10).
+    M = 150 pads the packed columns; K != N catches a swapped operand."""
+    rng = np.random.default_rng(9)
+    M, K, N = 150, 13, 21
+    A = _grid_exact(rng, M, K, axis=0)
+    dY = _grid_exact(rng, M, N, axis=0)
+    dW, (Aq2, sA2, cA2), (dYq2, sdY2, cdY2) = O.wgrad(A, dY)
+    assert dW.shape == (K, N)
+    assert np.array_equal(dW, A.astype(np.float64).T @ dY.astype(np.float64))
+    assert Aq2.shape == (K, O.packed_ld(M)) and dYq2.shape == (N, O.packed_ld(M))
+
+
+def test_wgrad_brute_force_tiny():
+    """Tiny wgrad by explicit loops: per-column amax, exactly rounded scales,
+    y = RN32(|x| * inv), nearest grid value (ties away), then the exact sum
+    over M scaled by both column scales (R2-R4, R10)."""
+    rng = np.random.default_rng(10)
+    M, K, N = 7, 3, 4
+    A = (rng.standard_normal((M, K)) * 3).astype(np.float32)
+    dY = (rng.standard_normal((M, N)) * 0.01).astype(np.float32)
+    A[2, 1] = 0.0
+    dY[:, 3] = 0.0   # an all-zero column: s = 0, codes +-0
+
+    def column_codes(X, j):
+        col = X[:, j]
+        amax = max(abs(float(v)) for v in col)
+        if amax == 0.0:
+            return [0.0] * len(col), np.float32(0.0), [(np.signbit(v) << 3) for v in col]
+        s = _rn32_fraction(Fraction(amax) / 6)
+        inv = _rn32_fraction(6 / Fraction(amax))
+        vals, codes = [], []
+        for v in col:
+            y = np.float32(np.float32(abs(v)) * inv)
+            m = int(_brute_nearest(np.array([y], np.float32))[0])
+            vals.append((-1.0 if np.signbit(v) else 1.0) * GRID[m])
+            codes.append((int(np.signbit(v)) << 3) | m)
+        return vals, s, codes
+
+    dW, (_, sA2, cA2), (_, sdY2, cdY2) = O.wgrad(A, dY)
+    for k in range(K):
+        va, sa, ca = column_codes(A, k)
+        assert sA2[k] == sa and list(cA2[k]) == ca, k
+        for n in range(N):
+            vd, sd, cd = column_codes(dY, n)
+            if k == 0:
+                assert sdY2[n] == sd and list(cdY2[n]) == cd, n
+            acc = sum(Fraction(a) * Fraction(b) for a, b in zip(va, vd))
+            assert dW[k, n] == float(acc * Fraction(float(sa)) * Fraction(float(sd))), (k, n)
+
+
 # ---------------------------------------------------------------------------
 # A hand-worked example (values derived by hand from the definitions)
 # ---------------------------------------------------------------------------
