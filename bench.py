@@ -8,10 +8,15 @@ loop issues the same work as the separate public calls with HIP events between
 them on the stream the kernels run on, for the per-stage breakdown and the
 per-kernel rooflines.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--pass forward|dgrad|wgrad]
 
 Prints one JSON line. Inputs are seeded synthetic matrices (workloads module),
 already resident in HBM when the timed region starts.
+
+--pass dgrad / wgrad time the backward GEMMs of the same layer instead, each
+step being its three public calls: dX = Q(dY) Q(W)^T (quantize_act on dY and on
+W rows, then gemm) or dW = Q(A)^T Q(dY) (quantize_weight on A and on dY, then
+gemm with K' = M).
 """
 from __future__ import annotations
 
@@ -49,6 +54,8 @@ def parse():
                    help="rows of A in the CPU-oracle sample (0 = the whole workload)")
     p.add_argument("--copy-calib", action="store_true",
                    help="also run a plain 1 GiB device copy (for PMC byte calibration)")
+    p.add_argument("--pass", dest="which", default="forward",
+                   choices=("forward", "dgrad", "wgrad"))
     return p.parse_args()
 
 
@@ -123,6 +130,182 @@ class Step:
         assert s == 0, s
 
 
+class BackwardStep:
+    """The three public calls of one backward GEMM, marshalled once.
+
+    dgrad: dX (M x K) = Q(dY) Q(W)^T, dY and W quantized per row over N.
+    wgrad: dW (K x N) = Q(A)^T Q(dY), A and dY quantized per column over M."""
+
+    def __init__(self, ql, which, A, W, dY, stream):
+        import torch
+        lib = ql.lib()
+        self.lib, self.which = lib, which
+        M, K = A.shape
+        N = W.shape[1]
+        dt = ql.BF16 if A.dtype == torch.bfloat16 else ql.F32
+        dev = A.device
+        P = ctypes.c_void_p
+        self.keep = [A, W, dY]
+        self.dt, self.stream = dt, P(stream.cuda_stream)
+        if which == "dgrad":
+            # operands: dY rows (M x N) and W rows (K x N), both over N
+            self.shape = (M, K, N)            # output rows, output cols, reduction
+            ops = [(dY, M, N), (W, K, N)]
+        else:
+            # operands: columns of A (M x K) and of dY (M x N), both over M
+            self.shape = (K, N, M)
+            ops = [(A, M, K), (dY, M, N)]
+        Mo, No, Ko = self.shape
+        ldq = ql.packed_ld(Ko)
+        self.ops = []
+        for X, r, c in ops:
+            if which == "dgrad":
+                q = torch.empty((r, ldq), dtype=torch.uint8, device=dev)
+                sc = torch.empty((r,), dtype=torch.float32, device=dev)
+                self.ops.append((P(X.data_ptr()), r, c, X.stride(0), q, sc, None))
+            else:
+                q = torch.empty((c, ldq), dtype=torch.uint8, device=dev)
+                sc = torch.empty((c,), dtype=torch.float32, device=dev)
+                wsb = max(int(lib.fp4lin_weight_workspace_bytes(r, c)), 16)
+                ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+                self.ops.append((P(X.data_ptr()), r, c, X.stride(0), q, sc, ws))
+        self.out = torch.empty((Mo, No), dtype=torch.float32, device=dev)
+
+    def quant(self, i):
+        X, r, c, ld, q, sc, ws = self.ops[i]
+        P = ctypes.c_void_p
+        if self.which == "dgrad":
+            st = self.lib.fp4lin_quantize_act(X, self.dt, r, c, ld, None, P(q.data_ptr()),
+                                              P(sc.data_ptr()), self.stream)
+        else:
+            st = self.lib.fp4lin_quantize_weight(X, self.dt, r, c, ld, P(q.data_ptr()),
+                                                 P(sc.data_ptr()), P(ws.data_ptr()), ws.numel(),
+                                                 self.stream)
+        assert st == 0, st
+
+    def gemm(self):
+        P = ctypes.c_void_p
+        (_, _, _, _, qa, sa, _), (_, _, _, _, qb, sb, _) = self.ops
+        Mo, No, Ko = self.shape
+        st = self.lib.fp4lin_gemm(P(qa.data_ptr()), P(sa.data_ptr()), P(qb.data_ptr()),
+                                  P(sb.data_ptr()), Mo, No, Ko, None, None, self.dt, 0,
+                                  P(self.out.data_ptr()), No, self.stream)
+        assert st == 0, st
+
+    def step(self):
+        self.quant(0)
+        self.quant(1)
+        self.gemm()
+
+
+def run_backward(args):
+    """One JSON line for --pass dgrad / wgrad."""
+    import torch
+    import quantized_linear_layer_amd as ql
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    L = wl.make_layer(args.workload, seed=args.seed)
+    dYh = wl.make_grad_output(L.M, L.N, seed=args.seed)
+    A, W, dY = upload(L.A, dev), upload(L.W, dev), upload(dYh, dev)
+    stream = torch.cuda.current_stream()
+    st = BackwardStep(ql, args.which, A, W, dY, stream)
+    Mo, No, Ko = st.shape
+    flops = 2.0 * Mo * No * Ko
+    for _ in range(max(args.warmup, 1)):
+        st.step()
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    f0.record(stream)
+    for _ in range(args.steps):
+        st.step()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    event_ms = f0.elapsed_time(f1) / args.steps
+    names = ("quant_0", "quant_1", "gemm")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        st.quant(0); e[1].record(stream)
+        st.quant(1); e[2].record(stream)
+        st.gemm(); e[3].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(names)}
+    gemm_tf = flops / (stage_ms["gemm"] * 1e-3) / 1e12
+    e = 2 if L.A.dtype == wl.BF16 else 4
+    ldq = ql.packed_ld(Ko)
+    # algorithmic bytes of the quantizers: operand read once, codes and scales written
+    qbytes = [e * r * c + (r if args.which == "dgrad" else c) * (ldq + 4)
+              for (_, r, c, _, _, _, _) in st.ops]
+    kernels = {"quant_0": {"ms": round(stage_ms["quant_0"], 5), "bytes": int(qbytes[0]),
+                           "GB/s": round(qbytes[0] / (stage_ms["quant_0"] * 1e-3) / 1e9, 1),
+                           "bound": "hbm"},
+               "quant_1": {"ms": round(stage_ms["quant_1"], 5), "bytes": int(qbytes[1]),
+                           "GB/s": round(qbytes[1] / (stage_ms["quant_1"] * 1e-3) / 1e9, 1),
+                           "bound": "hbm"},
+               "gemm": {"ms": round(stage_ms["gemm"], 5), "TFLOP/s": round(gemm_tf, 1),
+                        "mfma_frac": round(gemm_tf / FP4_PEAK_TFLOPS, 4), "bound": "mfma"}}
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_gemm_{args.workload}_{args.which}.json")
+    if os.path.exists(tfile):
+        tr = json.load(open(tfile))
+        if tr.get("source_sha256") == file_sha(os.path.join(ROOT, tr["source"])):
+            traffic = tr.get("bytes_per_launch")
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    what = {"dgrad": "dX = Q(dY) Q(W)^T", "wgrad": "dW = Q(A)^T Q(dY)"}[args.which]
+    out = {
+        "metric": f"FP4 linear {args.which} effective TFLOP/s ({what}, 1 GPU)",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4", "data": "synthetic",
+        "config": {"workload": f"{args.workload}_{args.which}", "M": L.M, "K": L.K, "N": L.N,
+                   "out_rows": Mo, "out_cols": No, "reduction": Ko, "input_dtype": L.A.dtype,
+                   "output_dtype": "f32", "seed": args.seed},
+        "pct_fp4_peak": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
+        "event_ms": round(event_ms, 5),
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "roofline": {"bound": "mfma", "kernel": "fp4_gemm_kernel", "achieved": round(gemm_tf, 2),
+                     "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tf / FP4_PEAK_TFLOPS, 4), "traffic": traffic},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(args.which, L, dYh, args.cpu_rows or 64)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_backward(which, L, dY, rows):
+    """The oracle's dgrad / wgrad on a sample of output rows (the quantization
+    of both whole operands included), timed on the host cores."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas_threads = 1
+    nrows = L.M if which == "dgrad" else L.K
+    sample = np.arange(min(rows, nrows))
+    t0 = time.perf_counter()
+    if which == "dgrad":
+        O.dgrad(dY.f32, L.W.f32, rows=sample)
+        red, cols = L.N, L.K
+    else:
+        O.wgrad(L.A.f32, dY.f32, rows=sample)
+        red, cols = L.M, L.N
+    t = time.perf_counter() - t0
+    flops = 2.0 * sample.size * cols * red
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{sample.size} of {nrows} output rows of the {which} GEMM (both operands "
+                      f"quantized whole, then the float64 integer product of the sampled rows) "
+                      f"took {t:.2f} s; host affinity {len(os.sched_getaffinity(0))} cpus, "
+                      f"BLAS threads {blas_threads}"}
+
+
 STAGES = ("select", "quant_a", "quant_w", "gemm", "sparse")
 
 
@@ -158,6 +341,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if args.which != "forward":
+        run_backward(args)
+        return
     import torch
     import quantized_linear_layer_amd as ql
     import workloads as wl

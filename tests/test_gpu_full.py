@@ -2,9 +2,9 @@
 configuration the benchmark times (one fp4lin_forward per layer).
 
 Bit-exact over the whole arrays: tau, the COO of dA (row, col, val, row_ptr),
-the packed codes and scales of A and W. Y (and dX for the dgrad GEMM) is
-compared with the oracle on sampled rows (first, last and a seeded spread),
-relative Frobenius error <= 1e-5.
+the packed codes and scales of A and W. Y (and dX and dW for the dgrad and
+wgrad GEMMs) is compared with the oracle on sampled rows (first, last and a
+seeded spread), relative Frobenius error <= 1e-5.
 """
 import numpy as np
 import pytest
@@ -113,4 +113,30 @@ def test_full_llama13b_qkv_dgrad(ql):
     got = host(dX[torch.from_numpy(rows).to(dX.device)])
     err = O.rel_fro(got, want_dX)
     log(f"[full] dgrad: dX rel_fro on {rows.size} rows {err:.3e}")
+    assert err <= Y_TOL, err
+
+
+def test_full_llama13b_qkv_wgrad(ql):
+    """dW = Q(A)^T Q(dY) through the public calls: quantize_weight on A and on
+    dY (both per column over M), then fp4lin_gemm with K' = M."""
+    import torch
+    L = wl.make_layer("llama13b_qkv")
+    M, K, N = L.M, L.K, L.N
+    log(f"[full] wgrad: A {M}x{K}, dY {M}x{N}")
+    dY = wl.make_grad_output(M, N)
+    Ad, dYd = to_device(L.A), to_device(dY)
+    Aq2, s_a2 = ql.quantize_weight(Ad)
+    dYq2, s_dy2 = ql.quantize_weight(dYd)
+    dW = ql.gemm(Aq2, s_a2, dYq2, s_dy2, K, N, M)
+    torch.cuda.synchronize()
+    log("[full] wgrad: oracle")
+    rows = sample_rows(K, seed=2)
+    want_dW, (q_a2, want_sa2, _), (q_dy2, want_sdy2, _) = O.wgrad(L.A.f32, dY.f32, rows=rows)
+    assert_bits_equal(host(s_a2), want_sa2, "s_A columns")
+    assert_bits_equal(host(Aq2), q_a2, "Aq columns")
+    assert_bits_equal(host(s_dy2), want_sdy2, "s_dY columns")
+    assert_bits_equal(host(dYq2), q_dy2, "dYq columns")
+    got = host(dW[torch.from_numpy(rows).to(dW.device)])
+    err = O.rel_fro(got, want_dW)
+    log(f"[full] wgrad: dW rel_fro on {rows.size} rows {err:.3e}")
     assert err <= Y_TOL, err

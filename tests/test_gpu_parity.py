@@ -537,6 +537,30 @@ def test_forward_matches_stage_calls(ql):
     assert_bits_equal(v["sA"], host(sA), "sA")
 
 
+# ---------------------------------------------------------------------------
+# wgrad dW = Q(A)^T Q(dY) through the public calls (reading R10)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("M,K,N", [(1, 5, 3), (300, 70, 90), (129, 256, 40), (1000, 33, 520)])
+def test_wgrad_public_calls(ql, dtype, M, K, N):
+    log(f"wgrad {dtype} M={M} K={K} N={N}")
+    t = torch()
+    rng = np.random.default_rng(M + 5 * K + 11 * N)
+    A = wl.random_matrix(rng, M, K, dtype, dist="t3")
+    dY = wl.random_matrix(rng, M, N, dtype, scale=1e-3)
+    Aq2, s_a2 = ql.quantize_weight(to_device(A))
+    dYq2, s_dy2 = ql.quantize_weight(to_device(dY))
+    dW = ql.gemm(Aq2, s_a2, dYq2, s_dy2, K, N, M)
+    t.cuda.synchronize()
+    want, (q_a2, want_sa2, _), (q_dy2, want_sdy2, _) = O.wgrad(A.f32, dY.f32)
+    assert_bits_equal(host(s_a2), want_sa2, "s_A columns")
+    assert_bits_equal(host(Aq2), q_a2, "Aq columns")
+    assert_bits_equal(host(s_dy2), want_sdy2, "s_dY columns")
+    assert_bits_equal(host(dYq2), q_dy2, "dYq columns")
+    err = O.rel_fro(host(dW), want)
+    assert err <= Y_TOL, err
+
+
 def test_gemm_equals_gemm_then_sparse_add(ql):
     """fp4lin_gemm(dA) == fp4lin_gemm(NULL) followed by fp4lin_sparse_add (same bits)."""
     t = torch()
