@@ -327,8 +327,24 @@ def cpu_baseline(workload, seed, rows):
     Y, _ = O.forward(L.A.f32, L.W.f32, L.q)
     t = time.perf_counter() - t0
     flops = 2.0 * L.M * L.N * L.K
+    # the same oracle stages once more, one at a time
+    stages = {}
+
+    def timed(name, fn, *a):
+        t1 = time.perf_counter()
+        r = fn(*a)
+        stages[name] = round(time.perf_counter() - t1, 4)
+        return r
+    tau, _ = timed("rank_and_tau", O.select_threshold, L.A.f32, L.q)
+    _, delta = timed("clamp_and_delta", O.clamp_and_residual, L.A.f32, tau)
+    _, sA, cA = timed("quantize_a", O.quantize_act, L.A.f32, tau)
+    _, sW, cW = timed("quantize_w", O.quantize_weight, L.W.f32)
+    acc = timed("integer_gemm", O.integer_product, cA, cW)
+    timed("scale_epilogue", O.scaled_product, acc, sA, sW)
+    timed("sparse_term", O.sparse_times_dense, delta, L.W.f32)
+    del acc
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
-            "kind": "oracle",
+            "kind": "oracle", "stages_s": stages,
             "sample": f"{rows} of {full} rows of A with the full {L.K}x{L.N} W, q={L.q}: "
                       f"the whole oracle forward (tau, clamp + COO, quantize A and W, float64 "
                       f"integer GEMM, sparse term) took {t:.2f} s; host affinity "
@@ -378,6 +394,21 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     forward_event_ms = f0.elapsed_time(f1) / args.steps
+
+    # secondary: the forward with the caches behind L2 cold (512 MB written
+    # before each call, outside the events)
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(min(args.steps, 20)):
+        flush.zero_()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        st.forward_call()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    del flush
+    forward_cold_ms = float(np.median(cold))
 
     # breakdown: the same work as separate public calls, events between stages
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
@@ -486,6 +517,7 @@ def main():
         "pct_fp4_peak": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
         "pct_hbm_roofline": round(100.0 * (alg_bytes / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBS, 2),
         "forward_event_ms": round(forward_event_ms, 5),
+        "forward_cold_ms": round(forward_cold_ms, 5),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
         "stages_step_ms": round(stages_step_ms, 5),
         "roofline": roof,
