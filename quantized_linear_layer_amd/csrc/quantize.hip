@@ -4,8 +4,9 @@
 // ScaleShift paragraphs — scale each vector into the FP4 range, then round to
 // the nearest FP4 value).
 //
-// Rows:    one wave per row; the row (all of it, for K up to 8192 bfloat16
-//          or 4096 float32) is loaded into registers with every 16-byte load
+// Rows:    one wave per row; the row (all of it, for K up to 8192 bfloat16,
+//          16384 when the rows are 16-byte aligned, or 4096 float32) is loaded
+//          into registers with every 16-byte load
 //          issued before the first is used, reduced to the (clamped) row amax
 //          with wave shuffles, and encoded from the registers, 8 codes per
 //          32-bit store; the zero padding up to roundup(K,128) is written too.
@@ -226,8 +227,8 @@ hipError_t run_quantize_weight(const void* Wp, int64_t K, int64_t N, int64_t ldw
 }
 
 // bfloat16 rows that are 16-byte aligned with K % 8 == 0 and fit one slab
-// (K <= 512 * CH): the raw 16-byte words are kept as loaded and quantized by
-// quantize_bf16_row.
+// (K <= 512 * CH, CH up to 32): the raw 16-byte words are kept as loaded and
+// quantized by quantize_bf16_row.
 template <int CH>
 __global__ __launch_bounds__(kRowWaves * kWave) void quantize_rows_bf16_kernel(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
@@ -254,10 +255,17 @@ hipError_t run_quantize_rows(const void* Xp, int64_t M, int64_t K, int64_t ldx, 
                              uint8_t* Xq, int64_t ldq, float* sX, hipStream_t stream) {
   const typename In::T* X = static_cast<const typename In::T*>(Xp);
   const unsigned blocks = row_blocks(M);
-  // rows up to 512 * CH padded columns kept in registers (bfloat16: 8192, float32: 4096)
+  // rows up to 512 * CH padded columns kept in registers (bfloat16: 8192, or
+  // 16384 for aligned rows; float32: 4096)
   constexpr int kMaxCh = In::kBytes == 2 ? 16 : 8;
   const int ch = chunks_per_lane(ldq * 2, kMaxCh);
   if constexpr (In::kBytes == 2 && kFast) {
+    // rows of 8193 .. 16384 padded columns stay in registers too (32 chunks
+    // per lane, two waves per SIMD) rather than being read twice
+    if (ldq * 2 > int64_t(kWave) * 16 * 8 && ldq * 2 <= int64_t(kWave) * 32 * 8) {
+      quantize_rows_bf16_kernel<32><<<blocks, kRowWaves * kWave, 0, stream>>>(X, M, K, ldx, tau, Xq, ldq, sX);
+      return hipGetLastError();
+    }
     if (int64_t(ch) * kWave * 8 >= ldq * 2) {
       switch (ch) {
         case 1: quantize_rows_bf16_kernel<1><<<blocks, kRowWaves * kWave, 0, stream>>>(X, M, K, ldx, tau, Xq, ldq, sX); break;

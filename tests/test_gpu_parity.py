@@ -115,7 +115,10 @@ def check_quantize_act(ql, X: wl.Matrix, tau=None, ld=None):
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 @pytest.mark.parametrize("M,K", [(1, 1), (3, 7), (5, 127), (4, 128), (9, 129), (37, 1000),
-                                 (70, 2051)])
+                                 (70, 2051),
+                                 # past 8192 columns: aligned bf16 rows stay in registers
+                                 # up to 16384 (32 chunks per lane), others take two reads
+                                 (6, 8200), (5, 13824), (3, 16384), (4, 16392), (3, 9001)])
 def test_quantize_act_shapes(ql, dtype, M, K):
     log(f"quantize_act {dtype} {M}x{K}")
     rng = np.random.default_rng(M * 1000 + K)
