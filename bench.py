@@ -234,6 +234,8 @@ def run_backward(args):
     torch.cuda.synchronize()
     stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, n in enumerate(names)}
+    if args.copy_calib:
+        copy_calibration(dev)
     gemm_tf = flops / (stage_ms["gemm"] * 1e-3) / 1e12
     e = 2 if L.A.dtype == wl.BF16 else 4
     ldq = ql.packed_ld(Ko)
@@ -429,15 +431,7 @@ def main():
     stages_step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)]))
 
     if args.copy_calib:
-        # plain copies of known size for PMC byte calibration: 1 GiB read and
-        # 1 GiB written, by the runtime's blit kernel and by an elementwise kernel
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(dev)
 
     value = flops / (ms_per_step * 1e-3) / 1e12
     # Algorithmic work per launch of each stage (the minimum the operation
@@ -526,6 +520,19 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.seed, args.cpu_rows)
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration(dev):
+    """Plain copies of known size for PMC byte calibration: 1 GiB read and
+    1 GiB written, by the runtime's blit kernel and by an elementwise kernel."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def upload(m, dev):
