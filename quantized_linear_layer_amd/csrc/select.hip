@@ -438,8 +438,9 @@ __device__ inline uint32_t count_above(const Vec8<In> (&v)[CH], uint32_t tkey) {
 
 // Per-row count of |a| > tau into cnt[r], and the workgroup's total into
 // gsum[blockIdx.x]. kPick (bfloat16): tau's key comes from the fine histogram
-// and workgroup 0 records it in st and tau; otherwise it is read from st. The
-// first row's loads are issued before the key is known.
+// and workgroup 0 records it in st and tau; otherwise it is read from st.
+// (Looking the key up between the first row's loads and their use measured
+// slower: it costs registers.)
 template <class In, bool kFast, int CH, bool kPick>
 __global__ __launch_bounds__(kRowWaves * kWave) void count_rows_kernel(
     const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
