@@ -308,6 +308,58 @@ def test_select_bf16_uneven_row_blocks(ql):
         check_select(ql, wl.from_f32(y, wl.BF16), q)
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_select_dirty_workspace(ql, dtype):
+    """No select kernel may rely on memory left by an earlier call or on a
+    cleared workspace: a workspace and COO pre-filled with 0xFF bytes, reused
+    for a second call of another shape, must give the oracle's bits."""
+    t = torch()
+    rng = np.random.default_rng(12)
+    shapes = [(300, 700), (40, 1000)]
+    big = max(ql.select_workspace_bytes(M, K, 0 if dtype == wl.F32 else 1) for M, K in shapes)
+    ws = t.full((big,), 0xFF, dtype=t.uint8, device="cuda:0")
+    for M, K in shapes:
+        A = wl.random_matrix(rng, M, K, dtype, dist="t3")
+        Ad = to_device(A)
+        q = 0.99
+        k = ql.quantile_rank(M * K, q)
+        coo = ql.CooBuffers.empty(M, M * K - 1 - k, Ad.device)
+        for buf in (coo.row, coo.col, coo.row_ptr):
+            buf.fill_(-1)
+        coo.val.fill_(float("nan"))
+        tau = t.full((1,), float("nan"), dtype=t.float32, device=Ad.device)
+        ql.fp4lin_outlier_select(Ad, q, tau, coo, ws)
+        t.cuda.synchronize()
+        want_tau, _ = O.select_threshold(A.f32, q)
+        _, d = O.clamp_and_residual(A.f32, want_tau)
+        assert_bits_equal(host(tau)[0], want_tau, "tau")
+        assert_bits_equal(host(coo.row_ptr), d.row_ptr.astype(np.int32), "row_ptr")
+        nnz = d.nnz
+        assert_bits_equal(host(coo.col)[:nnz], d.col, "coo col")
+        assert_bits_equal(host(coo.val)[:nnz], d.val32, "coo val")
+
+
+def test_forward_dirty_workspace(ql):
+    """fp4lin_forward with its workspace pre-filled with 0xFF bytes, then reused
+    for a smaller layer, gives the same bits as with a fresh workspace."""
+    t = torch()
+    rng = np.random.default_rng(13)
+    layers = []
+    for M, K, N in [(200, 1024, 96), (70, 512, 40)]:
+        a = wl.draw_activation(rng, M, K, "t3", max(1, K // 200), 50.0)
+        w = wl.draw_weight(rng, K, N)
+        layers.append(wl.Layer("dirty", wl.from_f32(a, wl.BF16), wl.from_f32(w, wl.BF16), 0.99))
+    big = max(ql.workspace_bytes(L.M, L.K, L.N, 1, L.q) for L in layers)
+    ws = t.full((big,), 0xFF, dtype=t.uint8, device="cuda:0")
+    for L in layers:
+        A, W = to_device(L.A), to_device(L.W)
+        Y1 = ql.forward(A, W, L.q)
+        Y2 = t.full((L.M, L.N), float("nan"), dtype=t.float32, device=A.device)
+        ql.fp4lin_forward(A, W, L.q, Y2, ws)
+        t.cuda.synchronize()
+        assert np.array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
+
+
 def test_select_bf16_layer_slice(ql):
     L = wl.make_layer("llama7b_ffn_up", M=64)
     check_select(ql, L.A, L.q)
