@@ -231,9 +231,11 @@ fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtyp
  * fp4lin_quantize_act (with the selected tau), fp4lin_quantize_weight and
  * fp4lin_gemm (with dA) compute, in that order on `stream`, keeping every
  * intermediate in `ws` at the offsets fp4lin_forward_layout reports. For bf16
- * A with 16-byte aligned rows and K <= 8192, the outlier compaction and the
- * token-wise quantization of A run as one kernel over one read of A; every
- * intermediate and Y are bit-identical to those of the separate calls.
+ * A and W with 16-byte aligned rows and K <= 8192, the outlier compaction and
+ * the token-wise quantization of A run as one kernel over one read of A, and
+ * the passes over W that fp4lin_quantize_weight makes share launches with the
+ * select's kernels (K <= 4096) or follow them; every intermediate and Y are
+ * bit-identical to those of the separate calls.
  *   A, W     device inputs (same dtype dt), leading dimensions lda, ldw
  *   Y        device output, M x N floats, leading dimension ldy
  *   ws       device workspace of >= fp4lin_workspace_bytes(M, K, N, dt, q)

@@ -98,8 +98,9 @@ fp4lin_status fp4lin_forward_layout(int64_t M, int64_t K, int64_t N, fp4lin_dtyp
   o.sA = take(size_t(M) * 4);
   o.Wq = take(size_t(N) * ldq);
   o.sW = take(size_t(N) * 4);
-  const size_t sws = select_ws(M, dt), wws = weight_ws(N);
-  o.scratch = take(sws > wws ? sws : wws);
+  // the select's workspace, then the column maxima of W's quantization (the
+  // forward keeps both live at once)
+  o.scratch = take(select_ws(M, dt) + weight_ws(N));
   o.capacity = cap;
   o.total = off;
   *out = o;
@@ -243,6 +244,10 @@ fp4lin_status fp4lin_forward(const void* A, const void* W, fp4lin_dtype dt, int6
   if (ls != FP4LIN_OK) return ls;
   if (!aligned16(ws)) return FP4LIN_ERR_ALIGN;
   if (ws_bytes < o.total) return FP4LIN_ERR_WORKSPACE;
+  // the GEMM's own limits, checked before anything is enqueued
+  const int64_t ldq = fp4lin_packed_ld(K);
+  if ((M + 1) * ldq >= kMaxDim || (N + 1) * ldq >= kMaxDim || !weight_addressable(K, ldw, dt))
+    return FP4LIN_ERR_SHAPE;
   char* base = static_cast<char*>(ws);
   float* tau = reinterpret_cast<float*>(base + o.tau);
   fp4lin_coo coo;
@@ -257,18 +262,36 @@ fp4lin_status fp4lin_forward(const void* A, const void* W, fp4lin_dtype dt, int6
   float* sW = reinterpret_cast<float*>(base + o.sW);
   void* scratch = base + o.scratch;
   const size_t scratch_bytes = o.total - o.scratch;
-  // bfloat16 rows that fit one slab are quantized by the select's compaction,
-  // which reads A anyway
-  bool a_done = false;
-  fp4lin_status s = select_impl(A, dt, M, K, lda, q, tau, coo, scratch, scratch_bytes, stream, Aq,
-                                sA, &a_done);
-  if (s != FP4LIN_OK) return s;
-  if (!a_done) {
-    s = fp4lin_quantize_act(A, dt, M, K, lda, tau, Aq, sA, stream);
+  fp4lin_status s;
+  if (fp4lin::forward_front_supported(A, W, dt == FP4LIN_BF16, K, lda, ldw)) {
+    // bf16, aligned rows, K <= 8192: select, quantization of A (in the
+    // compaction) and of W (for K <= 4096 sharing launches with the select's
+    // row kernels; W's column maxima are cleared by the select's first pass)
+    uint32_t* colmax = reinterpret_cast<uint32_t*>(static_cast<char*>(scratch) + select_ws(M, dt));
+    bool w_done = false;
+    s = launch_status(fp4lin::launch_forward_front(
+        A, M, K, lda, fp4lin_quantile_rank(M * K, q), tau, coo.capacity, coo.row, coo.col,
+        coo.val, coo.row_ptr, scratch, Aq, ldq, sA, W, N, ldw, Wq, sW, colmax, &w_done, stream));
+    if (s != FP4LIN_OK) return s;
+    if (!w_done) {
+      s = launch_status(fp4lin::launch_quantize_weight_cleared(
+          static_cast<const uint16_t*>(W), K, N, ldw, Wq, ldq, sW, colmax, stream));
+      if (s != FP4LIN_OK) return s;
+    }
+  } else {
+    // bfloat16 rows that fit one slab are quantized by the select's
+    // compaction, which reads A anyway
+    bool a_done = false;
+    s = select_impl(A, dt, M, K, lda, q, tau, coo, scratch, scratch_bytes, stream, Aq, sA,
+                    &a_done);
+    if (s != FP4LIN_OK) return s;
+    if (!a_done) {
+      s = fp4lin_quantize_act(A, dt, M, K, lda, tau, Aq, sA, stream);
+      if (s != FP4LIN_OK) return s;
+    }
+    s = fp4lin_quantize_weight(W, dt, K, N, ldw, Wq, sW, scratch, scratch_bytes, stream);
     if (s != FP4LIN_OK) return s;
   }
-  s = fp4lin_quantize_weight(W, dt, K, N, ldw, Wq, sW, scratch, scratch_bytes, stream);
-  if (s != FP4LIN_OK) return s;
   return fp4lin_gemm(Aq, sA, Wq, sW, M, N, K, &coo, W, dt, ldw, Y, ldy, stream);
 }
 

@@ -10,6 +10,12 @@ namespace fp4lin {
 size_t select_workspace_bytes(bool bf16, int64_t M);
 size_t weight_workspace_bytes(int64_t N);
 
+// The two passes of launch_quantize_weight for bf16 W with 16-byte aligned rows,
+// with colmax (N words) already zero.
+hipError_t launch_quantize_weight_cleared(const uint16_t* W, int64_t K, int64_t N, int64_t ldw,
+                                          uint8_t* Wq, int64_t ldq, float* sW, uint32_t* colmax,
+                                          hipStream_t stream);
+
 // With quantized set, rows that allow it are also quantized token-wise (Xq
 // with row stride ldq, scales sX, clamped to tau) by the compaction, and
 // *quantized says whether that happened; with quantized null, Xq is ignored.
@@ -18,6 +24,22 @@ hipError_t launch_outlier_select(const void* A, bool bf16, int64_t M, int64_t K,
                                  int32_t* col, float* val, int32_t* row_ptr, void* ws,
                                  hipStream_t stream, uint8_t* Xq = nullptr, int64_t ldq = 0,
                                  float* sX = nullptr, bool* quantized = nullptr);
+
+// Whole-layer forward, front half (select, quantization of A and of W) for
+// bf16 A and W with 16-byte aligned rows, K % 8 == 0 and K up to 8192
+// (forward_front_supported): the select of launch_outlier_select with the
+// token-wise quantization of A in its compaction; colmax (N words of
+// workspace apart from ws) is cleared by the select's first pass. For K up to
+// 4096 the channel-wise quantization of W shares launches with the select's
+// row kernels and *w_done is set; otherwise the caller runs
+// launch_quantize_weight_cleared.
+bool forward_front_supported(const void* A, const void* W, bool bf16, int64_t K, int64_t lda,
+                             int64_t ldw);
+hipError_t launch_forward_front(const void* A, int64_t M, int64_t K, int64_t lda, int64_t k,
+                                float* tau, int64_t capacity, int32_t* row, int32_t* col,
+                                float* val, int32_t* row_ptr, void* ws, uint8_t* Aq, int64_t ldq,
+                                float* sA, const void* W, int64_t N, int64_t ldw, uint8_t* Wq,
+                                float* sW, uint32_t* colmax, bool* w_done, hipStream_t stream);
 
 hipError_t launch_quantize_rows(const void* X, bool bf16, int64_t M, int64_t K, int64_t ldx,
                                 const float* tau, uint8_t* Xq, int64_t ldq, float* sX,

@@ -16,6 +16,7 @@
 //          floats order like their bits); pass 2 gives each thread 8 columns x
 //          8 consecutive rows, so the 8 codes of one column along K are one
 //          32-bit word of the column's packed (N-major) row, stored directly.
+#include "colquant.hpp"
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -101,114 +102,29 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
     p[i] = v;
 }
 
-constexpr int kColStrip = 512;    // columns per workgroup (8 per lane)
-constexpr int kColRows = 64;      // rows per workgroup split
-constexpr int kColUnroll = 8;     // loads in flight per thread
-
 template <class In, bool kAligned>
 __global__ __launch_bounds__(256) void colmax_kernel(const typename In::T* __restrict__ W,
                                                      int64_t K, int64_t N, int64_t ldw,
                                                      uint32_t* __restrict__ colmax) {
-  __shared__ uint32_t red[4][kColStrip];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int64_t c = int64_t(blockIdx.x) * kColStrip + lane * 8;
-  const int64_t k0 = int64_t(blockIdx.y) * kColRows;
-  const int64_t k1 = (k0 + kColRows < K) ? k0 + kColRows : K;
-  const int64_t valid = N - c;
-  float m[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m[i] = 0.0f;
-  if (valid > 0) {
-    // kColUnroll rows in flight per thread; rows past k1 read as zero
-    for (int64_t kb = k0 + wave; kb < k1; kb += 4 * kColUnroll) {
-      Vec8<In> v[kColUnroll];
-#pragma unroll
-      for (int u = 0; u < kColUnroll; ++u) {
-        const int64_t k = kb + 4 * u;
-        if (k < k1) {
-          load8<In, kAligned>(W + k * ldw + c, valid, v[u]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[u].v[i] = typename In::T(0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kColUnroll; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(In::widen(v[u].v[i])));
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = __float_as_uint(m[i]);
-  __syncthreads();
-  for (int j = threadIdx.x; j < kColStrip; j += blockDim.x) {
-    uint32_t x = red[0][j];
-    x = x > red[1][j] ? x : red[1][j];
-    x = x > red[2][j] ? x : red[2][j];
-    x = x > red[3][j] ? x : red[3][j];
-    const int64_t col = int64_t(blockIdx.x) * kColStrip + j;
-    if (col < N) atomicMax(&colmax[col], x);
-  }
+  colmax_body<In, kAligned>(blockIdx.x, blockIdx.y, W, K, N, ldw, colmax);
 }
-
-// Pass 2 tile: 128 codes along K x 128 columns. Thread (kg, g) = (t % 16,
-// t / 16) owns rows k0 + 8kg .. +7 and columns n0 + 8g .. +7, so for each of its
-// columns the 8 codes along K form one 32-bit word of that column's packed row
-// (low nibble first), stored directly: a wave's store covers 64 contiguous
-// bytes of each of 4 packed rows, and its loads 64 contiguous bytes of each of
-// 16 rows of W.
-constexpr int kTK = 128;
-constexpr int kTN = 128;
 
 template <class In, bool kAligned>
 __global__ __launch_bounds__(256) void quantize_cols_kernel(
     const typename In::T* __restrict__ W, int64_t K, int64_t N, int64_t ldw,
     const uint32_t* __restrict__ colmax, uint8_t* __restrict__ Wq, int64_t ldq,
     float* __restrict__ sW) {
-  __shared__ float inv_s[kTN];
-  const int t = threadIdx.x;
-  const int64_t n0 = int64_t(blockIdx.x) * kTN;
-  const int64_t k0 = int64_t(blockIdx.y) * kTK;
-  if (t < kTN) {
-    const int64_t n = n0 + t;
-    float s = 0.0f, inv = 0.0f;
-    if (n < N) {
-      vector_scale(__uint_as_float(colmax[n]), s, inv);
-      if (blockIdx.y == 0) sW[n] = s;
-    }
-    inv_s[t] = inv;
-  }
-  const int kg = t & 15, g = t >> 4;
-  const int64_t c = n0 + g * 8;
-  const int64_t valid = N - c;
-  const int64_t kr = k0 + kg * 8;
-  Vec8<In> v[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (kr + u < K && valid > 0) {
-      load8<In, kAligned>(W + (kr + u) * ldw + c, valid, v[u]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[u].v[j] = typename In::T(0);
-    }
-  }
-  __syncthreads();
-  if (valid <= 0) return;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= valid) break;
-    const float inv = inv_s[g * 8 + j];
-    uint32_t word = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      // rows past K were loaded as zero and encode to the zero padding
-      const uint32_t code =
-          e2m1_magnitude(fabsf(In::widen(v[u].v[j])), inv) | (In::sign_bit(v[u].v[j]) << 3);
-      word |= code << (4 * u);
-    }
-    *reinterpret_cast<uint32_t*>(Wq + (c + j) * ldq + kr / 2) = word;
-  }
+  quantize_cols_body<In, kAligned>(blockIdx.x, blockIdx.y, W, K, N, ldw, colmax, Wq, ldq, sW);
+}
+
+// the column maxima (into colmax, which starts at zero) and the codes
+template <class In, bool kAligned>
+void launch_col_passes(const typename In::T* W, int64_t K, int64_t N, int64_t ldw, uint8_t* Wq,
+                       int64_t ldq, float* sW, uint32_t* colmax, hipStream_t stream) {
+  dim3 g1(unsigned((N + kColStrip - 1) / kColStrip), unsigned((K + kColRows - 1) / kColRows));
+  colmax_kernel<In, kAligned><<<g1, 256, 0, stream>>>(W, K, N, ldw, colmax);
+  dim3 g2(unsigned((N + kTN - 1) / kTN), unsigned((ldq * 2) / kTK));
+  quantize_cols_kernel<In, kAligned><<<g2, 256, 0, stream>>>(W, K, N, ldw, colmax, Wq, ldq, sW);
 }
 
 template <class In, bool kAligned>
@@ -219,10 +135,7 @@ hipError_t run_quantize_weight(const void* Wp, int64_t K, int64_t N, int64_t ldw
   uint32_t* colmax = static_cast<uint32_t*>(ws);
   fill_u32_kernel<<<dim3(unsigned((N + 255) / 256 < 1024 ? (N + 255) / 256 : 1024)), 256, 0,
                     stream>>>(colmax, N, 0u);
-  dim3 g1(unsigned((N + kColStrip - 1) / kColStrip), unsigned((K + kColRows - 1) / kColRows));
-  colmax_kernel<In, kAligned><<<g1, 256, 0, stream>>>(W, K, N, ldw, colmax);
-  dim3 g2(unsigned((N + kTN - 1) / kTN), unsigned((ldq * 2) / kTK));
-  quantize_cols_kernel<In, kAligned><<<g2, 256, 0, stream>>>(W, K, N, ldw, colmax, Wq, ldq, sW);
+  launch_col_passes<In, kAligned>(W, K, N, ldw, Wq, ldq, sW, colmax, stream);
   return hipGetLastError();
 }
 
@@ -329,6 +242,13 @@ hipError_t launch_quantize_weight(const void* W, bool bf16, int64_t K, int64_t N
                    : run_quantize_weight<BF16In, false>(W, K, N, ldw, Wq, ldq, sW, ws, stream);
   return aligned ? run_quantize_weight<F32In, true>(W, K, N, ldw, Wq, ldq, sW, ws, stream)
                  : run_quantize_weight<F32In, false>(W, K, N, ldw, Wq, ldq, sW, ws, stream);
+}
+
+hipError_t launch_quantize_weight_cleared(const uint16_t* W, int64_t K, int64_t N, int64_t ldw,
+                                          uint8_t* Wq, int64_t ldq, float* sW, uint32_t* colmax,
+                                          hipStream_t stream) {
+  launch_col_passes<BF16In, true>(W, K, N, ldw, Wq, ldq, sW, colmax, stream);
+  return hipGetLastError();
 }
 
 }  // namespace fp4lin

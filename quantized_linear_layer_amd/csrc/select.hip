@@ -35,6 +35,7 @@
 // its own, which gives row_ptr and the row-major positions without a separate
 // scan. In the whole-layer forward, bfloat16 rows that fit one slab are also
 // quantized token-wise by the compaction kernel, from the same registers.
+#include "colquant.hpp"
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -255,7 +256,8 @@ template <bool kFast, bool kFine, int CH>
 __global__ __launch_bounds__(kH16Threads) void select_hist16_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rows_per_wg,
     uint32_t* __restrict__ part, int nparts, uint32_t k, SelState* __restrict__ st,
-    uint32_t* __restrict__ fine, uint32_t* __restrict__ win, uint32_t* __restrict__ fwin) {
+    uint32_t* __restrict__ fine, uint32_t* __restrict__ win, uint32_t* __restrict__ fwin,
+    uint32_t* __restrict__ clear, int64_t nclear) {
   constexpr int kBins = kFine ? kFineBins : kKeyBins16;
   __shared__ uint32_t h[kBins];
   const int t = threadIdx.x;
@@ -294,6 +296,10 @@ __global__ __launch_bounds__(kH16Threads) void select_hist16_kernel(
   } else {
     if (blockIdx.x == 0)
       for (int i = t; i < kFineBins; i += kH16Threads) fine[i] = 0u;
+    // forward: the column maxima of W's quantization start from zero
+    for (int64_t i = int64_t(blockIdx.x) * kH16Threads + t; i < nclear;
+         i += int64_t(gridDim.x) * kH16Threads)
+      clear[i] = 0u;
   }
   __syncthreads();
   const int lane = t & (kWave - 1);
@@ -442,21 +448,21 @@ __device__ inline uint32_t count_above(const Vec8<In> (&v)[CH], uint32_t tkey) {
 // (Looking the key up between the first row's loads and their use measured
 // slower: it costs registers.)
 template <class In, bool kFast, int CH, bool kPick>
-__global__ __launch_bounds__(kRowWaves * kWave) void count_rows_kernel(
-    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
-    SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
+__device__ __attribute__((always_inline)) inline void count_rows_body(
+    int64_t bid, const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda,
+    int64_t rpw, SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
     uint32_t* __restrict__ cnt, uint32_t* __restrict__ gsum) {
   __shared__ uint32_t wsum[kRowWaves];
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);  // wave-uniform
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t R = int64_t(kRowWaves) * rpw;
-  const int64_t r0 = int64_t(blockIdx.x) * R;
+  const int64_t r0 = bid * R;
   const int64_t r1 = (r0 + R < M) ? r0 + R : M;
   const int64_t slab = int64_t(kWave) * CH * 8;
   uint32_t tkey;
   if constexpr (kPick) {
     tkey = fine_pick(st, fine);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (bid == 0 && threadIdx.x == 0) {
       st->tau_key = tkey;
       *tau = In::key_to_float(tkey);
     }
@@ -482,8 +488,16 @@ __global__ __launch_bounds__(kRowWaves * kWave) void count_rows_kernel(
     uint32_t s = 0;
 #pragma unroll
     for (int i = 0; i < kRowWaves; ++i) s += wsum[i];
-    gsum[blockIdx.x] = s;
+    gsum[bid] = s;
   }
+}
+
+template <class In, bool kFast, int CH, bool kPick>
+__global__ __launch_bounds__(kRowWaves * kWave) void count_rows_kernel(
+    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+    SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
+    uint32_t* __restrict__ cnt, uint32_t* __restrict__ gsum) {
+  count_rows_body<In, kFast, CH, kPick>(blockIdx.x, A, M, K, lda, rpw, st, fine, tau, cnt, gsum);
 }
 
 // Write every |a| > tau entry of a row, ascending column, from position pos.
@@ -638,8 +652,8 @@ __device__ inline void compact_words(const uint4 (&wv)[CH], int64_t r, uint32_t 
 // token-wise quantization of the row clamped to tau (quantize_bf16_row) from
 // one read of A.
 template <int CH>
-__global__ __launch_bounds__(kRowWaves * kWave) void compact_quantize_rows_kernel(
-    const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+__device__ __attribute__((always_inline)) inline void compact_quantize_rows_body(
+    int64_t bid, const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
     const SelState* __restrict__ st, const float* __restrict__ tau_p,
     const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
@@ -648,17 +662,17 @@ __global__ __launch_bounds__(kRowWaves * kWave) void compact_quantize_rows_kerne
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);  // wave-uniform
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t R = int64_t(kRowWaves) * rpw;
-  const int64_t r0 = int64_t(blockIdx.x) * R;
+  const int64_t r0 = bid * R;
   const int64_t r1 = (r0 + R < M) ? r0 + R : M;
   const uint32_t tkey = st->tau_key;
   const float tau = *tau_p;
   const uint32_t cap = uint32_t(capacity < INT32_MAX ? capacity : INT32_MAX);
-  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
+  if (bid == 0 && threadIdx.x == 0) row_ptr[0] = 0;
   // entries of the workgroups before this one
   uint32_t base = 0;
   {
     uint32_t s = 0;
-    for (int64_t g = threadIdx.x; g < int64_t(blockIdx.x); g += kRowWaves * kWave) s += gsum[g];
+    for (int64_t g = threadIdx.x; g < bid; g += kRowWaves * kWave) s += gsum[g];
     s = wave_sum_u32(s);
     if (lane == 0) wsum[w] = s;
     __syncthreads();
@@ -691,6 +705,71 @@ __global__ __launch_bounds__(kRowWaves * kWave) void compact_quantize_rows_kerne
     }
     base += all;
   }
+}
+
+template <int CH>
+__global__ __launch_bounds__(kRowWaves * kWave) void compact_quantize_rows_kernel(
+    const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+    const SelState* __restrict__ st, const float* __restrict__ tau_p,
+    const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
+    int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
+    float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX) {
+  compact_quantize_rows_body<CH>(blockIdx.x, A, M, K, lda, rpw, st, tau_p, cnt, gsum, capacity,
+                                 row_ptr, out_row, out_col, out_val, Xq, ldq, sX);
+}
+
+// ---------------------------------------------------------------------------
+// Whole-layer forward, bfloat16 with aligned rows: the quantization of W has
+// no dependence on the select, so its two passes share launches with the
+// select's row kernels (the column maxima with the row count, the codes with
+// the compaction), and its cleared maxima come from the coarse pass.
+// ---------------------------------------------------------------------------
+// Launch index b of a pair launch of na + nb workgroups belongs to the first
+// body when floor((b+1)*na/(na+nb)) > floor(b*na/(na+nb)); the two kinds are
+// interleaved in proportion, and each gets the indexes 0 .. n-1 once.
+__device__ inline bool pair_first(int64_t b, int64_t na, int64_t nb, int64_t& idx) {
+  const int64_t t = na + nb;
+  const int64_t lo = b * na / t, hi = (b + 1) * na / t;
+  idx = hi > lo ? lo : b - lo;
+  return hi > lo;
+}
+
+struct ColQuantArgs {
+  const uint16_t* W;
+  int64_t K, N, ldw;
+  uint32_t* colmax;
+  uint8_t* Wq;
+  int64_t ldq;
+  float* sW;
+};
+
+template <int CH>
+__global__ __launch_bounds__(kRowWaves * kWave) void count_colmax_kernel(
+    const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw, SelState* st,
+    const uint32_t* __restrict__ fine, float* __restrict__ tau, uint32_t* __restrict__ cnt,
+    uint32_t* __restrict__ gsum, int64_t na, ColQuantArgs cq, int64_t gx, int64_t nb) {
+  int64_t i;
+  if (pair_first(blockIdx.x, na, nb, i))
+    count_rows_body<BF16In, true, CH, true>(i, A, M, K, lda, rpw, st, fine, tau, cnt, gsum);
+  else
+    colmax_body<BF16In, true>(i % gx, i / gx, cq.W, cq.K, cq.N, cq.ldw, cq.colmax);
+}
+
+template <int CH>
+__global__ __launch_bounds__(kRowWaves * kWave) void compact_qcols_kernel(
+    const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+    const SelState* __restrict__ st, const float* __restrict__ tau_p,
+    const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
+    int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
+    float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX,
+    int64_t na, ColQuantArgs cq, int64_t gx, int64_t nb) {
+  int64_t i;
+  if (pair_first(blockIdx.x, na, nb, i))
+    compact_quantize_rows_body<CH>(i, A, M, K, lda, rpw, st, tau_p, cnt, gsum, capacity, row_ptr,
+                                   out_row, out_col, out_val, Xq, ldq, sX);
+  else
+    quantize_cols_body<BF16In, true>(i % gx, i / gx, cq.W, cq.K, cq.N, cq.ldw, cq.colmax, cq.Wq,
+                                     cq.ldq, cq.sW);
 }
 
 // Words after the 256-byte state: bfloat16 has the coarse partial rows, the
@@ -791,6 +870,53 @@ hipError_t rows_dispatch(const typename In::T* A, int64_t M, int64_t K, int64_t 
   }
 }
 
+// The bfloat16 select's workspace: state, then the coarse partial rows, the
+// fine histogram, the saved windows, the row-group totals and the row counts.
+struct H16Work {
+  SelState* st;
+  uint32_t *part, *fine, *win, *fwin, *gsum, *cnt;
+  explicit H16Work(void* ws) {
+    st = static_cast<SelState*>(ws);
+    part = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 256);
+    fine = part + size_t(kMaxH16Groups) * kCoarseBins;
+    win = fine + kFineBins;
+    fwin = win + kMaxH16Groups;
+    gsum = part + hist_words<BF16In>();
+    cnt = gsum + kMaxRowGroups;
+  }
+};
+
+// The two bfloat16 histogram passes (the coarse one also clears nclear words
+// at clear).
+template <bool kFast>
+hipError_t launch_hist16(const uint16_t* A, int64_t M, int64_t K, int64_t lda, int64_t k,
+                         const H16Work& w, uint32_t* clear, int64_t nclear, hipStream_t stream) {
+  // one workgroup per CU (MI355X: 256), at least one row per wave
+  int64_t wgs = (M + kH16Waves - 1) / kH16Waves;
+  wgs = wgs < kMaxH16Groups ? wgs : kMaxH16Groups;
+  const int64_t per = (M + wgs - 1) / wgs;
+  const dim3 g(static_cast<unsigned>(wgs));
+  // k < M*K < 2^32
+  const uint32_t k32 = uint32_t(k);
+  switch (chunks_per_lane(K, 16)) {
+#define FP4LIN_H16(CH)                                                                           \
+  case CH:                                                                                       \
+    select_hist16_kernel<kFast, false, CH><<<g, kH16Threads, 0, stream>>>(                       \
+        A, M, K, lda, per, w.part, 0, k32, w.st, w.fine, w.win, w.fwin, clear, nclear);          \
+    select_hist16_kernel<kFast, true, CH><<<g, kH16Threads, 0, stream>>>(                        \
+        A, M, K, lda, per, w.part, int(wgs), k32, w.st, w.fine, w.win, w.fwin, nullptr, 0);      \
+    return hipSuccess;
+    FP4LIN_H16(1)
+    FP4LIN_H16(2)
+    FP4LIN_H16(4)
+    FP4LIN_H16(8)
+    FP4LIN_H16(16)
+#undef FP4LIN_H16
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
 template <class In, bool kFast>
 hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t k, float* tau,
                       int64_t capacity, int32_t* row, int32_t* col, float* val,
@@ -803,35 +929,10 @@ hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t
   uint32_t* cnt = gsum + kMaxRowGroups;
   hipError_t e = hipSuccess;
   if constexpr (In::kBytes == 2) {
-    // one workgroup per CU (MI355X: 256), at least one row per wave
-    int64_t wgs = (M + kH16Waves - 1) / kH16Waves;
-    wgs = wgs < kMaxH16Groups ? wgs : kMaxH16Groups;
-    const int64_t per = (M + wgs - 1) / wgs;
-    uint32_t* part = hist;
-    uint32_t* fine = part + size_t(kMaxH16Groups) * kCoarseBins;
-    uint32_t* win = fine + kFineBins;
-    uint32_t* fwin = win + kMaxH16Groups;
-    const dim3 g(static_cast<unsigned>(wgs));
-    // k < M*K < 2^32
-    const uint32_t k32 = uint32_t(k);
-    switch (chunks_per_lane(K, 16)) {
-#define FP4LIN_H16(CH)                                                                           \
-  case CH:                                                                                       \
-    select_hist16_kernel<kFast, false, CH><<<g, kH16Threads, 0, stream>>>(                       \
-        A, M, K, lda, per, part, 0, k32, st, fine, win, fwin);                                   \
-    select_hist16_kernel<kFast, true, CH><<<g, kH16Threads, 0, stream>>>(                        \
-        A, M, K, lda, per, part, int(wgs), k32, st, fine, win, fwin);                            \
-    break;
-      FP4LIN_H16(1)
-      FP4LIN_H16(2)
-      FP4LIN_H16(4)
-      FP4LIN_H16(8)
-      FP4LIN_H16(16)
-#undef FP4LIN_H16
-      default:
-        return hipErrorInvalidValue;
-    }
-    e = rows_dispatch<In, kFast, true>(A, M, K, lda, st, fine, tau, gsum, cnt, capacity, row,
+    const H16Work w(ws);
+    e = launch_hist16<kFast>(A, M, K, lda, k, w, nullptr, 0, stream);
+    if (e != hipSuccess) return e;
+    e = rows_dispatch<In, kFast, true>(A, M, K, lda, st, w.fine, tau, gsum, cnt, capacity, row,
                                        col, val, row_ptr, rq, stream);
   } else {
     select_init_kernel<<<1, 256, 0, stream>>>(st, hist, int64_t(hist_words<In>()), k);
@@ -884,6 +985,86 @@ hipError_t launch_outlier_select(const void* A, bool bf16, int64_t M, int64_t K,
              : run_select<F32In, false>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, rq, stream);
   if (quantized != nullptr) *quantized = done && e == hipSuccess;
   return e;
+}
+
+namespace {
+
+template <int CH>
+hipError_t forward_front(const uint16_t* A, int64_t M, int64_t K, int64_t lda, int64_t k,
+                         float* tau, int64_t capacity, int32_t* row, int32_t* col, float* val,
+                         int32_t* row_ptr, void* ws, uint8_t* Aq, int64_t ldq, float* sA,
+                         const ColQuantArgs& cq, bool* w_done, hipStream_t stream) {
+  const H16Work w(ws);
+  hipError_t e = launch_hist16<true>(A, M, K, lda, k, w, cq.colmax, cq.N, stream);
+  if (e != hipSuccess) return e;
+  const int64_t rpw = rows_per_wave(M);
+  const int64_t na = row_groups(M);
+  if constexpr (CH > 8) {
+    // the 16-chunk row kernels need up to 162 VGPRs (three waves per SIMD),
+    // which would hold the paired column passes to the same occupancy (measured
+    // slower): the row kernels run alone and W is quantized afterwards
+    count_rows_kernel<BF16In, true, CH, true><<<dim3(unsigned(na)), kRowWaves * kWave, 0,
+                                                stream>>>(A, M, K, lda, rpw, w.st, w.fine, tau,
+                                                          w.cnt, w.gsum);
+    compact_quantize_rows_kernel<CH><<<dim3(unsigned(na)), kRowWaves * kWave, 0, stream>>>(
+        A, M, K, lda, rpw, w.st, tau, w.cnt, w.gsum, capacity, row_ptr, row, col, val, Aq, ldq,
+        sA);
+    *w_done = false;
+    return hipGetLastError();
+  } else {
+    // column maxima: 512-column strips x 64-row splits
+    const int64_t gx1 = (cq.N + kColStrip - 1) / kColStrip;
+    const int64_t nb1 = gx1 * ((cq.K + kColRows - 1) / kColRows);
+    count_colmax_kernel<CH><<<dim3(unsigned(na + nb1)), kRowWaves * kWave, 0, stream>>>(
+        A, M, K, lda, rpw, w.st, w.fine, tau, w.cnt, w.gsum, na, cq, gx1, nb1);
+    // codes: 128-column x 128-row tiles
+    const int64_t gx2 = (cq.N + kTN - 1) / kTN;
+    const int64_t nb2 = gx2 * ((cq.ldq * 2) / kTK);
+    compact_qcols_kernel<CH><<<dim3(unsigned(na + nb2)), kRowWaves * kWave, 0, stream>>>(
+        A, M, K, lda, rpw, w.st, tau, w.cnt, w.gsum, capacity, row_ptr, row, col, val, Aq, ldq,
+        sA, na, cq, gx2, nb2);
+    *w_done = true;
+    return hipGetLastError();
+  }
+}
+
+}  // namespace
+
+bool forward_front_supported(const void* A, const void* W, bool bf16, int64_t K, int64_t lda,
+                             int64_t ldw) {
+  const bool a_fast = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && ((lda * 2) % 16 == 0) &&
+                      (K % 8 == 0);
+  const bool w_aligned = (reinterpret_cast<uintptr_t>(W) % 16 == 0) && ((ldw * 2) % 16 == 0);
+  // the padded row fits one slab of 16 chunks per lane
+  const int64_t kp = (K + 127) / 128 * 128;
+  return bf16 && a_fast && w_aligned && kp <= int64_t(kWave) * 16 * 8;
+}
+
+hipError_t launch_forward_front(const void* A, int64_t M, int64_t K, int64_t lda, int64_t k,
+                                float* tau, int64_t capacity, int32_t* row, int32_t* col,
+                                float* val, int32_t* row_ptr, void* ws, uint8_t* Aq, int64_t ldq,
+                                float* sA, const void* W, int64_t N, int64_t ldw, uint8_t* Wq,
+                                float* sW, uint32_t* colmax, bool* w_done, hipStream_t stream) {
+  const uint16_t* A16 = static_cast<const uint16_t*>(A);
+  const ColQuantArgs cq{static_cast<const uint16_t*>(W), K, N, ldw, colmax, Wq, ldq, sW};
+  // the padded row length (a multiple of 128) needs no more chunks than K:
+  // 512 * CH is a multiple of 128
+  const int ch = chunks_per_lane(K, 16);
+  if (chunks_per_lane(ldq * 2, 16) != ch) return hipErrorInvalidValue;
+  switch (ch) {
+#define FP4LIN_FF(CH)                                                                            \
+  case CH:                                                                                       \
+    return forward_front<CH>(A16, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, Aq,   \
+                             ldq, sA, cq, w_done, stream);
+    FP4LIN_FF(1)
+    FP4LIN_FF(2)
+    FP4LIN_FF(4)
+    FP4LIN_FF(8)
+    FP4LIN_FF(16)
+#undef FP4LIN_FF
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fp4lin

@@ -79,8 +79,9 @@ def test_workspace_layout_consistent():
             (o.tau, 4), (o.coo_row, 4 * max(o.capacity, 1)), (o.coo_col, 4 * max(o.capacity, 1)),
             (o.coo_val, 4 * max(o.capacity, 1)), (o.row_ptr, 4 * (M + 1)), (o.Aq, M * ldq),
             (o.sA, 4 * M), (o.Wq, N * ldq), (o.sW, 4 * N),
-            (o.scratch, max(L.fp4lin_select_workspace_bytes(M, K, dt),
-                            L.fp4lin_weight_workspace_bytes(K, N)))])
+            # the select's workspace and W's column maxima are live together
+            (o.scratch, L.fp4lin_select_workspace_bytes(M, K, dt)
+             + L.fp4lin_weight_workspace_bytes(K, N))])
         for (a, na), (b, _) in zip(regions, regions[1:]):
             assert a + na <= b                       # no overlap
         for off, _ in regions:
@@ -223,6 +224,11 @@ def test_forward_errors():
     assert forward(ws=MISALIGNED) == _lib.ERR_ALIGN
     need = L.fp4lin_workspace_bytes(4, 8, 4, 1, 0.5)
     assert forward(wsb=need - 1) == _lib.ERR_WORKSPACE
+    # the GEMM's limits are checked before anything is enqueued (no device here:
+    # a launch would fail with a launch error instead)
+    assert forward(M=2 ** 20 - 1, K=2 ** 12, lda=2 ** 12, q=1.0, wsb=1 << 40) == _lib.ERR_SHAPE
+    assert forward(M=1, K=2 ** 20, lda=2 ** 20, N=8, ldw=2 ** 11, ldy=8, q=1.0,
+                   wsb=1 << 40) == _lib.ERR_SHAPE          # W beyond 2 GiB
 
 
 def test_python_binding_refuses_cpu_tensors():
