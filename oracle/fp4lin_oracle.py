@@ -53,6 +53,23 @@ Readings where the pages are silent (each is listed in the design notes):
   R10 wgrad dW = Q(A)^T Q(dY): A and dY both quantized per column over M (the
       reduction), with no clamp and no compensation term, so that both scales
       leave the reduction; the channel-wise quantizer of W applied to A and dY.
+  R11 Micro-scaled variant ([mx] section 3: groups with one scale each taken
+      from the group's max, elements divided by it and rounded to FP4;
+      [survey] custom-formats section: one E8M0 scale per block beside
+      low-precision elements). Blocks are 32 consecutive elements along the
+      reduction (K): per row of A, per column of W. A block's scale is 2^e
+      with e the smallest integer >= -127 for which 6 * 2^e >= the block's
+      max |x| (the max lands inside the FP4 range, none is clipped, and E8M0
+      holds only powers of two); it is stored as the byte e + 127. Elements
+      are y = |x| / 2^e (exact) rounded as in R3/R4. A is clamped to +-tau
+      first, as in the forward. Padding elements are zero; an all-zero block
+      has e = -127. Y0[i,j] = sum over blocks b of
+      2^(eA[i,b] + eW[j,b]) * sum_{k in b} v(qa[i,k]) v(qw[j,k]), with no
+      separate scale epilogue, and Y = Y0 + Delta A . W.
+
+Page tags: [news] "微软首创FP4训练框架，训练效果媲美BF16，助力大模型训练更高效";
+[mx] "FP4量化训练的硬件挑战：NVIDIA Blackwell架构上的微缩放格式（Micro-scaling）实现";
+[survey] "训练大型语言模型的挑战".
 """
 from __future__ import annotations
 
@@ -328,6 +345,123 @@ def wgrad(A32: np.ndarray, dY32: np.ndarray, rows=None):
         rows = np.arange(c_a2.shape[0])
     acc = integer_product(c_a2[rows], c_dy2)
     return scaled_product(acc, s_a2[rows], s_dy2), (Aq2, s_a2, c_a2), (dYq2, s_dy2, c_dy2)
+
+
+# --------------------------------------------------------------------------
+# Micro-scaled variant ([mx] section 3, the principle and the steps of
+# micro-scaling; [survey] custom-formats section, per-block E8M0 scales;
+# reading R11)
+# --------------------------------------------------------------------------
+MX_BLOCK = 32          # elements per block along the reduction
+E8M0_BIAS = 127
+E8M0_MIN_EXP = -127    # byte 0
+
+
+def mx_block_exponents(amax) -> np.ndarray:
+    """Smallest integer e >= -127 with 6 * 2**e >= amax, elementwise (amax >= 0)."""
+    a = np.asarray(amax, dtype=np.float64)
+    e = np.full(a.shape, E8M0_MIN_EXP, dtype=np.int64)
+    nz = a > 0
+    with np.errstate(divide="ignore"):
+        guess = np.ceil(np.log2(np.where(nz, a, 1.0) / FP4_MAX)).astype(np.int64)
+    e = np.where(nz, guess, e)
+    # log2 is rounded: move to the exact boundary (6 * 2**e is exact in float64)
+    for _ in range(3):
+        e = np.where(nz & (np.ldexp(FP4_MAX, e) < a), e + 1, e)
+    for _ in range(3):
+        e = np.where(nz & (np.ldexp(FP4_MAX, e - 1) >= a), e - 1, e)
+    return np.maximum(e, E8M0_MIN_EXP)
+
+
+def quantize_rows_mx(X32: np.ndarray):
+    """Blocks of 32 along each row. Returns (codes uint8 R x L, exponents
+    int64 R x (packed_ld(L)/16)); the blocks cover the zero padding too."""
+    X32 = np.asarray(X32, dtype=np.float32)
+    R, L = X32.shape
+    Lp = packed_ld(L) * 2
+    full = np.zeros((R, Lp), dtype=np.float64)
+    full[:, :L] = X32
+    nb = Lp // MX_BLOCK
+    blocks = np.abs(full).reshape(R, nb, MX_BLOCK)
+    e = mx_block_exponents(blocks.max(axis=2))
+    y = np.ldexp(blocks, -e[:, :, None]).reshape(R, Lp)[:, :L]   # exact
+    mag = np.zeros((R, L), dtype=np.uint8)
+    for t in E2M1_MIDPOINTS.astype(np.float64):
+        mag += (y >= t).astype(np.uint8)
+    sign = np.signbit(X32).astype(np.uint8)
+    return (sign << 3) | mag, e
+
+
+def mx_scale_bytes(e: np.ndarray) -> np.ndarray:
+    """E8M0 byte of each block exponent."""
+    return (np.asarray(e, dtype=np.int64) + E8M0_BIAS).astype(np.uint8)
+
+
+def quantize_act_mx(X32: np.ndarray, tau=None):
+    """Micro-scaled quantization of (optionally clamped) activations.
+
+    Returns (packed codes M x packed_ld(K), scale bytes M x packed_ld(K)/16,
+    codes M x K, exponents)."""
+    X32 = np.asarray(X32, dtype=np.float32)
+    if tau is not None:
+        tau = np.float32(tau)
+        X32 = np.where(np.abs(X32) > tau, np.copysign(tau, X32), X32).astype(np.float32)
+    codes, e = quantize_rows_mx(X32)
+    return pack_rows(codes), mx_scale_bytes(e), codes, e
+
+
+def quantize_weight_mx(W32: np.ndarray):
+    """Micro-scaled quantization of a K x N weight along K, packed N-major.
+
+    Returns (packed N x packed_ld(K), scale bytes N x packed_ld(K)/16,
+    codes N x K, exponents)."""
+    codes_nk, e = quantize_rows_mx(np.ascontiguousarray(np.asarray(W32, dtype=np.float32).T))
+    return pack_rows(codes_nk), mx_scale_bytes(e), codes_nk, e
+
+
+def mx_product(codesA, eA, codesB_nmajor, eB):
+    """Y0[i,j] = sum_b 2^(eA[i,b]+eB[j,b]) sum_{k in b} v(A[i,k]) v(B[j,k]).
+
+    Each block's sum is exact in float64 (integers / 4); the blocks are added
+    in ascending order. Returns (Y0, sum over blocks of |term|), both float64."""
+    codesA = np.asarray(codesA, dtype=np.uint8)
+    codesB = np.asarray(codesB_nmajor, dtype=np.uint8)
+    K = codesA.shape[1]
+    Kp = packed_ld(K) * 2
+    a2 = np.zeros((codesA.shape[0], Kp))
+    b2 = np.zeros((codesB.shape[0], Kp))
+    a2[:, :K] = 2.0 * decode(codesA)
+    b2[:, :K] = 2.0 * decode(codesB)
+    y = np.zeros((a2.shape[0], b2.shape[0]))
+    mag = np.zeros_like(y)
+    for b in range(Kp // MX_BLOCK):
+        blk = slice(b * MX_BLOCK, (b + 1) * MX_BLOCK)
+        acc = (a2[:, blk] @ b2[:, blk].T) / 4.0
+        term = np.ldexp(acc, np.asarray(eA)[:, b][:, None] + np.asarray(eB)[:, b][None, :])
+        y += term
+        mag += np.abs(term)
+    return y, mag
+
+
+def forward_mx(A32: np.ndarray, W32: np.ndarray, q: float, rows=None):
+    """Micro-scaled forward Y = Q_mx(A_c) Q_mx(W) + Delta A . W (reading R11).
+
+    Returns (Y float64 for all or the listed rows, |term| sums, tau, delta,
+    (Aq, As, codesA, eA), (Wq, Ws, codesW, eW))."""
+    tau, _ = select_threshold(A32, q)
+    _, delta = clamp_and_residual(A32, tau)
+    qa = quantize_act_mx(A32, tau)
+    qw = quantize_weight_mx(W32)
+    if rows is None:
+        rows = np.arange(qa[2].shape[0])
+    rows = np.asarray(rows)
+    y, mag = mx_product(qa[2][rows], qa[3][rows], qw[2], qw[3])
+    W64 = np.asarray(W32, dtype=np.float64)
+    for t, i in enumerate(rows):
+        lo, hi = int(delta.row_ptr[i]), int(delta.row_ptr[i + 1])
+        if hi > lo:
+            y[t] += delta.val64[lo:hi] @ W64[delta.col[lo:hi]]
+    return y, mag, tau, delta, qa, qw
 
 
 def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:

@@ -414,3 +414,121 @@ def test_golden_tiny_fixture():
     assert h(ops.delta.row_ptr.astype(np.int32)) == g["row_ptr_sha256"]
     assert h(ops.delta.val32.astype(np.float32)) == g["coo_val32_sha256"]
     assert abs(float(np.linalg.norm(Y)) - g["Y_fro"]) <= 1e-9 * g["Y_fro"]
+
+
+# ---------------------------------------------------------------------------
+# Micro-scaled variant (reading R11; "FP4量化训练的硬件挑战：NVIDIA Blackwell架构上
+# 的微缩放格式（Micro-scaling）实现", section 3, and the custom-formats section of
+# "训练大型语言模型的挑战": one E8M0 scale per block)
+# ---------------------------------------------------------------------------
+def test_mx_exponent_closed_forms():
+    """e is the least integer >= -127 with 6 * 2^e >= amax: worked by hand."""
+    f32 = np.float32
+    cases = {
+        0.0: -127,                       # empty block: byte 0
+        6.0: 0, 12.0: 1, 3.0: -1, 1.5: -2, 0.75: -3,   # exactly 6 * 2^e
+        1.0: -2,                         # 6/4 = 1.5 >= 1 > 6/8
+        float(np.nextafter(f32(6), f32(7))): 1,
+        float(np.nextafter(f32(1.5), f32(2))): -1,
+        float(np.nextafter(f32(0), f32(1))): -127,     # smallest subnormal
+        float(np.finfo(np.float32).tiny): -127,        # 2^-126 <= 6 * 2^-127
+        float(np.finfo(np.float32).max): 126,          # < 2^128 <= 6 * 2^126
+        float(f32(2.0 ** 100)): 98,                     # 6 * 2^97 < 2^100 <= 6 * 2^98
+    }
+    e = O.mx_block_exponents(np.array(list(cases.keys())))
+    assert e.tolist() == list(cases.values())
+    assert O.mx_scale_bytes(e).tolist() == [v + 127 for v in cases.values()]
+
+
+def test_mx_exponent_is_least_covering_power():
+    """Against the definition by search over every candidate exponent."""
+    rng = np.random.default_rng(5)
+    amax = np.abs(rng.standard_normal(2000) * np.exp2(rng.integers(-140, 120, 2000))).astype(np.float32)
+    e = O.mx_block_exponents(amax.astype(np.float64))
+    for a, ei in zip(amax.astype(np.float64), e):
+        want = next(c for c in range(-127, 200) if 6.0 * 2.0 ** c >= a)
+        assert ei == want
+
+
+def test_mx_round_trip_exact_on_grid_blocks():
+    """Blocks made of grid values times a per-block power of two, each holding
+    +-6 * 2^e, decode back exactly, with exponent e."""
+    rng = np.random.default_rng(6)
+    R, L = 5, 256
+    grid = np.array(GRID)
+    vals = grid[rng.integers(0, 8, (R, L))] * rng.choice([-1.0, 1.0], (R, L))
+    ex = rng.integers(-20, 20, (R, L // 32))
+    vals.reshape(R, L // 32, 32)[:, :, 7] = 6.0            # each block reaches 6
+    X = (vals.reshape(R, L // 32, 32) * np.exp2(ex)[:, :, None]).reshape(R, L).astype(np.float32)
+    codes, e = O.quantize_rows_mx(X)
+    assert np.array_equal(e[:, : L // 32], ex)
+    back = O.decode(codes).reshape(R, L // 32, 32) * np.exp2(e[:, : L // 32])[:, :, None]
+    assert np.array_equal(back.reshape(R, L), X.astype(np.float64))
+
+
+def test_mx_codes_are_nearest_grid_values():
+    """Every code is the nearest grid value of x / 2^e (ties away from zero),
+    found by brute-force distance search; the block max lands in (3, 6]."""
+    rng = np.random.default_rng(7)
+    X = (rng.standard_t(3, (64, 200)) * np.exp2(rng.integers(-30, 30, (64, 1)))).astype(np.float32)
+    codes, e = O.quantize_rows_mx(X)
+    full = np.zeros((64, 256))
+    full[:, :200] = X
+    y = np.abs(full.reshape(64, 8, 32)) / np.exp2(e)[:, :, None]
+    near = _brute_nearest(y.reshape(64, 256)[:, :200].astype(np.float32))
+    assert np.array_equal(codes & 7, near)
+    assert np.array_equal(codes >> 3, np.signbit(X).astype(np.uint8))
+    bmax = y.max(axis=2)
+    live = bmax > 0
+    assert np.all((bmax[live] > 3.0) & (bmax[live] <= 6.0))
+    assert np.all(e[~live] == -127)
+    # x / 2^e is exact: no value of y is rounded
+    assert np.array_equal(y * np.exp2(e)[:, :, None], np.abs(full.reshape(64, 8, 32)))
+
+
+def test_mx_product_equals_dequantized_matmul():
+    """The block-scaled sum equals the plain product of the dequantized
+    operands (v * 2^e expanded over each block), and a triple loop on a tiny case."""
+    rng = np.random.default_rng(8)
+    M, N, K = 9, 7, 150
+    A = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-8, 8, (M, 1)))).astype(np.float32)
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    _, _, ca, ea = O.quantize_act_mx(A)
+    _, _, cw, ew = O.quantize_weight_mx(W)
+    y, mag = O.mx_product(ca, ea, cw, ew)
+    Kp = O.packed_ld(K) * 2
+    da = np.zeros((M, Kp)); da[:, :K] = O.decode(ca)
+    dw = np.zeros((N, Kp)); dw[:, :K] = O.decode(cw)
+    da *= np.repeat(np.exp2(ea), 32, axis=1)
+    dw *= np.repeat(np.exp2(ew), 32, axis=1)
+    ref = da @ dw.T
+    assert np.allclose(y, ref, rtol=1e-13, atol=0)
+    assert np.all(mag >= np.abs(y) * (1 - 1e-13))
+    for i in (0, 4):
+        for j in (0, 6):
+            s = sum(Fraction(float(da[i, k])) * Fraction(float(dw[j, k])) for k in range(Kp))
+            assert float(s) == pytest.approx(y[i, j], rel=1e-14, abs=1e-300)
+
+
+def test_mx_unit_scales_reduce_to_integer_product():
+    """With every exponent 0 the block-scaled product is the plain integer product."""
+    rng = np.random.default_rng(9)
+    ca = rng.integers(0, 16, (6, 96)).astype(np.uint8)
+    cb = rng.integers(0, 16, (5, 96)).astype(np.uint8)
+    nb = O.packed_ld(96) // 16
+    y, _ = O.mx_product(ca, np.zeros((6, nb), int), cb, np.zeros((5, nb), int))
+    assert np.array_equal(y, O.integer_product(ca, cb))
+
+
+def test_mx_weight_blocks_run_along_k():
+    """W's blocks are 32 consecutive k of one column: scaling one column's
+    block by 2^s moves only that block's exponent, by s."""
+    rng = np.random.default_rng(10)
+    W = rng.standard_normal((100, 6)).astype(np.float32)
+    _, sb, c0, e0 = O.quantize_weight_mx(W)
+    W2 = W.copy(); W2[32:64, 3] *= np.float32(8.0)
+    _, _, c1, e1 = O.quantize_weight_mx(W2)
+    diff = e1 - e0
+    assert diff[3, 1] == 3 and np.count_nonzero(diff) == 1
+    assert np.array_equal(c0, c1)
+    assert sb.shape == (6, O.packed_ld(100) // 16)
