@@ -226,6 +226,63 @@ fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtyp
                                 int64_t K, int64_t ldw, int64_t M, int64_t N, float* Y,
                                 int64_t ldy, hipStream_t stream);
 
+/* ---- micro-scaled (MXFP4) variant ------------------------------------------
+ * Micro-scaling lecture "FP4量化训练的硬件挑战：NVIDIA Blackwell架构上的微缩放格式
+ * （Micro-scaling）实现", section 3 (one scale per small group, taken from the
+ * group's max, elements divided by it and rounded to FP4), with the per-block
+ * E8M0 scales of the format survey "训练大型语言模型的挑战" (custom-formats
+ * section). Blocks are 32 consecutive codes along K: per row of A, per column
+ * of W. A block's scale is 2^e, e the least integer >= -127 with
+ * 6 * 2^e >= the block's max |x| (so no element is clipped), stored as the
+ * byte e + 127; each element is |x| / 2^e (exact) rounded to the nearest E2M1
+ * value, ties away from zero, sign copied. Padding codes are zero and a block
+ * with no non-zero element has the byte 0. A scale row holds
+ * fp4lin_mx_scales_ld(K) = fp4lin_packed_ld(K) / 16 bytes. */
+
+/* Bytes per row of E8M0 block scales for rows of L codes, or -1 if L < 1. */
+int64_t fp4lin_mx_scales_ld(int64_t L);
+
+/* Micro-scaled activation quantization: X (clamped to [-tau, tau] when tau is
+ * given, as in the forward) in blocks of 32 along each row.
+ *   X        device, M x K, dtype dt, leading dimension ldx
+ *   tau      device, 1 float, or NULL for no clamping
+ *   Xq       device, M x fp4lin_packed_ld(K) bytes (output, padding zeroed)
+ *   Xs       device, M x fp4lin_mx_scales_ld(K) bytes (output)
+ * Xq and Xs must be 16-byte aligned.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, LAUNCH. */
+fp4lin_status fp4lin_quantize_act_mx(const void* X, fp4lin_dtype dt, int64_t M, int64_t K,
+                                     int64_t ldx, const float* tau, uint8_t* Xq, uint8_t* Xs,
+                                     hipStream_t stream);
+
+/* Micro-scaled weight quantization: blocks of 32 along K in each column of the
+ * K x N weight, written N-major like fp4lin_quantize_weight. Needs no workspace.
+ *   W        device, K x N, dtype dt, leading dimension ldw
+ *   Wq       device, N x fp4lin_packed_ld(K) bytes (output, padding zeroed)
+ *   Ws       device, N x fp4lin_mx_scales_ld(K) bytes (output)
+ * Wq and Ws must be 16-byte aligned; K must be below 2^23 (tiles of 128 codes
+ * along K index the second grid dimension), else FP4LIN_ERR_SHAPE.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, LAUNCH. */
+fp4lin_status fp4lin_quantize_weight_mx(const void* W, fp4lin_dtype dt, int64_t K, int64_t N,
+                                        int64_t ldw, uint8_t* Wq, uint8_t* Ws,
+                                        hipStream_t stream);
+
+/* Micro-scaled FP4 GEMM: the block scales go to the matrix core's scale
+ * operands, so
+ *   Y[i,j] = sum over blocks b of 2^(eA[i,b] + eB[j,b]) *
+ *            sum_{k in b} v(Aq[i,k]) v(Bq[j,k])       (fp32 accumulation)
+ *            + s[i,j]                                  (as in fp4lin_gemm)
+ * with no separate scale epilogue. Each block's dot product and its scaling
+ * are exact; the sum over blocks is rounded to fp32.
+ *   Aq, As   device, M x packed_ld(K) bytes, M x mx_scales_ld(K) bytes
+ *   Bq, Bs   device, N x packed_ld(K) bytes (N-major), N x mx_scales_ld(K)
+ *   dA, W, wdt, ldw, Y, ldy   as in fp4lin_gemm
+ * Aq, Bq, As and Bs must be 16-byte aligned; the limits of fp4lin_gemm apply.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, LAUNCH. */
+fp4lin_status fp4lin_gemm_mx(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq,
+                             const uint8_t* Bs, int64_t M, int64_t N, int64_t K,
+                             const fp4lin_coo* dA, const void* W, fp4lin_dtype wdt,
+                             int64_t ldw, float* Y, int64_t ldy, hipStream_t stream);
+
 /* The whole layer forward (forward-start paragraph: W and A are quantized when
  * the layer's forward begins). Computes what fp4lin_outlier_select,
  * fp4lin_quantize_act (with the selected tau), fp4lin_quantize_weight and

@@ -19,7 +19,8 @@ __all__ = [
     "weight_workspace_bytes", "workspace_bytes", "forward_layout",
     "fp4lin_outlier_select", "fp4lin_quantize_act", "fp4lin_quantize_weight", "fp4lin_gemm",
     "fp4lin_sparse_add", "fp4lin_forward", "outlier_select", "quantize_act", "quantize_weight", "gemm", "forward",
-    "CooBuffers",
+    "CooBuffers", "mx_scales_ld", "fp4lin_quantize_act_mx", "fp4lin_quantize_weight_mx",
+    "fp4lin_gemm_mx", "quantize_act_mx", "quantize_weight_mx", "gemm_mx",
 ]
 
 
@@ -189,6 +190,34 @@ def fp4lin_forward(A, W, q, Y, ws, stream=None):
            "fp4lin_forward")
 
 
+def fp4lin_quantize_act_mx(X, tau, Xq, Xs, stream=None):
+    M, K, ldx = _matrix(X, "X")
+    _check(lib().fp4lin_quantize_act_mx(_dev(X, "X"), _dtype_code(X), M, K, ldx,
+                                        _dev(tau, "tau"), _dev(Xq, "Xq"), _dev(Xs, "Xs"),
+                                        _stream(stream)),
+           "fp4lin_quantize_act_mx")
+
+
+def fp4lin_quantize_weight_mx(W, Wq, Ws, stream=None):
+    K, N, ldw = _matrix(W, "W")
+    _check(lib().fp4lin_quantize_weight_mx(_dev(W, "W"), _dtype_code(W), K, N, ldw,
+                                           _dev(Wq, "Wq"), _dev(Ws, "Ws"), _stream(stream)),
+           "fp4lin_quantize_weight_mx")
+
+
+def fp4lin_gemm_mx(Aq, As, Bq, Bs, M, N, K, coo: CooBuffers | None, W, Y, stream=None):
+    _, _, ldy = _matrix(Y, "Y")
+    if coo is not None:
+        _, _, ldw = _matrix(W, "W")
+        c = coo.struct()
+        cp, wp, wdt = ctypes.byref(c), _dev(W, "W"), _dtype_code(W)
+    else:
+        cp, wp, wdt, ldw = None, None, F32, 0
+    _check(lib().fp4lin_gemm_mx(_dev(Aq, "Aq"), _dev(As, "As"), _dev(Bq, "Bq"), _dev(Bs, "Bs"),
+                                M, N, K, cp, wp, wdt, ldw, _dev(Y, "Y"), ldy, _stream(stream)),
+           "fp4lin_gemm_mx")
+
+
 # ---- allocating helpers --------------------------------------------------------------
 def _empty(shape, dtype, device):
     return _torch().empty(shape, dtype=dtype, device=device)
@@ -249,3 +278,34 @@ def forward(A, W, q, stream=None, return_workspace=False):
     Y = _empty((M, N), torch.float32, A.device)
     fp4lin_forward(A, W, q, Y, ws, stream)
     return (Y, ws) if return_workspace else Y
+
+
+def mx_scales_ld(L: int) -> int:
+    return lib().fp4lin_mx_scales_ld(L)
+
+
+def quantize_act_mx(X, tau=None, stream=None):
+    """Micro-scaled: returns (Xq uint8 M x packed_ld(K), Xs uint8 M x mx_scales_ld(K))."""
+    torch = _torch()
+    M, K, _ = _matrix(X, "X")
+    Xq = _empty((M, packed_ld(K)), torch.uint8, X.device)
+    Xs = _empty((M, mx_scales_ld(K)), torch.uint8, X.device)
+    fp4lin_quantize_act_mx(X, tau, Xq, Xs, stream)
+    return Xq, Xs
+
+
+def quantize_weight_mx(W, stream=None):
+    """Micro-scaled: returns (Wq uint8 N x packed_ld(K), Ws uint8 N x mx_scales_ld(K))."""
+    torch = _torch()
+    K, N, _ = _matrix(W, "W")
+    Wq = _empty((N, packed_ld(K)), torch.uint8, W.device)
+    Ws = _empty((N, mx_scales_ld(K)), torch.uint8, W.device)
+    fp4lin_quantize_weight_mx(W, Wq, Ws, stream)
+    return Wq, Ws
+
+
+def gemm_mx(Aq, As, Bq, Bs, M, N, K, coo=None, W=None, stream=None):
+    """Micro-scaled GEMM; returns Y float32 M x N."""
+    Y = _empty((M, N), _torch().float32, Aq.device)
+    fp4lin_gemm_mx(Aq, As, Bq, Bs, M, N, K, coo, W, Y, stream)
+    return Y

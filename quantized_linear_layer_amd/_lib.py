@@ -53,6 +53,13 @@ SIGNATURES = {
                                   c_ptr, c_i64, c_ptr]),
     "fp4lin_forward": (c_int, [c_ptr, c_ptr, c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl,
                                c_ptr, c_i64, c_ptr, c_size, c_ptr]),
+    "fp4lin_mx_scales_ld": (c_i64, [c_i64]),
+    "fp4lin_quantize_act_mx": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr, c_ptr,
+                                       c_ptr]),
+    "fp4lin_quantize_weight_mx": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr,
+                                          c_ptr]),
+    "fp4lin_gemm_mx": (c_int, [c_ptr, c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64,
+                               ctypes.POINTER(Coo), c_ptr, c_int, c_i64, c_ptr, c_i64, c_ptr]),
 }
 
 _lib = None

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp4lin.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "select.hip", "quantize.hip", "gemm.hip", "spmm.hip"]
+SOURCES = ["api.hip", "select.hip", "quantize.hip", "mx.hip", "gemm.hip", "spmm.hip"]
 
 # Packed fp32 VALU ops are switched off for all device code; fp32 denormals are
 # kept (inputs may be subnormal and the encoder must see them); no FMA

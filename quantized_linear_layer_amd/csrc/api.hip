@@ -232,6 +232,56 @@ fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtyp
   return launch_status(fp4lin::launch_sparse_add(sp, M, N, Y, ldy, stream));
 }
 
+int64_t fp4lin_mx_scales_ld(int64_t L) {
+  if (L < 1) return -1;
+  return fp4lin_packed_ld(L) / 16;
+}
+
+fp4lin_status fp4lin_quantize_act_mx(const void* X, fp4lin_dtype dt, int64_t M, int64_t K,
+                                     int64_t ldx, const float* tau, uint8_t* Xq, uint8_t* Xs,
+                                     hipStream_t stream) {
+  if (X == nullptr || Xq == nullptr || Xs == nullptr) return FP4LIN_ERR_NULL;
+  if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
+  if (!ok_dim(M) || !ok_dim(K) || ldx < K) return FP4LIN_ERR_SHAPE;
+  if (!aligned16(Xq) || !aligned16(Xs)) return FP4LIN_ERR_ALIGN;
+  return launch_status(fp4lin::launch_quantize_rows_mx(X, dt == FP4LIN_BF16, M, K, ldx, tau, Xq,
+                                                       fp4lin_packed_ld(K), Xs, stream));
+}
+
+fp4lin_status fp4lin_quantize_weight_mx(const void* W, fp4lin_dtype dt, int64_t K, int64_t N,
+                                        int64_t ldw, uint8_t* Wq, uint8_t* Ws,
+                                        hipStream_t stream) {
+  if (W == nullptr || Wq == nullptr || Ws == nullptr) return FP4LIN_ERR_NULL;
+  if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
+  if (!ok_dim(K) || !ok_dim(N) || ldw < N || K >= (int64_t(1) << 23)) return FP4LIN_ERR_SHAPE;
+  if (!aligned16(Wq) || !aligned16(Ws)) return FP4LIN_ERR_ALIGN;
+  return launch_status(fp4lin::launch_quantize_cols_mx(W, dt == FP4LIN_BF16, K, N, ldw, Wq,
+                                                       fp4lin_packed_ld(K), Ws, stream));
+}
+
+fp4lin_status fp4lin_gemm_mx(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq,
+                             const uint8_t* Bs, int64_t M, int64_t N, int64_t K,
+                             const fp4lin_coo* dA, const void* W, fp4lin_dtype wdt,
+                             int64_t ldw, float* Y, int64_t ldy, hipStream_t stream) {
+  if (Aq == nullptr || As == nullptr || Bq == nullptr || Bs == nullptr || Y == nullptr)
+    return FP4LIN_ERR_NULL;
+  if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldy < N) return FP4LIN_ERR_SHAPE;
+  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, false, 0, 0};
+  if (dA != nullptr) {
+    if (dA->row_ptr == nullptr || dA->col == nullptr || dA->val == nullptr || W == nullptr)
+      return FP4LIN_ERR_NULL;
+    if (bad_dtype(wdt)) return FP4LIN_ERR_DTYPE;
+    if (ldw < N || !weight_addressable(K, ldw, wdt)) return FP4LIN_ERR_SHAPE;
+    sp = fp4lin::SparseArgs{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K};
+  }
+  // packed operands and scale rows are addressed with 32-bit byte offsets
+  const int64_t ldq = fp4lin_packed_ld(K);
+  if ((M + 1) * ldq >= kMaxDim || (N + 1) * ldq >= kMaxDim) return FP4LIN_ERR_SHAPE;
+  if (!aligned16(Aq) || !aligned16(Bq) || !aligned16(As) || !aligned16(Bs))
+    return FP4LIN_ERR_ALIGN;
+  return launch_status(fp4lin::launch_fp4_gemm_mx(Aq, As, Bq, Bs, M, N, ldq, sp, Y, ldy, stream));
+}
+
 fp4lin_status fp4lin_forward(const void* A, const void* W, fp4lin_dtype dt, int64_t M, int64_t K,
                              int64_t N, int64_t lda, int64_t ldw, double q, float* Y, int64_t ldy,
                              void* ws, size_t ws_bytes, hipStream_t stream) {

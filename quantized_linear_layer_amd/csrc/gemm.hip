@@ -16,6 +16,14 @@
 //   Y[i,j] = RN32(RN32(acc[i,j] * sA[i]) * sB[j])
 // The sparse compensation term is added afterwards by spmm.hip.
 //
+// Micro-scaled variant (kMx; the micro-scaling lecture "FP4量化训练的硬件挑战：
+// NVIDIA Blackwell架构上的微缩放格式（Micro-scaling）实现", section 3, with the E8M0
+// block scales of the format survey "训练大型语言模型的挑战"): A and B carry one
+// E8M0 byte per 32 codes along K (mx.hip), which the instruction takes as its
+// per-lane block-scale operands in place of the unit scales, and the epilogue
+// writes the accumulator as it is: Y[i,j] = sum over blocks of
+// 2^(eA + eB) * (block's FP4 dot product), accumulated in fp32.
+//
 // Layout and schedule:
 //  * A is M x ldq bytes and B is N x ldq bytes, K-contiguous packed rows.
 //  * A workgroup of 4 waves (2 x 2 grid, each wave 64 x 128 outputs) owns a
@@ -46,6 +54,8 @@
 //    instructions than storing from the MFMA layout). The stores are
 //    non-temporal: the output stream is not kept in L2 at the expense of the
 //    operand tiles that concurrent workgroups re-read.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -124,11 +134,12 @@ __device__ inline void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int v
 // the caller waits for the counters it needs first.
 __device__ inline void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <class C>
+template <class C, bool kMx>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
     const uint8_t* __restrict__ Aq, const float* __restrict__ sA,
     const uint8_t* __restrict__ Bq, const float* __restrict__ sB, int M, int N, int ldq,
-    int tiles_m, float* __restrict__ Y, int64_t ldy) {
+    int tiles_m, float* __restrict__ Y, int64_t ldy, const uint8_t* __restrict__ As,
+    const uint8_t* __restrict__ Bs) {
   constexpr int BM = C::BM, BN = C::BN, WN = C::WN, BKB = C::BKB, CPR = C::CPR;
   constexpr int FM = C::FM, FN = C::FN, NT = C::kThreads;
   constexpr int SB = C::kStageBytes;
@@ -214,14 +225,57 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
       bf[fn] = v8i{int(u.x), int(u.y), int(u.z), int(u.w), 0, 0, 0, 0};
     }
   };
-  auto mfmas = [&](const v8i* af, const v8i* bf) {
+  // Block scales (kMx). The E8M0 bytes of a row's blocks 4kt .. 4kt+3 (the
+  // 128 codes of K step kt) are one aligned 32-bit word of its scale row
+  // (ldq / 16 bytes). Lane half h supplies codes 32h .. 32h+31 of each 64-code
+  // sub-step, i.e. block 4kt + 2kk + h in sub-step kk: the word shifted right
+  // by 8h, byte kk*2 of it picked by the instruction's op_sel. Rows past M (N)
+  // read the scale word as zero, beside their zero codes. The words of step kt
+  // go into slot kt mod 3 of a register ring, loaded three steps ahead.
+  constexpr int NS = kMx ? FM + FN : 0;
+  const int nblk = ldq / 16;
+  const __amdgpu_buffer_rsrc_t rsSA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(As), 0, kMx ? M * nblk : 0, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsSB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Bs), 0, kMx ? N * nblk : 0, kBufferFlags);
+  int sc_off[NS > 0 ? NS : 1];
+  if constexpr (kMx) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      sc_off[fm] = (m0 + a_row[fm] < M) ? (m0 + a_row[fm]) * nblk : M * nblk;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      sc_off[FM + fn] = (n0 + b_row[fn] < N) ? (n0 + b_row[fn]) * nblk : N * nblk;
+  }
+  const int hshift = (lane >> 5) * 8;
+  uint32_t sc0[NS > 0 ? NS : 1], sc1[NS > 0 ? NS : 1], sc2[NS > 0 ? NS : 1];
+  // The manual vmcnt waits below count the stage loads and these in issue
+  // order; scheduling barriers keep every group where it is written.
+  auto load_scales = [&](int kt, uint32_t* dst) {
+    if constexpr (kMx) {
+#pragma unroll
+      for (int f = 0; f < NS; ++f)
+        dst[f] = __builtin_amdgcn_raw_buffer_load_b32(f < FM ? rsSA : rsSB, sc_off[f] + kt * 4, 0, 0);
+    }
+  };
+  // kk_c: the sub-step (0 or 1) as a type, so that op_sel is a constant
+  auto mfmas = [&](auto kk_c, const v8i* af, const v8i* bf, const uint32_t* sc) {
+    constexpr int KK = decltype(kk_c)::value;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf[fn], acc[fm][fn], 4, 4,
-                                                                      0, 127, 0, 127);
+      for (int fn = 0; fn < FN; ++fn) {
+        if constexpr (kMx)
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[fm], bf[fn], acc[fm][fn], 4, 4, 2 * KK, int(sc[fm] >> hshift), 2 * KK,
+              int(sc[FM + fn] >> hshift));
+        else
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf[fn], acc[fm][fn],
+                                                                        4, 4, 0, 127, 0, 127);
+      }
   };
+  using Sub0 = std::integral_constant<int, 0>;
+  using Sub1 = std::integral_constant<int, 1>;
 
   // Pipeline over K steps (stage of step s: s mod 3). On entry to step kt the
   // first sub-step's fragments of stage kt are in registers. The step reads
@@ -233,50 +287,61 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   // go there; then the second sub-step's MFMAs and the next step's first
   // fragment reads. Every wave issues kPer loads per step on every path
   // (past the last step they repeat it into a stage that is not read).
-  constexpr int kWaitCnt = waitcnt_vm_lgkm(kPer, 0);
-  static_assert(2 * kPer < 64, "vmcnt immediate");
+  // With block scales, each step also loads the NS scale words of step kt+3
+  // after its second sub-step; a step's wait then leaves that step's and the
+  // previous step's scale words in flight besides the stage of kt+2.
+  constexpr int kWaitCnt = waitcnt_vm_lgkm(kPer + 2 * NS, 0);
+  static_assert(2 * kPer + 2 * NS < 64, "vmcnt immediate");
   v8i a0[FM], b0[FN], a1[FM], b1[FN];
-  // a full step inside the main loop (steps kt, kt+1 and kt+2 all exist)
-  auto step = [&](int kt, const uint8_t* cur, const uint8_t* nxt, uint8_t* ldst) {
+  // a full step inside the main loop (steps kt, kt+1 and kt+2 all exist);
+  // sc holds the scale words of step kt and is refilled for step kt+3
+  auto step = [&](int kt, const uint8_t* cur, const uint8_t* nxt, uint8_t* ldst, uint32_t* sc) {
     read_frags(cur, 1, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(a0, b0);
+    mfmas(Sub0{}, a0, b0, sc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitCnt);
     raw_barrier();
     __builtin_amdgcn_sched_barrier(0);
     dma(kt + 3 < nkt ? kt + 3 : nkt - 1, ldst);
-    mfmas(a1, b1);
+    mfmas(Sub1{}, a1, b1, sc);
     __builtin_amdgcn_sched_barrier(0);
+    load_scales(kt + 3 < nkt ? kt + 3 : nkt - 1, sc);
     read_frags(nxt, 0, a0, b0);
   };
   // one of the last (up to two) steps: no more loads are issued
-  auto tail_step = [&](const uint8_t* cur, const uint8_t* nxt, bool has_next) {
+  auto tail_step = [&](const uint8_t* cur, const uint8_t* nxt, bool has_next, const uint32_t* sc) {
     read_frags(cur, 1, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(a0, b0);
+    mfmas(Sub0{}, a0, b0, sc);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, 0));
     raw_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(a1, b1);
+    mfmas(Sub1{}, a1, b1, sc);
     __builtin_amdgcn_sched_barrier(0);
     if (has_next) read_frags(nxt, 0, a0, b0);
   };
   dma(0, st0);
+  load_scales(0, sc0);
+  __builtin_amdgcn_sched_barrier(0);
   dma(nkt > 1 ? 1 : nkt - 1, st1);
+  load_scales(nkt > 1 ? 1 : nkt - 1, sc1);
+  __builtin_amdgcn_sched_barrier(0);
   dma(nkt > 2 ? 2 : nkt - 1, st2);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(2 * kPer, 0));  // step 0 landed
+  load_scales(nkt > 2 ? 2 : nkt - 1, sc2);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(2 * kPer + 2 * NS, 0));  // step 0 landed
   raw_barrier();
   read_frags(st0, 0, a0, b0);
   int kt0 = 0;
   for (; kt0 + 3 <= nkt; kt0 += 3) {
-    step(kt0, st0, st1, st0);
-    step(kt0 + 1, st1, st2, st1);
-    step(kt0 + 2, st2, st0, st2);
+    step(kt0, st0, st1, st0, sc0);
+    step(kt0 + 1, st1, st2, st1, sc1);
+    step(kt0 + 2, st2, st0, st2, sc2);
   }
-  if (kt0 < nkt) tail_step(st0, st1, kt0 + 1 < nkt);
-  if (kt0 + 1 < nkt) tail_step(st1, st2, false);
+  if (kt0 < nkt) tail_step(st0, st1, kt0 + 1 < nkt, sc0);
+  if (kt0 + 1 < nkt) tail_step(st1, st2, false, sc1);
   // every load has landed and every wave is done with the stages before they
   // are reused for the output
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, 0));
@@ -287,21 +352,24 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   // lanes 0..31 hold 32 consecutive columns of one row and lanes 32..63 the
   // same columns four rows down. All row and column scales of the lane are
   // loaded before any is used.
+  // (With block scales the accumulator is the output and no scale is loaded.)
   const int col_l = lane & 31;
   float sb[FN];
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    const int gc = n0 + wn * (FN * 32) + fn * 32 + col_l;
-    sb[fn] = (gc < N) ? sB[gc] : 0.0f;
-  }
   float sa[FM][16];
+  if constexpr (!kMx) {
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int gr = m0 + wm * (FM * 32) + fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      sa[fm][r] = (gr < M) ? sA[gr] : 0.0f;
+    for (int fn = 0; fn < FN; ++fn) {
+      const int gc = n0 + wn * (FN * 32) + fn * 32 + col_l;
+      sb[fn] = (gc < N) ? sB[gc] : 0.0f;
     }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gr = m0 + wm * (FM * 32) + fm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        sa[fm][r] = (gr < M) ? sA[gr] : 0.0f;
+      }
+  }
   // Output through a wave-private LDS block (the stage buffers are free after
   // the main loop's last barrier): two 32x32 fragments at a time are written
   // in the MFMA layout, read back as rows and stored 16 bytes per lane.
@@ -322,7 +390,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rl = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          eb[rl * kER + h * 32 + col_l] = __fmul_rn(__fmul_rn(acc[fm][fp + h][r], sa[fm][r]), sb[fp + h]);
+          eb[rl * kER + h * 32 + col_l] =
+              kMx ? acc[fm][fp + h][r] : __fmul_rn(__fmul_rn(acc[fm][fp + h][r], sa[fm][r]), sb[fp + h]);
         }
       const int row_base = m0 + wm * (FM * 32) + fm * 32;
       const int col_base = n0 + wn * (FN * 32) + fp * 32;
@@ -349,22 +418,35 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
 
 using GemmTile = GemmCfg<128, 256, 2, 2, 64, 2>;
 
-}  // namespace
-
-hipError_t launch_fp4_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const float* sB,
-                           int64_t M, int64_t N, int64_t ldq, const SparseArgs& sp, float* Y,
-                           int64_t ldy, hipStream_t stream) {
+template <bool kMx>
+hipError_t run_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const float* sB,
+                    const uint8_t* As, const uint8_t* Bs, int64_t M, int64_t N, int64_t ldq,
+                    const SparseArgs& sp, float* Y, int64_t ldy, hipStream_t stream) {
   using C = GemmTile;
   // K steps are whole 64-byte chunks of the packed rows (the packed row length
   // is a multiple of 64 bytes), so no step reads past a row.
   if (ldq % C::BKB != 0) return hipErrorInvalidValue;
   const int tiles_m = int((M + C::BM - 1) / C::BM);
   const int tiles_n = int((N + C::BN - 1) / C::BN);
-  fp4_gemm_kernel<C><<<dim3(unsigned(tiles_m * tiles_n)), C::kThreads, 0, stream>>>(
-      Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy);
+  fp4_gemm_kernel<C, kMx><<<dim3(unsigned(tiles_m * tiles_n)), C::kThreads, 0, stream>>>(
+      Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.row_ptr == nullptr) return e;
   return launch_sparse_add(sp, M, N, Y, ldy, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fp4_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const float* sB,
+                           int64_t M, int64_t N, int64_t ldq, const SparseArgs& sp, float* Y,
+                           int64_t ldy, hipStream_t stream) {
+  return run_gemm<false>(Aq, sA, Bq, sB, nullptr, nullptr, M, N, ldq, sp, Y, ldy, stream);
+}
+
+hipError_t launch_fp4_gemm_mx(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq,
+                              const uint8_t* Bs, int64_t M, int64_t N, int64_t ldq,
+                              const SparseArgs& sp, float* Y, int64_t ldy, hipStream_t stream) {
+  return run_gemm<true>(Aq, nullptr, Bq, nullptr, As, Bs, M, N, ldq, sp, Y, ldy, stream);
 }
 
 }  // namespace fp4lin

@@ -67,4 +67,15 @@ hipError_t launch_fp4_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq
                            int64_t M, int64_t N, int64_t ldq, const SparseArgs& sp, float* Y,
                            int64_t ldy, hipStream_t stream);
 
+// Micro-scaled operands: E2M1 codes with one E8M0 byte per 32 codes along K
+// (rows of ldq / 16 bytes). Xs / Ws / As / Bs are those scale rows.
+hipError_t launch_quantize_rows_mx(const void* X, bool bf16, int64_t M, int64_t K, int64_t ldx,
+                                   const float* tau, uint8_t* Xq, int64_t ldq, uint8_t* Xs,
+                                   hipStream_t stream);
+hipError_t launch_quantize_cols_mx(const void* W, bool bf16, int64_t K, int64_t N, int64_t ldw,
+                                   uint8_t* Wq, int64_t ldq, uint8_t* Ws, hipStream_t stream);
+hipError_t launch_fp4_gemm_mx(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq,
+                              const uint8_t* Bs, int64_t M, int64_t N, int64_t ldq,
+                              const SparseArgs& sp, float* Y, int64_t ldy, hipStream_t stream);
+
 }  // namespace fp4lin

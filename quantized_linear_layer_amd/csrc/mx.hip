@@ -1,0 +1,200 @@
+// Micro-scaled (MXFP4) quantization: E2M1 codes in blocks of 32 consecutive
+// elements along the reduction dimension K, one power-of-two scale per block
+// stored as an E8M0 byte.
+//
+// Method: the micro-scaling lecture ("FP4量化训练的硬件挑战：NVIDIA Blackwell架构上
+// 的微缩放格式（Micro-scaling）实现", section 3) splits a tensor into small groups,
+// gives each group its own scale taken from the group's maximum magnitude,
+// divides the elements by it and rounds them to FP4; the survey of number
+// formats ("训练大型语言模型的挑战", custom-formats section) pairs such blocks with
+// an E8M0 scale. A block's scale is 2^e with e the least integer >= -127 for
+// which 6 * 2^e covers the block's max |x| (so nothing is clipped), stored as
+// e + 127; each element is y = |x| / 2^e, exact, rounded to the nearest E2M1
+// value with ties away from zero, as in the token-wise quantizer. Activations
+// are clamped to +-tau first. The GEMM takes the bytes as the matrix core's
+// block-scale operands (gemm.hip).
+//
+// Rows (activations): one thread per 8-code chunk of a padded row, so four
+//   consecutive lanes hold one block and its max is two lane exchanges away;
+//   each thread writes its 8 codes as one 32-bit word and the first lane of a
+//   block writes the scale byte. No block needs more than its own 32 values, so
+//   rows of any length stream through once.
+// Columns (weights, K x N row-major): the 128 x 128 tiles of the channel-wise
+//   encode pass; a thread holds 8 consecutive rows of 8 columns, so the four
+//   lanes with the same columns and consecutive row groups hold one block of
+//   each of those columns.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace fp4lin {
+
+namespace {
+
+constexpr int kMxThreads = 256;
+
+// Least e >= -127 with 6 * 2^e >= amax (amax >= 0, finite). With
+// amax = m * 2^E, 1 <= m < 2: 1.5 * 2^E = 6 * 2^(E-2) covers amax exactly when
+// m <= 1.5, else 3 * 2^E = 6 * 2^(E-1) does. Zero and subnormal amax (and
+// every normal one below 6 * 2^-127) give -127.
+__device__ inline int mx_exponent(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int biased = int(b >> 23);
+  int e = ((b & 0x7fffffu) <= 0x400000u) ? biased - 129 : biased - 128;
+  if (biased == 0) e = -127;
+  return e < -127 ? -127 : e;
+}
+
+// Magnitude index of y = ax / 2^e: 4y = ax * 2^(2-e) is exact (ldexp never
+// rounds a result that reaches a midpoint; 4y <= 24), and the index is the
+// table lookup of the token-wise encoder at n = min(floor(4y), 20).
+__device__ inline uint32_t mx_magnitude(float ax, int e) {
+  uint32_t n = cvt_u32_sat(ldexpf(ax, 2 - e));
+  n = n < 20u ? n : 20u;
+  return uint32_t(e2m1_lut() >> (3u * n)) & 7u;
+}
+
+__device__ inline float quad_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, kWave));
+  return fmaxf(v, __shfl_xor(v, 2, kWave));
+}
+
+// Thread t takes chunk c = t mod cpr of row t / cpr (cpr = ldq / 4 chunks of 8
+// codes per padded row, a multiple of 16). Four consecutive t hold one block
+// and sit on four consecutive lanes, and the grid stride is a multiple of 4,
+// so a block's lanes are active together.
+template <class In, bool kFast>
+__global__ __launch_bounds__(kMxThreads) void quantize_rows_mx_kernel(
+    const typename In::T* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
+    const float* __restrict__ tau_p, uint8_t* __restrict__ Xq, int64_t ldq,
+    uint8_t* __restrict__ Xs, int64_t lds) {
+  const float tau = tau_p ? *tau_p : __builtin_huge_valf();
+  const int64_t cpr = ldq / 4;
+  const int64_t total = M * cpr;
+  for (int64_t t = int64_t(blockIdx.x) * kMxThreads + threadIdx.x; t < total;
+       t += int64_t(gridDim.x) * kMxThreads) {
+    const int64_t r = t / cpr;
+    const int64_t c = t - r * cpr;
+    Vec8<In> v;
+    load_chunk<In, kFast>(X + r * ldx, c * 8, K, v);
+    float ax[8];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ax[i] = fminf(fabsf(In::widen(v.v[i])), tau);
+      m = fmaxf(m, ax[i]);
+    }
+    const int e = mx_exponent(quad_max(m));
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      word |= (mx_magnitude(ax[i], e) | (In::sign_bit(v.v[i]) << 3)) << (4 * i);
+    *reinterpret_cast<uint32_t*>(Xq + r * ldq + c * 4) = word;
+    if ((c & 3) == 0) Xs[r * lds + c / 4] = uint8_t(e + 127);
+  }
+}
+
+constexpr int kMxTK = 128;  // codes along K per column tile
+constexpr int kMxTN = 128;  // columns per tile
+
+// Tile (bx, by): columns bx*128 .. +127, rows by*128 .. +127 (rows past K read
+// as zero and give the zero padding). Thread (kg, g) = (t % 16, t / 16) owns
+// rows k0 + 8kg .. +7 of columns n0 + 8g .. +7: the 8 codes of one column are
+// one 32-bit word of its packed row, and lanes 4q .. 4q+3 share block q.
+template <class In, bool kAligned>
+__global__ __launch_bounds__(kMxThreads) void quantize_cols_mx_kernel(
+    const typename In::T* __restrict__ W, int64_t K, int64_t N, int64_t ldw,
+    uint8_t* __restrict__ Wq, int64_t ldq, uint8_t* __restrict__ Ws, int64_t lds) {
+  const int t = threadIdx.x;
+  const int kg = t & 15, g = t >> 4;
+  const int64_t n0 = int64_t(blockIdx.x) * kMxTN;
+  const int64_t k0 = int64_t(blockIdx.y) * kMxTK;
+  const int64_t c = n0 + g * 8;
+  const int64_t valid = N - c;
+  const int64_t kr = k0 + kg * 8;
+  Vec8<In> v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (kr + u < K && valid > 0) {
+      load8<In, kAligned>(W + (kr + u) * ldw + c, valid, v[u]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[u].v[j] = typename In::T(0);
+    }
+  }
+  int e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float m = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(In::widen(v[u].v[j])));
+    e[j] = mx_exponent(quad_max(m));
+  }
+  if (valid <= 0) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= valid) break;
+    uint32_t word = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      word |= (mx_magnitude(fabsf(In::widen(v[u].v[j])), e[j]) | (In::sign_bit(v[u].v[j]) << 3))
+              << (4 * u);
+    *reinterpret_cast<uint32_t*>(Wq + (c + j) * ldq + kr / 2) = word;
+    if ((kg & 3) == 0) Ws[(c + j) * lds + kr / 32] = uint8_t(e[j] + 127);
+  }
+}
+
+unsigned mx_row_grid(int64_t threads) {
+  const int64_t b = (threads + kMxThreads - 1) / kMxThreads;
+  return unsigned(b < (int64_t(1) << 20) ? b : (int64_t(1) << 20));
+}
+
+template <class In>
+hipError_t run_rows_mx(const void* X, int64_t M, int64_t K, int64_t ldx, const float* tau,
+                       uint8_t* Xq, int64_t ldq, uint8_t* Xs, hipStream_t stream) {
+  using T = typename In::T;
+  const T* x = static_cast<const T*>(X);
+  const bool fast = (reinterpret_cast<uintptr_t>(X) % 16 == 0) &&
+                    ((ldx * In::kBytes) % 16 == 0) && (K % 8 == 0);
+  const unsigned grid = mx_row_grid(M * (ldq / 4));
+  if (fast)
+    quantize_rows_mx_kernel<In, true><<<grid, kMxThreads, 0, stream>>>(x, M, K, ldx, tau, Xq, ldq,
+                                                                       Xs, ldq / 16);
+  else
+    quantize_rows_mx_kernel<In, false><<<grid, kMxThreads, 0, stream>>>(x, M, K, ldx, tau, Xq,
+                                                                        ldq, Xs, ldq / 16);
+  return hipGetLastError();
+}
+
+template <class In>
+hipError_t run_cols_mx(const void* Wp, int64_t K, int64_t N, int64_t ldw, uint8_t* Wq,
+                       int64_t ldq, uint8_t* Ws, hipStream_t stream) {
+  using T = typename In::T;
+  const T* W = static_cast<const T*>(Wp);
+  const bool aligned = (reinterpret_cast<uintptr_t>(Wp) % 16 == 0) &&
+                       ((ldw * In::kBytes) % 16 == 0);
+  const dim3 grid(unsigned((N + kMxTN - 1) / kMxTN), unsigned((ldq * 2) / kMxTK));
+  if (aligned)
+    quantize_cols_mx_kernel<In, true><<<grid, kMxThreads, 0, stream>>>(W, K, N, ldw, Wq, ldq, Ws,
+                                                                       ldq / 16);
+  else
+    quantize_cols_mx_kernel<In, false><<<grid, kMxThreads, 0, stream>>>(W, K, N, ldw, Wq, ldq,
+                                                                        Ws, ldq / 16);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows_mx(const void* X, bool bf16, int64_t M, int64_t K, int64_t ldx,
+                                   const float* tau, uint8_t* Xq, int64_t ldq, uint8_t* Xs,
+                                   hipStream_t stream) {
+  return bf16 ? run_rows_mx<BF16In>(X, M, K, ldx, tau, Xq, ldq, Xs, stream)
+              : run_rows_mx<F32In>(X, M, K, ldx, tau, Xq, ldq, Xs, stream);
+}
+
+hipError_t launch_quantize_cols_mx(const void* W, bool bf16, int64_t K, int64_t N, int64_t ldw,
+                                   uint8_t* Wq, int64_t ldq, uint8_t* Ws, hipStream_t stream) {
+  return bf16 ? run_cols_mx<BF16In>(W, K, N, ldw, Wq, ldq, Ws, stream)
+              : run_cols_mx<F32In>(W, K, N, ldw, Wq, ldq, Ws, stream);
+}
+
+}  // namespace fp4lin

@@ -207,6 +207,54 @@ def test_sparse_add_errors():
     assert sparse_add(K=2 ** 20, ldw=2 ** 11) == _lib.ERR_SHAPE   # W beyond 2 GiB
 
 
+def test_mx_scales_ld():
+    for K in (1, 32, 127, 128, 129, 4096, 5120, 13824):
+        assert L.fp4lin_mx_scales_ld(K) == O.packed_ld(K) // 16
+    assert L.fp4lin_mx_scales_ld(0) == -1
+
+
+def test_quantize_mx_errors():
+    def act(X=FAKE, dt=1, M=4, K=8, ldx=8, Xq=FAKE, Xs=FAKE):
+        return L.fp4lin_quantize_act_mx(X, dt, M, K, ldx, None, Xq, Xs, None)
+
+    def wt(W=FAKE, dt=1, K=8, N=4, ldw=4, Wq=FAKE, Ws=FAKE):
+        return L.fp4lin_quantize_weight_mx(W, dt, K, N, ldw, Wq, Ws, None)
+
+    assert act(X=None) == _lib.ERR_NULL
+    assert act(Xs=None) == _lib.ERR_NULL
+    assert act(dt=7) == _lib.ERR_DTYPE
+    assert act(M=0) == _lib.ERR_SHAPE
+    assert act(ldx=7) == _lib.ERR_SHAPE
+    assert act(Xq=MISALIGNED) == _lib.ERR_ALIGN
+    assert act(Xs=MISALIGNED) == _lib.ERR_ALIGN
+    assert wt(Ws=None) == _lib.ERR_NULL
+    assert wt(dt=3) == _lib.ERR_DTYPE
+    assert wt(N=0) == _lib.ERR_SHAPE
+    assert wt(ldw=3) == _lib.ERR_SHAPE
+    assert wt(K=1 << 23, N=1, ldw=1) == _lib.ERR_SHAPE
+    assert wt(Wq=MISALIGNED) == _lib.ERR_ALIGN
+    assert wt(Ws=MISALIGNED) == _lib.ERR_ALIGN
+
+
+def test_gemm_mx_errors():
+    def g(Aq=FAKE, As=FAKE, Bq=FAKE, Bs=FAKE, M=4, N=4, K=8, dA=None, W=None, wdt=1, ldw=4,
+          Y=FAKE, ldy=4):
+        p = ctypes.byref(dA) if dA is not None else None
+        return L.fp4lin_gemm_mx(Aq, As, Bq, Bs, M, N, K, p, W, wdt, ldw, Y, ldy, None)
+
+    assert g(As=None) == _lib.ERR_NULL
+    assert g(Bs=None) == _lib.ERR_NULL
+    assert g(M=0) == _lib.ERR_SHAPE
+    assert g(ldy=3) == _lib.ERR_SHAPE
+    assert g(M=2 ** 26, K=2 ** 6) == _lib.ERR_SHAPE   # (M+1)*packed_ld(K) >= 2^31
+    assert g(As=MISALIGNED) == _lib.ERR_ALIGN
+    assert g(Bs=MISALIGNED) == _lib.ERR_ALIGN
+    c = _lib.Coo(FAKE, FAKE, FAKE, FAKE, 10)
+    assert g(dA=c, W=None) == _lib.ERR_NULL
+    assert g(dA=c, W=FAKE, wdt=5) == _lib.ERR_DTYPE
+    assert g(dA=c, W=FAKE, ldw=3) == _lib.ERR_SHAPE
+
+
 def forward(A=FAKE, W=FAKE, dt=1, M=4, K=8, N=4, lda=8, ldw=4, q=0.5, Y=FAKE, ldy=4, ws=FAKE,
             wsb=1 << 30):
     return L.fp4lin_forward(A, W, dt, M, K, N, lda, ldw, q, Y, ldy, ws, wsb, None)
