@@ -9,6 +9,7 @@ them on the stream the kernels run on, for the per-stage breakdown and the
 per-kernel rooflines.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--pass forward|dgrad|wgrad]
+                    [--quant token|mx]
 
 Prints one JSON line. Inputs are seeded synthetic matrices (workloads module),
 already resident in HBM when the timed region starts.
@@ -17,6 +18,11 @@ already resident in HBM when the timed region starts.
 step being its three public calls: dX = Q(dY) Q(W)^T (quantize_act on dY and on
 W rows, then gemm) or dW = Q(A)^T Q(dY) (quantize_weight on A and on dY, then
 gemm with K' = M).
+
+--quant mx times the micro-scaled variant of the forward instead: each step is
+the five public calls outlier_select, quantize_act_mx, quantize_weight_mx,
+gemm_mx and sparse_add (32-code blocks along K with E8M0 scales, the block
+scales applied by the matrix core).
 """
 from __future__ import annotations
 
@@ -56,6 +62,8 @@ def parse():
                    help="also run a plain 1 GiB device copy (for PMC byte calibration)")
     p.add_argument("--pass", dest="which", default="forward",
                    choices=("forward", "dgrad", "wgrad"))
+    p.add_argument("--quant", default="token", choices=("token", "mx"),
+                   help="token: the vector-wise forward (default); mx: the micro-scaled one")
     return p.parse_args()
 
 
@@ -128,6 +136,170 @@ class Step:
                                     ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(),
                                     self.stream)
         assert s == 0, s
+
+
+class MxStep(Step):
+    """The micro-scaled forward as its five public calls: the select's outputs
+    and the packed codes live in the forward layout, the E8M0 scale rows in
+    their own buffers."""
+
+    def __init__(self, ql, A, W, q, stream):
+        super().__init__(ql, A, W, q, stream)
+        nb = ql.mx_scales_ld(self.K)   # scale bytes per row (stored step-major)
+        self.As_t = self.torch.empty((self.M * nb,), dtype=self.torch.uint8, device=A.device)
+        self.Ws_t = self.torch.empty((self.N * nb,), dtype=self.torch.uint8, device=A.device)
+        self.As = ctypes.c_void_p(self.As_t.data_ptr())
+        self.Ws = ctypes.c_void_p(self.Ws_t.data_ptr())
+
+    def quant_a(self):
+        s = self.lib.fp4lin_quantize_act_mx(self.A, self.dt, self.M, self.K, self.lda, self.tau,
+                                            self.Aq, self.As, self.stream)
+        assert s == 0, s
+
+    def quant_w(self):
+        s = self.lib.fp4lin_quantize_weight_mx(self.W, self.dt, self.K, self.N, self.ldw,
+                                               self.Wq, self.Ws, self.stream)
+        assert s == 0, s
+
+    def gemm(self):
+        s = self.lib.fp4lin_gemm_mx(self.Aq, self.As, self.Wq, self.Ws, self.M, self.N, self.K,
+                                    None, None, self.dt, 0, ctypes.c_void_p(self.Y.data_ptr()),
+                                    self.N, self.stream)
+        assert s == 0, s
+
+    def step(self):
+        self.select(); self.quant_a(); self.quant_w(); self.gemm(); self.sparse()
+
+
+def run_forward_mx(args):
+    """One JSON line for --quant mx: the micro-scaled forward, step = five calls."""
+    import torch
+    import quantized_linear_layer_amd as ql
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    L = wl.make_layer(args.workload, seed=args.seed)
+    A, W = upload(L.A, dev), upload(L.W, dev)
+    stream = torch.cuda.current_stream()
+    st = MxStep(ql, A, W, L.q, stream)
+    M, K, N = L.M, L.K, L.N
+    flops = 2.0 * M * N * K
+    for _ in range(max(args.warmup, 1)):
+        st.step()
+    torch.cuda.synchronize()
+    nnz = int(st.ws[st.offsets.row_ptr + 4 * M: st.offsets.row_ptr + 4 * M + 4]
+              .cpu().numpy().view(np.int32)[0])
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    f0.record(stream)
+    for _ in range(args.steps):
+        st.step()
+    f1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    event_ms = f0.elapsed_time(f1) / args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        st.select(); e[1].record(stream)
+        st.quant_a(); e[2].record(stream)
+        st.quant_w(); e[3].record(stream)
+        st.gemm(); e[4].record(stream)
+        st.sparse(); e[5].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(STAGES)}
+    if args.copy_calib:
+        copy_calibration(dev)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    e = 2 if L.A.dtype == wl.BF16 else 4
+    ldq = ql.packed_ld(K)
+    nb = ql.mx_scales_ld(K)
+    # algorithmic bytes: as the token-wise forward, with a scale row of nb
+    # bytes per row of A and column of W instead of one float
+    hbm_bytes = {
+        "select": 2 * e * M * K + 12 * nnz + 4 * (M + 1),
+        "quant_a": e * M * K + M * (ldq + nb),
+        "quant_w": e * K * N + N * (ldq + nb),
+        "gemm": (M + N) * (ldq + nb) + 4 * M * N,
+        "sparse": 8 * M * N + 12 * nnz + 4 * (M + 1) + e * N * min(K, nnz),
+    }
+    kernels = {}
+    for name in STAGES:
+        gbs = hbm_bytes[name] / (stage_ms[name] * 1e-3) / 1e9
+        kernels[name] = {"ms": round(stage_ms[name], 5), "bytes": int(hbm_bytes[name]),
+                         "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "bound": "hbm"}
+    gemm_tf = flops / (stage_ms["gemm"] * 1e-3) / 1e12
+    kernels["gemm"].update({"bound": "mfma", "TFLOP/s": round(gemm_tf, 1),
+                            "mfma_frac": round(gemm_tf / FP4_PEAK_TFLOPS, 4)})
+    sp_tf = 2.0 * nnz * N / (stage_ms["sparse"] * 1e-3) / 1e12
+    kernels["sparse"].update({"bound": "alu", "fp32_TFLOP/s": round(sp_tf, 2),
+                              "alu_frac": round(sp_tf / VALU_FP32_PEAK_TFLOPS, 4)})
+    dom = max(STAGES, key=lambda n: stage_ms[n])
+    traffic = None
+    tname = {"gemm": f"traffic_gemm_{args.workload}_mx.json",
+             "sparse": f"traffic_sparse_{args.workload}.json"}.get(dom)
+    if tname and os.path.exists(os.path.join(ROOT, "profiles", tname)):
+        tr = json.load(open(os.path.join(ROOT, "profiles", tname)))
+        if tr.get("source_sha256") == file_sha(os.path.join(ROOT, tr["source"])):
+            traffic = tr.get("bytes_per_launch")
+    if dom == "sparse":
+        roof = {"bound": "alu", "kernel": "sparse_add_kernel", "achieved": round(sp_tf, 2),
+                "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(sp_tf / VALU_FP32_PEAK_TFLOPS, 4), "traffic": traffic}
+    elif dom == "gemm":
+        roof = {"bound": "mfma", "kernel": "fp4_gemm_kernel (block scales)",
+                "achieved": round(gemm_tf, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gemm_tf / FP4_PEAK_TFLOPS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GB/s"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["hbm_frac"],
+                "traffic": None}
+    out = {
+        "metric": "FP4 linear fwd effective TFLOP/s, micro-scaled operands (MXFP4, 32-code "
+                  "E8M0 blocks; 1 GPU)",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4", "data": "synthetic",
+        "config": {"workload": f"{args.workload}_mx", "M": M, "K": K, "N": N, "q": L.q,
+                   "input_dtype": L.A.dtype, "output_dtype": "f32", "seed": args.seed,
+                   "nnz_dA": nnz, "block": 32},
+        "pct_fp4_peak": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
+        "event_ms": round(event_ms, 5),
+        "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_mx(L, args.cpu_rows or 256)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_mx(L, rows):
+    """The oracle's micro-scaled forward on the first `rows` rows of A (tau from
+    those rows; W quantized whole), timed on the host cores."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas_threads = 1
+    rows = min(rows, L.M)
+    t0 = time.perf_counter()
+    O.forward_mx(L.A.f32[:rows], L.W.f32, L.q)
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * L.N * L.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{rows} of {L.M} rows of A with the full {L.K}x{L.N} W, q={L.q}: the "
+                      f"oracle's micro-scaled forward (tau of the sample, clamp + COO, block "
+                      f"quantization of A and W, block-scaled float64 product, sparse term) took "
+                      f"{t:.2f} s; host affinity {len(os.sched_getaffinity(0))} cpus, BLAS "
+                      f"threads {blas_threads}"}
 
 
 class BackwardStep:
@@ -360,7 +532,13 @@ def main():
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if args.which != "forward":
+        if args.quant != "token":
+            print("--quant mx applies to the forward only", file=sys.stderr)
+            sys.exit(2)
         run_backward(args)
+        return
+    if args.quant == "mx":
+        run_forward_mx(args)
         return
     import torch
     import quantized_linear_layer_amd as ql

@@ -236,8 +236,12 @@ fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtyp
  * 6 * 2^e >= the block's max |x| (so no element is clipped), stored as the
  * byte e + 127; each element is |x| / 2^e (exact) rounded to the nearest E2M1
  * value, ties away from zero, sign copied. Padding codes are zero and a block
- * with no non-zero element has the byte 0. A scale row holds
- * fp4lin_mx_scales_ld(K) = fp4lin_packed_ld(K) / 16 bytes. */
+ * with no non-zero element has the byte 0. Each row (of A) or column (of W)
+ * has fp4lin_mx_scales_ld(K) = fp4lin_packed_ld(K) / 16 scale bytes, stored
+ * step-major for the GEMM: for each K step s of 128 codes, one 32-bit word per
+ * row holds the bytes of blocks 4s .. 4s+3 (low byte first), and the words of
+ * consecutive rows are adjacent. With R rows, the byte of block b of row i is
+ * at offset (b / 4) * 4R + 4i + b % 4 (R * mx_scales_ld(K) bytes in all). */
 
 /* Bytes per row of E8M0 block scales for rows of L codes, or -1 if L < 1. */
 int64_t fp4lin_mx_scales_ld(int64_t L);
@@ -247,7 +251,7 @@ int64_t fp4lin_mx_scales_ld(int64_t L);
  *   X        device, M x K, dtype dt, leading dimension ldx
  *   tau      device, 1 float, or NULL for no clamping
  *   Xq       device, M x fp4lin_packed_ld(K) bytes (output, padding zeroed)
- *   Xs       device, M x fp4lin_mx_scales_ld(K) bytes (output)
+ *   Xs       device, M * fp4lin_mx_scales_ld(K) bytes, step-major (output)
  * Xq and Xs must be 16-byte aligned.
  * Errors: NULL, SHAPE, DTYPE, ALIGN, LAUNCH. */
 fp4lin_status fp4lin_quantize_act_mx(const void* X, fp4lin_dtype dt, int64_t M, int64_t K,
@@ -258,7 +262,7 @@ fp4lin_status fp4lin_quantize_act_mx(const void* X, fp4lin_dtype dt, int64_t M, 
  * K x N weight, written N-major like fp4lin_quantize_weight. Needs no workspace.
  *   W        device, K x N, dtype dt, leading dimension ldw
  *   Wq       device, N x fp4lin_packed_ld(K) bytes (output, padding zeroed)
- *   Ws       device, N x fp4lin_mx_scales_ld(K) bytes (output)
+ *   Ws       device, N * fp4lin_mx_scales_ld(K) bytes, step-major (output)
  * Wq and Ws must be 16-byte aligned; K must be below 2^23 (tiles of 128 codes
  * along K index the second grid dimension), else FP4LIN_ERR_SHAPE.
  * Errors: NULL, SHAPE, DTYPE, ALIGN, LAUNCH. */
@@ -273,8 +277,9 @@ fp4lin_status fp4lin_quantize_weight_mx(const void* W, fp4lin_dtype dt, int64_t 
  *            + s[i,j]                                  (as in fp4lin_gemm)
  * with no separate scale epilogue. Each block's dot product and its scaling
  * are exact; the sum over blocks is rounded to fp32.
- *   Aq, As   device, M x packed_ld(K) bytes, M x mx_scales_ld(K) bytes
- *   Bq, Bs   device, N x packed_ld(K) bytes (N-major), N x mx_scales_ld(K)
+ *   Aq, As   device, M x packed_ld(K) bytes; M * mx_scales_ld(K) bytes
+ *   Bq, Bs   device, N x packed_ld(K) bytes (N-major); N * mx_scales_ld(K)
+ *            (scales step-major, as the quantizers write them)
  *   dA, W, wdt, ldw, Y, ldy   as in fp4lin_gemm
  * Aq, Bq, As and Bs must be 16-byte aligned; the limits of fp4lin_gemm apply.
  * Errors: NULL, SHAPE, DTYPE, ALIGN, LAUNCH. */

@@ -285,21 +285,23 @@ def mx_scales_ld(L: int) -> int:
 
 
 def quantize_act_mx(X, tau=None, stream=None):
-    """Micro-scaled: returns (Xq uint8 M x packed_ld(K), Xs uint8 M x mx_scales_ld(K))."""
+    """Micro-scaled: returns (Xq uint8 M x packed_ld(K), Xs uint8 (steps, M, 4)),
+    the scales step-major: Xs[s, i, j] is the byte of block 4s + j of row i."""
     torch = _torch()
     M, K, _ = _matrix(X, "X")
     Xq = _empty((M, packed_ld(K)), torch.uint8, X.device)
-    Xs = _empty((M, mx_scales_ld(K)), torch.uint8, X.device)
+    Xs = _empty((mx_scales_ld(K) // 4, M, 4), torch.uint8, X.device)
     fp4lin_quantize_act_mx(X, tau, Xq, Xs, stream)
     return Xq, Xs
 
 
 def quantize_weight_mx(W, stream=None):
-    """Micro-scaled: returns (Wq uint8 N x packed_ld(K), Ws uint8 N x mx_scales_ld(K))."""
+    """Micro-scaled: returns (Wq uint8 N x packed_ld(K), Ws uint8 (steps, N, 4)),
+    the scales step-major as for quantize_act_mx, per column of W."""
     torch = _torch()
     K, N, _ = _matrix(W, "W")
     Wq = _empty((N, packed_ld(K)), torch.uint8, W.device)
-    Ws = _empty((N, mx_scales_ld(K)), torch.uint8, W.device)
+    Ws = _empty((mx_scales_ld(K) // 4, N, 4), torch.uint8, W.device)
     fp4lin_quantize_weight_mx(W, Wq, Ws, stream)
     return Wq, Ws
 

@@ -225,13 +225,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
       bf[fn] = v8i{int(u.x), int(u.y), int(u.z), int(u.w), 0, 0, 0, 0};
     }
   };
-  // Block scales (kMx). The E8M0 bytes of a row's blocks 4kt .. 4kt+3 (the
-  // 128 codes of K step kt) are one aligned 32-bit word of its scale row
-  // (ldq / 16 bytes). Lane half h supplies codes 32h .. 32h+31 of each 64-code
-  // sub-step, i.e. block 4kt + 2kk + h in sub-step kk: the word shifted right
-  // by 8h, byte kk*2 of it picked by the instruction's op_sel. Rows past M (N)
-  // read the scale word as zero, beside their zero codes. The words of step kt
-  // go into slot kt mod 3 of a register ring, loaded three steps ahead.
+  // Block scales (kMx), stored step-major: for K step kt (128 codes, blocks
+  // 4kt .. 4kt+3) each row has one 32-bit word at 4 * (kt * rows + row), so
+  // the 32 rows of a fragment read 128 contiguous bytes. Lane half h supplies
+  // codes 32h .. 32h+31 of each 64-code sub-step, i.e. block 4kt + 2kk + h in
+  // sub-step kk: the word shifted right by 8h, byte kk*2 of it picked by the
+  // instruction's op_sel. Rows past M (N) take the scales of the last row:
+  // their codes are zero, so any finite scale gives zero. The words of step
+  // kt go into slot kt mod 3 of a register ring, loaded three steps ahead.
   constexpr int NS = kMx ? FM + FN : 0;
   const int nblk = ldq / 16;
   const __amdgpu_buffer_rsrc_t rsSA = __builtin_amdgcn_make_buffer_rsrc(
@@ -242,10 +243,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   if constexpr (kMx) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
-      sc_off[fm] = (m0 + a_row[fm] < M) ? (m0 + a_row[fm]) * nblk : M * nblk;
+      sc_off[fm] = 4 * ((m0 + a_row[fm] < M) ? m0 + a_row[fm] : M - 1);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
-      sc_off[FM + fn] = (n0 + b_row[fn] < N) ? (n0 + b_row[fn]) * nblk : N * nblk;
+      sc_off[FM + fn] = 4 * ((n0 + b_row[fn] < N) ? n0 + b_row[fn] : N - 1);
   }
   const int hshift = (lane >> 5) * 8;
   uint32_t sc0[NS > 0 ? NS : 1], sc1[NS > 0 ? NS : 1], sc2[NS > 0 ? NS : 1];
@@ -255,7 +256,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
     if constexpr (kMx) {
 #pragma unroll
       for (int f = 0; f < NS; ++f)
-        dst[f] = __builtin_amdgcn_raw_buffer_load_b32(f < FM ? rsSA : rsSB, sc_off[f] + kt * 4, 0, 0);
+        dst[f] = __builtin_amdgcn_raw_buffer_load_b32(f < FM ? rsSA : rsSB,
+                                                      sc_off[f] + kt * 4 * (f < FM ? M : N), 0, 0);
     }
   };
   // kk_c: the sub-step (0 or 1) as a type, so that op_sel is a constant

@@ -14,6 +14,12 @@
 // are clamped to +-tau first. The GEMM takes the bytes as the matrix core's
 // block-scale operands (gemm.hip).
 //
+// Scale layout (step-major): for each K step of 128 codes, one 32-bit word per
+// row (per column of W) holds the bytes of its blocks 4s .. 4s+3, low byte
+// first, and the words of consecutive rows are adjacent: the byte of block b
+// of row i (of R rows) is at (b / 4) * 4R + 4i + b % 4. The GEMM then reads the
+// scales of 32 consecutive rows for one step as 128 contiguous bytes.
+//
 // Rows (activations): one thread per 8-code chunk of a padded row, so four
 //   consecutive lanes hold one block and its max is two lane exchanges away;
 //   each thread writes its 8 codes as one 32-bit word and the first lane of a
@@ -66,7 +72,7 @@ template <class In, bool kFast>
 __global__ __launch_bounds__(kMxThreads) void quantize_rows_mx_kernel(
     const typename In::T* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ tau_p, uint8_t* __restrict__ Xq, int64_t ldq,
-    uint8_t* __restrict__ Xs, int64_t lds) {
+    uint8_t* __restrict__ Xs) {
   const float tau = tau_p ? *tau_p : __builtin_huge_valf();
   const int64_t cpr = ldq / 4;
   const int64_t total = M * cpr;
@@ -89,7 +95,8 @@ __global__ __launch_bounds__(kMxThreads) void quantize_rows_mx_kernel(
     for (int i = 0; i < 8; ++i)
       word |= (mx_magnitude(ax[i], e) | (In::sign_bit(v.v[i]) << 3)) << (4 * i);
     *reinterpret_cast<uint32_t*>(Xq + r * ldq + c * 4) = word;
-    if ((c & 3) == 0) Xs[r * lds + c / 4] = uint8_t(e + 127);
+    // chunk c: block c / 4 = 4 * (c / 16) + (c / 4) % 4
+    if ((c & 3) == 0) Xs[(c / 16) * 4 * M + 4 * r + ((c / 4) & 3)] = uint8_t(e + 127);
   }
 }
 
@@ -103,7 +110,7 @@ constexpr int kMxTN = 128;  // columns per tile
 template <class In, bool kAligned>
 __global__ __launch_bounds__(kMxThreads) void quantize_cols_mx_kernel(
     const typename In::T* __restrict__ W, int64_t K, int64_t N, int64_t ldw,
-    uint8_t* __restrict__ Wq, int64_t ldq, uint8_t* __restrict__ Ws, int64_t lds) {
+    uint8_t* __restrict__ Wq, int64_t ldq, uint8_t* __restrict__ Ws) {
   const int t = threadIdx.x;
   const int kg = t & 15, g = t >> 4;
   const int64_t n0 = int64_t(blockIdx.x) * kMxTN;
@@ -139,7 +146,8 @@ __global__ __launch_bounds__(kMxThreads) void quantize_cols_mx_kernel(
       word |= (mx_magnitude(fabsf(In::widen(v[u].v[j])), e[j]) | (In::sign_bit(v[u].v[j]) << 3))
               << (4 * u);
     *reinterpret_cast<uint32_t*>(Wq + (c + j) * ldq + kr / 2) = word;
-    if ((kg & 3) == 0) Ws[(c + j) * lds + kr / 32] = uint8_t(e[j] + 127);
+    // rows kr .. kr+7: block kr / 32 of K step kr / 128 (the tile's step by)
+    if ((kg & 3) == 0) Ws[(kr / 128) * 4 * N + 4 * (c + j) + ((kr / 32) & 3)] = uint8_t(e[j] + 127);
   }
 }
 
@@ -158,10 +166,10 @@ hipError_t run_rows_mx(const void* X, int64_t M, int64_t K, int64_t ldx, const f
   const unsigned grid = mx_row_grid(M * (ldq / 4));
   if (fast)
     quantize_rows_mx_kernel<In, true><<<grid, kMxThreads, 0, stream>>>(x, M, K, ldx, tau, Xq, ldq,
-                                                                       Xs, ldq / 16);
+                                                                       Xs);
   else
     quantize_rows_mx_kernel<In, false><<<grid, kMxThreads, 0, stream>>>(x, M, K, ldx, tau, Xq,
-                                                                        ldq, Xs, ldq / 16);
+                                                                        ldq, Xs);
   return hipGetLastError();
 }
 
@@ -174,11 +182,10 @@ hipError_t run_cols_mx(const void* Wp, int64_t K, int64_t N, int64_t ldw, uint8_
                        ((ldw * In::kBytes) % 16 == 0);
   const dim3 grid(unsigned((N + kMxTN - 1) / kMxTN), unsigned((ldq * 2) / kMxTK));
   if (aligned)
-    quantize_cols_mx_kernel<In, true><<<grid, kMxThreads, 0, stream>>>(W, K, N, ldw, Wq, ldq, Ws,
-                                                                       ldq / 16);
+    quantize_cols_mx_kernel<In, true><<<grid, kMxThreads, 0, stream>>>(W, K, N, ldw, Wq, ldq, Ws);
   else
     quantize_cols_mx_kernel<In, false><<<grid, kMxThreads, 0, stream>>>(W, K, N, ldw, Wq, ldq,
-                                                                        Ws, ldq / 16);
+                                                                        Ws);
   return hipGetLastError();
 }
 

@@ -140,3 +140,33 @@ def test_full_llama13b_qkv_wgrad(ql):
     err = O.rel_fro(got, want_dW)
     log(f"[full] wgrad: dW rel_fro on {rows.size} rows {err:.3e}")
     assert err <= Y_TOL, err
+
+
+def test_full_llama7b_ffn_up_mx(ql):
+    """The micro-scaled forward at the benchmark's size, as bench.py --quant mx
+    runs it (select, quantize_act_mx, quantize_weight_mx, gemm_mx with the
+    compensation): codes and scale bytes bit-exact over the whole arrays, Y on
+    sampled rows."""
+    import torch
+    L = wl.make_layer("llama7b_ffn_up")
+    log(f"[full] {L.name} (micro-scaled): GPU calls")
+    A, W = to_device(L.A), to_device(L.W)
+    tau, coo = ql.outlier_select(A, L.q)
+    Aq, As = ql.quantize_act_mx(A, tau)
+    Wq, Ws = ql.quantize_weight_mx(W)
+    Y = ql.gemm_mx(Aq, As, Wq, Ws, L.M, L.N, L.K, coo, W)
+    torch.cuda.synchronize()
+    rows = sample_rows(L.M, seed=7)
+    log(f"[full] {L.name} (micro-scaled): oracle")
+    want, mag, otau, delta, qa, qw = O.forward_mx(L.A.f32, L.W.f32, L.q, rows=rows)
+    assert_bits_equal(host(tau)[0], otau, "tau")
+    # step-major (steps, rows, 4) scale bytes as rows x blocks
+    rows_of = lambda a, R: np.ascontiguousarray(np.asarray(a).reshape(-1, R, 4)
+                                                .transpose(1, 0, 2).reshape(R, -1))
+    assert_bits_equal(rows_of(host(As), L.M), qa[1], "A scale bytes")
+    assert_bits_equal(host(Aq), qa[0], "A codes")
+    assert_bits_equal(rows_of(host(Ws), L.N), qw[1], "W scale bytes")
+    assert_bits_equal(host(Wq), qw[0], "W codes")
+    err = O.rel_fro(host(Y[torch.as_tensor(rows, device=Y.device)]), want)
+    log(f"[full] {L.name} (micro-scaled): Y rel err {err:.3g}")
+    assert err <= Y_TOL

@@ -39,6 +39,19 @@ def upload(a):
     return torch().from_numpy(np.ascontiguousarray(a)).to("cuda:0")
 
 
+def scales_to_rows(dev_scales, rows):
+    """The library's step-major scale bytes (steps, rows, 4) as rows x blocks."""
+    a = np.asarray(dev_scales).reshape(-1, rows, 4)
+    return np.ascontiguousarray(a.transpose(1, 0, 2).reshape(rows, -1))
+
+
+def scales_to_steps(row_bytes):
+    """Rows x blocks scale bytes in the library's step-major layout."""
+    a = np.asarray(row_bytes, np.uint8)
+    R, nb = a.shape
+    return np.ascontiguousarray(a.reshape(R, nb // 4, 4).transpose(1, 0, 2))
+
+
 def tau_tensor(tau):
     t = torch()
     return None if tau is None else t.tensor([float(tau)], dtype=t.float32, device="cuda:0")
@@ -54,7 +67,7 @@ def check_act_mx(ql, X: wl.Matrix, tau=None, ld=None):
     Xq, Xs = ql.quantize_act_mx(Xd, tau_tensor(tau))
     torch().cuda.synchronize()
     want_q, want_s, _, _ = O.quantize_act_mx(X.f32, tau)
-    assert_bits_equal(host(Xs), want_s, "scale bytes")
+    assert_bits_equal(scales_to_rows(host(Xs), X.shape[0]), want_s, "scale bytes")
     assert_bits_equal(host(Xq), want_q, "packed codes")
 
 
@@ -65,7 +78,7 @@ def check_weight_mx(ql, W: wl.Matrix, ld=None):
     Wq, Ws = ql.quantize_weight_mx(Wd)
     torch().cuda.synchronize()
     want_q, want_s, _, _ = O.quantize_weight_mx(W.f32)
-    assert_bits_equal(host(Ws), want_s, "scale bytes")
+    assert_bits_equal(scales_to_rows(host(Ws), W.shape[1]), want_s, "scale bytes")
     assert_bits_equal(host(Wq), want_q, "packed codes")
 
 
@@ -156,8 +169,9 @@ def run_gemm_mx(ql, codesA, eA, codesB, eB, K, delta=None, W=None):
                             upload(pad(delta.val32, np.float32)),
                             upload(np.asarray(delta.row_ptr, np.int32)))
         Wd = to_device(W)
-    Y = ql.gemm_mx(upload(O.pack_rows(codesA)), upload(O.mx_scale_bytes(eA)),
-                   upload(O.pack_rows(codesB)), upload(O.mx_scale_bytes(eB)), M, N, K, coo, Wd)
+    Y = ql.gemm_mx(upload(O.pack_rows(codesA)), upload(scales_to_steps(O.mx_scale_bytes(eA))),
+                   upload(O.pack_rows(codesB)), upload(scales_to_steps(O.mx_scale_bytes(eB))),
+                   M, N, K, coo, Wd)
     torch().cuda.synchronize()
     return host(Y).astype(np.float64)
 
@@ -268,7 +282,7 @@ def test_layer_mx_workloads(ql, name):
     want, mag, otau, delta, qa, qw = O.forward_mx(L.A.f32, L.W.f32, L.q)
     assert_bits_equal(host(tau)[0], otau, "tau")
     assert_bits_equal(host(Aq), qa[0], "A codes")
-    assert_bits_equal(host(As), qa[1], "A scale bytes")
+    assert_bits_equal(scales_to_rows(host(As), L.M), qa[1], "A scale bytes")
     assert_bits_equal(host(Wq), qw[0], "W codes")
-    assert_bits_equal(host(Ws), qw[1], "W scale bytes")
+    assert_bits_equal(scales_to_rows(host(Ws), L.N), qw[1], "W scale bytes")
     assert O.rel_fro(host(Y), want) <= Y_TOL
