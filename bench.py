@@ -241,7 +241,7 @@ def run_forward_mx(args):
     dom = max(STAGES, key=lambda n: stage_ms[n])
     traffic = None
     tname = {"gemm": f"traffic_gemm_{args.workload}_mx.json",
-             "sparse": f"traffic_sparse_{args.workload}.json"}.get(dom)
+             "sparse": f"traffic_sparse_{args.workload}_mx.json"}.get(dom)
     if tname and os.path.exists(os.path.join(ROOT, "profiles", tname)):
         tr = json.load(open(os.path.join(ROOT, "profiles", tname)))
         if tr.get("source_sha256") == file_sha(os.path.join(ROOT, tr["source"])):
