@@ -22,7 +22,9 @@ gemm with K' = M).
 --quant mx times the micro-scaled variant of the forward instead: each step is
 the five public calls outlier_select, quantize_act_mx, quantize_weight_mx,
 gemm_mx and sparse_add (32-code blocks along K with E8M0 scales, the block
-scales applied by the matrix core).
+scales applied by the matrix core). With --pass dgrad / wgrad it takes the
+micro-scaled quantizers and gemm_mx for the backward GEMMs (blocks along the
+reduction: N for dgrad, M for wgrad).
 """
 from __future__ import annotations
 
@@ -308,10 +310,10 @@ class BackwardStep:
     dgrad: dX (M x K) = Q(dY) Q(W)^T, dY and W quantized per row over N.
     wgrad: dW (K x N) = Q(A)^T Q(dY), A and dY quantized per column over M."""
 
-    def __init__(self, ql, which, A, W, dY, stream):
+    def __init__(self, ql, which, A, W, dY, stream, mx=False):
         import torch
         lib = ql.lib()
-        self.lib, self.which = lib, which
+        self.lib, self.which, self.mx = lib, which, mx
         M, K = A.shape
         N = W.shape[1]
         dt = ql.BF16 if A.dtype == torch.bfloat16 else ql.F32
@@ -329,9 +331,16 @@ class BackwardStep:
             ops = [(A, M, K), (dY, M, N)]
         Mo, No, Ko = self.shape
         ldq = ql.packed_ld(Ko)
+        nb = ql.mx_scales_ld(Ko)
         self.ops = []
         for X, r, c in ops:
-            if which == "dgrad":
+            if mx:
+                # micro-scaled: codes plus nb E8M0 bytes per packed row, no workspace
+                rows = r if which == "dgrad" else c
+                q = torch.empty((rows, ldq), dtype=torch.uint8, device=dev)
+                sc = torch.empty((rows * nb,), dtype=torch.uint8, device=dev)
+                self.ops.append((P(X.data_ptr()), r, c, X.stride(0), q, sc, None))
+            elif which == "dgrad":
                 q = torch.empty((r, ldq), dtype=torch.uint8, device=dev)
                 sc = torch.empty((r,), dtype=torch.float32, device=dev)
                 self.ops.append((P(X.data_ptr()), r, c, X.stride(0), q, sc, None))
@@ -346,7 +355,13 @@ class BackwardStep:
     def quant(self, i):
         X, r, c, ld, q, sc, ws = self.ops[i]
         P = ctypes.c_void_p
-        if self.which == "dgrad":
+        if self.mx and self.which == "dgrad":
+            st = self.lib.fp4lin_quantize_act_mx(X, self.dt, r, c, ld, None, P(q.data_ptr()),
+                                                 P(sc.data_ptr()), self.stream)
+        elif self.mx:
+            st = self.lib.fp4lin_quantize_weight_mx(X, self.dt, r, c, ld, P(q.data_ptr()),
+                                                    P(sc.data_ptr()), self.stream)
+        elif self.which == "dgrad":
             st = self.lib.fp4lin_quantize_act(X, self.dt, r, c, ld, None, P(q.data_ptr()),
                                               P(sc.data_ptr()), self.stream)
         else:
@@ -359,7 +374,8 @@ class BackwardStep:
         P = ctypes.c_void_p
         (_, _, _, _, qa, sa, _), (_, _, _, _, qb, sb, _) = self.ops
         Mo, No, Ko = self.shape
-        st = self.lib.fp4lin_gemm(P(qa.data_ptr()), P(sa.data_ptr()), P(qb.data_ptr()),
+        gemm = self.lib.fp4lin_gemm_mx if self.mx else self.lib.fp4lin_gemm
+        st = gemm(P(qa.data_ptr()), P(sa.data_ptr()), P(qb.data_ptr()),
                                   P(sb.data_ptr()), Mo, No, Ko, None, None, self.dt, 0,
                                   P(self.out.data_ptr()), No, self.stream)
         assert st == 0, st
@@ -380,7 +396,8 @@ def run_backward(args):
     dYh = wl.make_grad_output(L.M, L.N, seed=args.seed)
     A, W, dY = upload(L.A, dev), upload(L.W, dev), upload(dYh, dev)
     stream = torch.cuda.current_stream()
-    st = BackwardStep(ql, args.which, A, W, dY, stream)
+    mx = args.quant == "mx"
+    st = BackwardStep(ql, args.which, A, W, dY, stream, mx=mx)
     Mo, No, Ko = st.shape
     flops = 2.0 * Mo * No * Ko
     for _ in range(max(args.warmup, 1)):
@@ -412,7 +429,8 @@ def run_backward(args):
     e = 2 if L.A.dtype == wl.BF16 else 4
     ldq = ql.packed_ld(Ko)
     # algorithmic bytes of the quantizers: operand read once, codes and scales written
-    qbytes = [e * r * c + (r if args.which == "dgrad" else c) * (ldq + 4)
+    sbytes = ql.mx_scales_ld(Ko) if mx else 4   # scale bytes per packed row
+    qbytes = [e * r * c + (r if args.which == "dgrad" else c) * (ldq + sbytes)
               for (_, r, c, _, _, _, _) in st.ops]
     kernels = {"quant_0": {"ms": round(stage_ms["quant_0"], 5), "bytes": int(qbytes[0]),
                            "GB/s": round(qbytes[0] / (stage_ms["quant_0"] * 1e-3) / 1e9, 1),
@@ -423,7 +441,8 @@ def run_backward(args):
                "gemm": {"ms": round(stage_ms["gemm"], 5), "TFLOP/s": round(gemm_tf, 1),
                         "mfma_frac": round(gemm_tf / FP4_PEAK_TFLOPS, 4), "bound": "mfma"}}
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_gemm_{args.workload}_{args.which}.json")
+    tag = f"{args.workload}_{args.which}" + ("_mx" if mx else "")
+    tfile = os.path.join(ROOT, "profiles", f"traffic_gemm_{tag}.json")
     if os.path.exists(tfile):
         tr = json.load(open(tfile))
         if tr.get("source_sha256") == file_sha(os.path.join(ROOT, tr["source"])):
@@ -431,27 +450,30 @@ def run_backward(args):
     value = flops / (ms_per_step * 1e-3) / 1e12
     what = {"dgrad": "dX = Q(dY) Q(W)^T", "wgrad": "dW = Q(A)^T Q(dY)"}[args.which]
     out = {
-        "metric": f"FP4 linear {args.which} effective TFLOP/s ({what}, 1 GPU)",
+        "metric": f"FP4 linear {args.which} effective TFLOP/s ({what}"
+                  + (", micro-scaled operands" if mx else "") + ", 1 GPU)",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp4", "data": "synthetic",
-        "config": {"workload": f"{args.workload}_{args.which}", "M": L.M, "K": L.K, "N": L.N,
+        "config": {"workload": tag, "M": L.M, "K": L.K, "N": L.N,
                    "out_rows": Mo, "out_cols": No, "reduction": Ko, "input_dtype": L.A.dtype,
                    "output_dtype": "f32", "seed": args.seed},
         "pct_fp4_peak": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
         "event_ms": round(event_ms, 5),
         "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()},
-        "roofline": {"bound": "mfma", "kernel": "fp4_gemm_kernel", "achieved": round(gemm_tf, 2),
+        "roofline": {"bound": "mfma",
+                     "kernel": "fp4_gemm_kernel" + (" (block scales)" if mx else ""),
+                     "achieved": round(gemm_tf, 2),
                      "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tf / FP4_PEAK_TFLOPS, 4), "traffic": traffic},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_backward(args.which, L, dYh, args.cpu_rows or 64)
+        out["cpu_baseline"] = cpu_baseline_backward(args.which, L, dYh, args.cpu_rows or 64, mx)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_backward(which, L, dY, rows):
+def cpu_baseline_backward(which, L, dY, rows, mx=False):
     """The oracle's dgrad / wgrad on a sample of output rows (the quantization
     of both whole operands included), timed on the host cores."""
     import oracle as O
@@ -465,17 +487,18 @@ def cpu_baseline_backward(which, L, dY, rows):
     sample = np.arange(min(rows, nrows))
     t0 = time.perf_counter()
     if which == "dgrad":
-        O.dgrad(dY.f32, L.W.f32, rows=sample)
+        (O.dgrad_mx if mx else O.dgrad)(dY.f32, L.W.f32, rows=sample)
         red, cols = L.N, L.K
     else:
-        O.wgrad(L.A.f32, dY.f32, rows=sample)
+        (O.wgrad_mx if mx else O.wgrad)(L.A.f32, dY.f32, rows=sample)
         red, cols = L.M, L.N
     t = time.perf_counter() - t0
     flops = 2.0 * sample.size * cols * red
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
             "kind": "oracle",
             "sample": f"{sample.size} of {nrows} output rows of the {which} GEMM (both operands "
-                      f"quantized whole, then the float64 integer product of the sampled rows) "
+                      f"quantized whole{' in 32-blocks' if mx else ''}, then the float64 "
+                      f"{'block-scaled' if mx else 'integer'} product of the sampled rows) "
                       f"took {t:.2f} s; host affinity {len(os.sched_getaffinity(0))} cpus, "
                       f"BLAS threads {blas_threads}"}
 
@@ -532,9 +555,6 @@ def main():
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if args.which != "forward":
-        if args.quant != "token":
-            print("--quant mx applies to the forward only", file=sys.stderr)
-            sys.exit(2)
         run_backward(args)
         return
     if args.quant == "mx":

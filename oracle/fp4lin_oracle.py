@@ -464,6 +464,34 @@ def forward_mx(A32: np.ndarray, W32: np.ndarray, q: float, rows=None):
     return y, mag, tau, delta, qa, qw
 
 
+def dgrad_mx(dY32: np.ndarray, W32: np.ndarray, rows=None):
+    """Micro-scaled dX = Q(dY) Q(W)^T: dY and W both in blocks of 32 along N,
+    the reduction (readings R9 and R11), no clamp.
+
+    Returns (dX float64 or its listed rows, |term| sums, dY's and W's
+    (packed, scale bytes, codes, exponents))."""
+    qd = quantize_act_mx(dY32, None)
+    qw = quantize_act_mx(W32, None)
+    if rows is None:
+        rows = np.arange(qd[2].shape[0])
+    y, mag = mx_product(qd[2][rows], qd[3][rows], qw[2], qw[3])
+    return y, mag, qd, qw
+
+
+def wgrad_mx(A32: np.ndarray, dY32: np.ndarray, rows=None):
+    """Micro-scaled dW = Q(A)^T Q(dY): A and dY both in blocks of 32 along M,
+    the reduction (readings R10 and R11), no clamp.
+
+    Returns (dW float64 K x N or its listed rows, |term| sums, A's and dY's
+    (packed, scale bytes, codes, exponents), each packed along M)."""
+    qa = quantize_weight_mx(A32)
+    qd = quantize_weight_mx(dY32)
+    if rows is None:
+        rows = np.arange(qa[2].shape[0])
+    y, mag = mx_product(qa[2][rows], qa[3][rows], qd[2], qd[3])
+    return y, mag, qa, qd
+
+
 def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:
     """Relative Frobenius error ||x - ref|| / ||ref|| (0 when both are zero)."""
     x = np.asarray(x, dtype=np.float64)

@@ -286,3 +286,46 @@ def test_layer_mx_workloads(ql, name):
     assert_bits_equal(host(Wq), qw[0], "W codes")
     assert_bits_equal(scales_to_rows(host(Ws), L.N), qw[1], "W scale bytes")
     assert O.rel_fro(host(Y), want) <= Y_TOL
+
+
+# ---------------------------------------------------------------------------
+# the backward GEMMs on micro-scaled operands, through the public calls:
+# dgrad blocks along N (quantize_act_mx on dY and on W), wgrad blocks along M
+# (quantize_weight_mx on A and on dY, then gemm_mx with K' = M)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("M,K,N", [(1, 1, 1), (70, 33, 129), (300, 100, 520)])
+def test_dgrad_mx_public_calls(ql, dtype, M, K, N):
+    log(f"dgrad_mx {dtype} {M}x{K}x{N}")
+    rng = np.random.default_rng(M + 7 * K + 11 * N)
+    dY = wl.random_matrix(rng, M, N, dtype, scale=1e-3)
+    W = wl.random_matrix(rng, K, N, dtype, scale=0.02)
+    dq, ds = ql.quantize_act_mx(to_device(dY))
+    wq, wsc = ql.quantize_act_mx(to_device(W))
+    dX = ql.gemm_mx(dq, ds, wq, wsc, M, K, N)
+    torch().cuda.synchronize()
+    want, mag, qd, qw = O.dgrad_mx(dY.f32, W.f32)
+    assert_bits_equal(host(dq), qd[0], "dY codes")
+    assert_bits_equal(scales_to_rows(host(ds), M), qd[1], "dY scale bytes")
+    assert_bits_equal(host(wq), qw[0], "W codes")
+    assert_bits_equal(scales_to_rows(host(wsc), K), qw[1], "W scale bytes")
+    assert_within_accumulation_bound(host(dX).astype(np.float64), want, mag, N)
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("M,K,N", [(1, 1, 1), (129, 33, 70), (1000, 100, 300)])
+def test_wgrad_mx_public_calls(ql, dtype, M, K, N):
+    log(f"wgrad_mx {dtype} {M}x{K}x{N}")
+    rng = np.random.default_rng(M + 3 * K + 5 * N)
+    A = wl.random_matrix(rng, M, K, dtype, dist="t3")
+    dY = wl.random_matrix(rng, M, N, dtype, scale=1e-3)
+    aq, asc = ql.quantize_weight_mx(to_device(A))
+    dq, ds = ql.quantize_weight_mx(to_device(dY))
+    dW = ql.gemm_mx(aq, asc, dq, ds, K, N, M)
+    torch().cuda.synchronize()
+    want, mag, qa, qd = O.wgrad_mx(A.f32, dY.f32)
+    assert_bits_equal(host(aq), qa[0], "A codes")
+    assert_bits_equal(scales_to_rows(host(asc), K), qa[1], "A scale bytes")
+    assert_bits_equal(host(dq), qd[0], "dY codes")
+    assert_bits_equal(scales_to_rows(host(ds), N), qd[1], "dY scale bytes")
+    assert_within_accumulation_bound(host(dW).astype(np.float64), want, mag, M)

@@ -532,3 +532,37 @@ def test_mx_weight_blocks_run_along_k():
     assert diff[3, 1] == 3 and np.count_nonzero(diff) == 1
     assert np.array_equal(c0, c1)
     assert sb.shape == (6, O.packed_ld(100) // 16)
+
+
+def _mx_grid_exact(rng, R, C, along_rows):
+    """Values that the micro-scaled quantizer keeps exactly: grid values times a
+    power of two per 32-block along the reduction, each block reaching 6 * 2^e."""
+    grid = np.array(GRID)
+    v = grid[rng.integers(0, 8, (R, C))] * rng.choice([-1.0, 1.0], (R, C))
+    if along_rows:          # blocks along each row (C is the reduction)
+        nb = C // 32
+        e = rng.integers(-6, 6, (R, nb))
+        v.reshape(R, nb, 32)[:, :, 0] = 6.0
+        v = (v.reshape(R, nb, 32) * np.exp2(e)[:, :, None]).reshape(R, C)
+    else:                   # blocks along each column (R is the reduction)
+        nb = R // 32
+        e = rng.integers(-6, 6, (nb, C))
+        v.reshape(nb, 32, C)[:, 0, :] = 6.0
+        v = (v.reshape(nb, 32, C) * np.exp2(e)[:, None, :]).reshape(R, C)
+    return v.astype(np.float32)
+
+
+def test_mx_dgrad_wgrad_exact_on_grid():
+    """On block-exact inputs the micro-scaled backward products equal the plain
+    float64 products: dX = dY W^T (blocks along N) and dW = A^T dY (blocks along M)."""
+    rng = np.random.default_rng(11)
+    M, K, N = 64, 40, 96
+    dY = _mx_grid_exact(rng, M, N, along_rows=True)
+    W = _mx_grid_exact(rng, K, N, along_rows=True)
+    dX, _, _, _ = O.dgrad_mx(dY, W)
+    assert np.array_equal(dX, dY.astype(np.float64) @ W.astype(np.float64).T)
+    A = _mx_grid_exact(rng, M, K, along_rows=False)
+    dY2 = _mx_grid_exact(rng, M, N, along_rows=False)
+    dW, _, _, _ = O.wgrad_mx(A, dY2)
+    assert np.array_equal(dW, A.astype(np.float64).T @ dY2.astype(np.float64))
+    assert dW.shape == (K, N) and dX.shape == (M, K)
