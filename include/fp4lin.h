@@ -184,6 +184,8 @@ fp4lin_status fp4lin_quantize_act(const void* X, fp4lin_dtype dt, int64_t M, int
  *   Wq       device, N x fp4lin_packed_ld(K) bytes (output, padding zeroed)
  *   sW       device, N floats (output): RN32(amax_j / 6)
  *   ws       device workspace of >= fp4lin_weight_workspace_bytes(K, N)
+ * K must be at most 65535 * 128 = 8388480 (tiles of 128 codes along K index
+ * the second grid dimension), else FP4LIN_ERR_SHAPE.
  * Errors: NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, LAUNCH. */
 fp4lin_status fp4lin_quantize_weight(const void* W, fp4lin_dtype dt, int64_t K, int64_t N,
                                      int64_t ldw, uint8_t* Wq, float* sW, void* ws,
@@ -263,8 +265,9 @@ fp4lin_status fp4lin_quantize_act_mx(const void* X, fp4lin_dtype dt, int64_t M, 
  *   W        device, K x N, dtype dt, leading dimension ldw
  *   Wq       device, N x fp4lin_packed_ld(K) bytes (output, padding zeroed)
  *   Ws       device, N * fp4lin_mx_scales_ld(K) bytes, step-major (output)
- * Wq and Ws must be 16-byte aligned; K must be below 2^23 (tiles of 128 codes
- * along K index the second grid dimension), else FP4LIN_ERR_SHAPE.
+ * Wq and Ws must be 16-byte aligned; K must be at most 65535 * 128 = 8388480
+ * (tiles of 128 codes along K index the second grid dimension), else
+ * FP4LIN_ERR_SHAPE.
  * Errors: NULL, SHAPE, DTYPE, ALIGN, LAUNCH. */
 fp4lin_status fp4lin_quantize_weight_mx(const void* W, fp4lin_dtype dt, int64_t K, int64_t N,
                                         int64_t ldw, uint8_t* Wq, uint8_t* Ws,

@@ -27,6 +27,10 @@ fp4lin_status launch_status(hipError_t e) {
   return e == hipSuccess ? FP4LIN_OK : FP4LIN_ERR_LAUNCH;
 }
 
+// The column quantizers launch one workgroup row per 128 codes of K along the
+// grid's second dimension, which holds at most 65535.
+constexpr int64_t kMaxColK = int64_t(65535) * 128;
+
 // COO entries the select can produce for rank k: #{|a| > tau} <= n - 1 - k.
 int64_t needed_capacity(int64_t n, int64_t k) { return n - 1 - k; }
 
@@ -188,7 +192,7 @@ fp4lin_status fp4lin_quantize_weight(const void* W, fp4lin_dtype dt, int64_t K, 
                                      size_t ws_bytes, hipStream_t stream) {
   if (W == nullptr || Wq == nullptr || sW == nullptr || ws == nullptr) return FP4LIN_ERR_NULL;
   if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
-  if (!ok_dim(K) || !ok_dim(N) || ldw < N) return FP4LIN_ERR_SHAPE;
+  if (!ok_dim(K) || !ok_dim(N) || ldw < N || K > kMaxColK) return FP4LIN_ERR_SHAPE;
   if (!aligned16(Wq) || !aligned16(ws)) return FP4LIN_ERR_ALIGN;
   if (ws_bytes < weight_ws(N)) return FP4LIN_ERR_WORKSPACE;
   return launch_status(fp4lin::launch_quantize_weight(W, dt == FP4LIN_BF16, K, N, ldw, Wq,
@@ -253,7 +257,7 @@ fp4lin_status fp4lin_quantize_weight_mx(const void* W, fp4lin_dtype dt, int64_t 
                                         hipStream_t stream) {
   if (W == nullptr || Wq == nullptr || Ws == nullptr) return FP4LIN_ERR_NULL;
   if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
-  if (!ok_dim(K) || !ok_dim(N) || ldw < N || K >= (int64_t(1) << 23)) return FP4LIN_ERR_SHAPE;
+  if (!ok_dim(K) || !ok_dim(N) || ldw < N || K > kMaxColK) return FP4LIN_ERR_SHAPE;
   if (!aligned16(Wq) || !aligned16(Ws)) return FP4LIN_ERR_ALIGN;
   return launch_status(fp4lin::launch_quantize_cols_mx(W, dt == FP4LIN_BF16, K, N, ldw, Wq,
                                                        fp4lin_packed_ld(K), Ws, stream));
@@ -294,9 +298,11 @@ fp4lin_status fp4lin_forward(const void* A, const void* W, fp4lin_dtype dt, int6
   if (ls != FP4LIN_OK) return ls;
   if (!aligned16(ws)) return FP4LIN_ERR_ALIGN;
   if (ws_bytes < o.total) return FP4LIN_ERR_WORKSPACE;
-  // the GEMM's own limits, checked before anything is enqueued
+  // the limits of the GEMM and of W's quantizer, checked before anything is
+  // enqueued
   const int64_t ldq = fp4lin_packed_ld(K);
-  if ((M + 1) * ldq >= kMaxDim || (N + 1) * ldq >= kMaxDim || !weight_addressable(K, ldw, dt))
+  if ((M + 1) * ldq >= kMaxDim || (N + 1) * ldq >= kMaxDim || !weight_addressable(K, ldw, dt) ||
+      K > kMaxColK)
     return FP4LIN_ERR_SHAPE;
   char* base = static_cast<char*>(ws);
   float* tau = reinterpret_cast<float*>(base + o.tau);

@@ -164,6 +164,8 @@ def test_quantize_weight_errors():
     assert quant_w(Wq=MISALIGNED) == _lib.ERR_ALIGN
     assert quant_w(ws=MISALIGNED) == _lib.ERR_ALIGN
     assert quant_w(wsb=4) == _lib.ERR_WORKSPACE
+    # tiles of 128 codes along K index the second grid dimension (at most 65535)
+    assert quant_w(K=65535 * 128 + 1, N=1, ldw=1) == _lib.ERR_SHAPE
 
 
 def gemm(Aq=FAKE, sA=FAKE, Bq=FAKE, sB=FAKE, M=4, N=4, K=8, dA=None, W=None, wdt=1, ldw=4,
@@ -231,7 +233,7 @@ def test_quantize_mx_errors():
     assert wt(dt=3) == _lib.ERR_DTYPE
     assert wt(N=0) == _lib.ERR_SHAPE
     assert wt(ldw=3) == _lib.ERR_SHAPE
-    assert wt(K=1 << 23, N=1, ldw=1) == _lib.ERR_SHAPE
+    assert wt(K=65535 * 128 + 1, N=1, ldw=1) == _lib.ERR_SHAPE   # grid y above 65535
     assert wt(Wq=MISALIGNED) == _lib.ERR_ALIGN
     assert wt(Ws=MISALIGNED) == _lib.ERR_ALIGN
 
