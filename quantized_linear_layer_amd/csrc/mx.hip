@@ -64,10 +64,11 @@ __device__ inline float quad_max(float v) {
   return fmaxf(v, __shfl_xor(v, 2, kWave));
 }
 
-// Thread t takes chunk c = t mod cpr of row t / cpr (cpr = ldq / 4 chunks of 8
-// codes per padded row, a multiple of 16). Four consecutive t hold one block
-// and sit on four consecutive lanes, and the grid stride is a multiple of 4,
-// so a block's lanes are active together.
+// Workgroup (bx, by) takes rows by, by + gridDim.y, ... and in each the chunks
+// c = bx * 256 + t, c + 256 * gridDim.x, ... (cpr = ldq / 4 chunks of 8 codes
+// per padded row, a multiple of 16). Four consecutive t hold one block and sit
+// on four consecutive lanes, and the chunk stride is a multiple of 4, so a
+// block's lanes are active together.
 template <class In, bool kFast>
 __global__ __launch_bounds__(kMxThreads) void quantize_rows_mx_kernel(
     const typename In::T* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
@@ -75,11 +76,9 @@ __global__ __launch_bounds__(kMxThreads) void quantize_rows_mx_kernel(
     uint8_t* __restrict__ Xs) {
   const float tau = tau_p ? *tau_p : __builtin_huge_valf();
   const int64_t cpr = ldq / 4;
-  const int64_t total = M * cpr;
-  for (int64_t t = int64_t(blockIdx.x) * kMxThreads + threadIdx.x; t < total;
-       t += int64_t(gridDim.x) * kMxThreads) {
-    const int64_t r = t / cpr;
-    const int64_t c = t - r * cpr;
+  for (int64_t r = blockIdx.y; r < M; r += gridDim.y)
+  for (int64_t c = int64_t(blockIdx.x) * kMxThreads + threadIdx.x; c < cpr;
+       c += int64_t(gridDim.x) * kMxThreads) {
     Vec8<In> v;
     load_chunk<In, kFast>(X + r * ldx, c * 8, K, v);
     float ax[8];
@@ -151,9 +150,10 @@ __global__ __launch_bounds__(kMxThreads) void quantize_cols_mx_kernel(
   }
 }
 
-unsigned mx_row_grid(int64_t threads) {
-  const int64_t b = (threads + kMxThreads - 1) / kMxThreads;
-  return unsigned(b < (int64_t(1) << 20) ? b : (int64_t(1) << 20));
+// chunks of a row across x (at most 64 workgroups), rows across y (at most 65535)
+dim3 mx_row_grid(int64_t M, int64_t cpr) {
+  const int64_t bx = (cpr + kMxThreads - 1) / kMxThreads;
+  return dim3(unsigned(bx < 64 ? bx : 64), unsigned(M < 65535 ? M : 65535));
 }
 
 template <class In>
@@ -163,7 +163,7 @@ hipError_t run_rows_mx(const void* X, int64_t M, int64_t K, int64_t ldx, const f
   const T* x = static_cast<const T*>(X);
   const bool fast = (reinterpret_cast<uintptr_t>(X) % 16 == 0) &&
                     ((ldx * In::kBytes) % 16 == 0) && (K % 8 == 0);
-  const unsigned grid = mx_row_grid(M * (ldq / 4));
+  const dim3 grid = mx_row_grid(M, ldq / 4);
   if (fast)
     quantize_rows_mx_kernel<In, true><<<grid, kMxThreads, 0, stream>>>(x, M, K, ldx, tau, Xq, ldq,
                                                                        Xs);
