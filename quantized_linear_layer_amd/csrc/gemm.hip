@@ -231,33 +231,52 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   // codes 32h .. 32h+31 of each 64-code sub-step, i.e. block 4kt + 2kk + h in
   // sub-step kk: the word shifted right by 8h, byte kk*2 of it picked by the
   // instruction's op_sel. Rows past M (N) take the scales of the last row:
-  // their codes are zero, so any finite scale gives zero. The words of step
-  // kt go into slot kt mod 3 of a register ring, loaded three steps ahead.
-  constexpr int NS = kMx ? FM + FN : 0;
+  // their codes are zero, so any finite scale gives zero. One load serves two
+  // fragments (A's two, then B's in pairs): lanes 0..31 read the rows of the
+  // first, lanes 32..63 those of the second (64 consecutive rows, 256
+  // contiguous bytes), and a lane-half swap (v_permlane32_swap) then gives
+  // every lane its row's word of both. The raw words of step kt go into slot
+  // kt mod 3 of a register ring, loaded three steps ahead.
+  constexpr int NS = kMx ? FM + FN : 0;  // scale words per step (one per fragment)
+  constexpr int NL = NS / 2;             // scale loads per step
+  static_assert(!kMx || (FM % 2 == 0 && FN % 2 == 0), "fragments pair up");
   const int nblk = ldq / 16;
   const __amdgpu_buffer_rsrc_t rsSA = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(As), 0, kMx ? M * nblk : 0, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsSB = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(Bs), 0, kMx ? N * nblk : 0, kBufferFlags);
-  int sc_off[NS > 0 ? NS : 1];
+  int sc_off[NL > 0 ? NL : 1];
   if constexpr (kMx) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-      sc_off[fm] = 4 * ((m0 + a_row[fm] < M) ? m0 + a_row[fm] : M - 1);
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-      sc_off[FM + fn] = 4 * ((n0 + b_row[fn] < N) ? n0 + b_row[fn] : N - 1);
+    for (int j = 0; j < NL; ++j) {
+      const int f = 2 * j + (lane >> 5);  // this lane's fragment of load j
+      const int row = f < FM ? m0 + a_row[f] : n0 + b_row[f - FM];
+      const int lim = f < FM ? M : N;
+      sc_off[j] = 4 * (row < lim ? row : lim - 1);
+    }
   }
   const int hshift = (lane >> 5) * 8;
-  uint32_t sc0[NS > 0 ? NS : 1], sc1[NS > 0 ? NS : 1], sc2[NS > 0 ? NS : 1];
+  uint32_t sc0[NL > 0 ? NL : 1], sc1[NL > 0 ? NL : 1], sc2[NL > 0 ? NL : 1];
   // The manual vmcnt waits below count the stage loads and these in issue
   // order; scheduling barriers keep every group where it is written.
   auto load_scales = [&](int kt, uint32_t* dst) {
     if constexpr (kMx) {
 #pragma unroll
-      for (int f = 0; f < NS; ++f)
-        dst[f] = __builtin_amdgcn_raw_buffer_load_b32(f < FM ? rsSA : rsSB,
-                                                      sc_off[f] + kt * 4 * (f < FM ? M : N), 0, 0);
+      for (int j = 0; j < NL; ++j)
+        dst[j] = __builtin_amdgcn_raw_buffer_load_b32(2 * j < FM ? rsSA : rsSB,
+                                                      sc_off[j] + kt * 4 * (2 * j < FM ? M : N), 0, 0);
+    }
+  };
+  // one scale word per fragment from the raw words of a step, shifted to the
+  // lane half's block
+  auto expand = [&](const uint32_t* raw, uint32_t* w) {
+    if constexpr (kMx) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(raw[j], raw[j], false, false);
+        w[2 * j] = uint32_t(sw[0]) >> hshift;
+        w[2 * j + 1] = uint32_t(sw[1]) >> hshift;
+      }
     }
   };
   // kk_c: the sub-step (0 or 1) as a type, so that op_sel is a constant
@@ -269,8 +288,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
       for (int fn = 0; fn < FN; ++fn) {
         if constexpr (kMx)
           acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af[fm], bf[fn], acc[fm][fn], 4, 4, 2 * KK, int(sc[fm] >> hshift), 2 * KK,
-              int(sc[FM + fn] >> hshift));
+              af[fm], bf[fn], acc[fm][fn], 4, 4, 2 * KK, int(sc[fm]), 2 * KK, int(sc[FM + fn]));
         else
           acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf[fn], acc[fm][fn],
                                                                         4, 4, 0, 127, 0, 127);
@@ -289,24 +307,26 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   // go there; then the second sub-step's MFMAs and the next step's first
   // fragment reads. Every wave issues kPer loads per step on every path
   // (past the last step they repeat it into a stage that is not read).
-  // With block scales, each step also loads the NS scale words of step kt+3
+  // With block scales, each step also issues the NL scale loads of step kt+3
   // after its second sub-step; a step's wait then leaves that step's and the
-  // previous step's scale words in flight besides the stage of kt+2.
-  constexpr int kWaitCnt = waitcnt_vm_lgkm(kPer + 2 * NS, 0);
-  static_assert(2 * kPer + 2 * NS < 64, "vmcnt immediate");
+  // previous step's scale loads in flight besides the stage of kt+2.
+  constexpr int kWaitCnt = waitcnt_vm_lgkm(kPer + 2 * NL, 0);
+  static_assert(2 * kPer + 2 * NL < 64, "vmcnt immediate");
   v8i a0[FM], b0[FN], a1[FM], b1[FN];
   // a full step inside the main loop (steps kt, kt+1 and kt+2 all exist);
-  // sc holds the scale words of step kt and is refilled for step kt+3
+  // sc holds the raw scale words of step kt and is refilled for step kt+3
+  uint32_t scw[NS > 0 ? NS : 1];
   auto step = [&](int kt, const uint8_t* cur, const uint8_t* nxt, uint8_t* ldst, uint32_t* sc) {
     read_frags(cur, 1, a1, b1);
+    expand(sc, scw);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(Sub0{}, a0, b0, sc);
+    mfmas(Sub0{}, a0, b0, scw);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitCnt);
     raw_barrier();
     __builtin_amdgcn_sched_barrier(0);
     dma(kt + 3 < nkt ? kt + 3 : nkt - 1, ldst);
-    mfmas(Sub1{}, a1, b1, sc);
+    mfmas(Sub1{}, a1, b1, scw);
     __builtin_amdgcn_sched_barrier(0);
     load_scales(kt + 3 < nkt ? kt + 3 : nkt - 1, sc);
     read_frags(nxt, 0, a0, b0);
@@ -314,13 +334,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   // one of the last (up to two) steps: no more loads are issued
   auto tail_step = [&](const uint8_t* cur, const uint8_t* nxt, bool has_next, const uint32_t* sc) {
     read_frags(cur, 1, a1, b1);
+    expand(sc, scw);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(Sub0{}, a0, b0, sc);
+    mfmas(Sub0{}, a0, b0, scw);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, 0));
     raw_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(Sub1{}, a1, b1, sc);
+    mfmas(Sub1{}, a1, b1, scw);
     __builtin_amdgcn_sched_barrier(0);
     if (has_next) read_frags(nxt, 0, a0, b0);
   };
@@ -333,7 +354,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   dma(nkt > 2 ? 2 : nkt - 1, st2);
   load_scales(nkt > 2 ? 2 : nkt - 1, sc2);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(2 * kPer + 2 * NS, 0));  // step 0 landed
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(2 * kPer + 2 * NL, 0));  // step 0 landed
   raw_barrier();
   read_frags(st0, 0, a0, b0);
   int kt0 = 0;
