@@ -676,3 +676,39 @@ def test_gemm_compensation_padded_layouts(ql, dtype, N, ldy_pad, ldw_pad):
     ql.fp4lin_sparse_add(coo, Wd, Y2)
     t.cuda.synchronize()
     assert np.array_equal(host(Ybuf2).view(np.uint32), full.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# the largest shape the 32-bit operand offsets allow
+# ---------------------------------------------------------------------------
+def test_gemm_largest_packed_offsets(ql):
+    """(M+1) * packed_ld(K) = 2^31 - 512, just under the limit the C ABI checks:
+    the last rows' tiles address the top of the 2 GiB packed operand (and of
+    its scale rows in the micro-scaled GEMM). Unit scales, so sampled rows are
+    exact integer products."""
+    t = torch()
+    K, N = 1024, 16
+    ldq = O.packed_ld(K)
+    M = (1 << 31) // ldq - 2
+    assert (M + 1) * ldq < (1 << 31) and (M + 2) * ldq >= (1 << 31)
+    log(f"gemm largest offsets M={M} K={K} N={N}")
+    rng = np.random.default_rng(12)
+    # packed codes generated directly (two random nibbles per byte)
+    Aq = t.randint(0, 256, (M, ldq), dtype=t.uint8, device="cuda:0",
+                   generator=t.Generator(device="cuda:0").manual_seed(5))
+    cb = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    Bq = upload_u8(O.pack_rows(cb))
+    Y = ql.gemm(Aq, t.ones(M, dtype=t.float32, device="cuda:0"), Bq,
+                t.ones(N, dtype=t.float32, device="cuda:0"), M, N, K)
+    nb = ql.mx_scales_ld(K)
+    As = t.full((M * nb,), 127, dtype=t.uint8, device="cuda:0")
+    Bs = t.full((N * nb,), 127, dtype=t.uint8, device="cuda:0")
+    Ymx = ql.gemm_mx(Aq, As, Bq, Bs, M, N, K)
+    t.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1, M - 2, M - 129], rng.choice(M, 60, replace=False)]))
+    sel = t.as_tensor(rows, device="cuda:0")
+    ca = O.unpack_rows(host(Aq[sel]), K)
+    want = O.integer_product(ca, cb)
+    assert np.array_equal(host(Y[sel]).astype(np.float64), want)
+    assert np.array_equal(host(Ymx[sel]).astype(np.float64), want)
+    del Aq, As, Y, Ymx
