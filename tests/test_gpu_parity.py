@@ -712,3 +712,77 @@ def test_gemm_largest_packed_offsets(ql):
     assert np.array_equal(host(Y[sel]).astype(np.float64), want)
     assert np.array_equal(host(Ymx[sel]).astype(np.float64), want)
     del Aq, As, Y, Ymx
+
+
+def test_select_largest_count(ql):
+    """M*K = 2^32 - 4096, just under the 32-bit histogram counts' limit (an
+    8 GiB bfloat16 A drawn on the device). Checked by properties that hold at
+    any size: tau is an element of |A| with #{|a| < tau} <= k < #{|a| <= tau};
+    row_ptr[M] = #{|a| > tau}; sampled rows' COO entries are exactly their
+    entries above tau, in column order, with val = RN32(a - sign(a) tau)."""
+    t = torch()
+    M, K, q = (1 << 20) - 1, 4096, 0.999
+    n = M * K
+    log(f"select largest count M={M} K={K}")
+    g = t.Generator(device="cuda:0").manual_seed(3)
+    A = t.randn((M, K), dtype=t.float32, device="cuda:0", generator=g).to(t.bfloat16)
+    tau_d, coo = ql.outlier_select(A, q)
+    t.cuda.synchronize()
+    k = O.quantile_rank(n, q)
+    tau = float(host(tau_d)[0])
+    absA = A.abs()
+    below = int((absA < tau).sum())
+    at_or_below = int((absA <= tau).sum())
+    assert below <= k < at_or_below
+    nnz = int(host(coo.row_ptr[M:M + 1])[0])
+    assert nnz == n - at_or_below
+    del absA
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)]))
+    rp = host(coo.row_ptr).astype(np.int64)
+    cols = host(coo.col)
+    vals = host(coo.val)
+    for i in rows:
+        a = A[int(i)].float().cpu().numpy()
+        want_c = np.nonzero(np.abs(a) > np.float32(tau))[0]
+        lo, hi = rp[i], rp[i + 1]
+        assert np.array_equal(cols[lo:hi], want_c), i
+        want_v = (a[want_c].astype(np.float64) - np.sign(a[want_c]) * tau).astype(np.float32)
+        assert_bits_equal(vals[lo:hi], want_v, f"row {i} values")
+    del A, coo
+
+
+def test_sparse_add_largest_weight_offsets(ql):
+    """K * ldw * 2 = 2^31 - 524288 (a 2 GiB bfloat16 W, just under the 32-bit
+    byte-offset limit the C ABI checks), with entries in W's last rows: each
+    row of Y equals its entries' sum of val * W[k, :] (float64 reference,
+    relative error of an fp32 sum of at most 64 terms)."""
+    t = torch()
+    K, N, M = 32768, 32760, 48
+    assert K * N * 2 < (1 << 31)
+    log(f"sparse_add largest offsets K={K} N={N}")
+    g = t.Generator(device="cuda:0").manual_seed(8)
+    W = (t.randn((K, N), dtype=t.float32, device="cuda:0", generator=g) * 0.02).to(t.bfloat16)
+    rng = np.random.default_rng(9)
+    rows, cols, vals = [], [], []
+    row_ptr = [0]
+    for i in range(M):
+        c = np.unique(np.concatenate([[K - 1, K - 2 - i], rng.choice(K, 40, replace=False)]))
+        rows += [i] * len(c)
+        cols += list(c)
+        vals += list(rng.standard_normal(len(c)).astype(np.float32) * 10)
+        row_ptr.append(len(cols))
+    coo = ql.CooBuffers(upload_i32(rows), upload_i32(cols), upload_f32(vals), upload_i32(row_ptr))
+    Y = t.zeros((M, N), dtype=t.float32, device="cuda:0")
+    ql.fp4lin_sparse_add(coo, W, Y)
+    t.cuda.synchronize()
+    Yh = host(Y).astype(np.float64)
+    vals = np.asarray(vals, np.float32).astype(np.float64)
+    for i in range(M):
+        lo, hi = row_ptr[i], row_ptr[i + 1]
+        idx = t.as_tensor(np.asarray(cols[lo:hi]), device="cuda:0")
+        Wr = W[idx].float().cpu().numpy().astype(np.float64)
+        want = vals[lo:hi] @ Wr
+        err = np.abs(Yh[i] - want).max() / max(np.abs(want).max(), 1e-30)
+        assert err < 1e-5, (i, err)
+    del W, Y
