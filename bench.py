@@ -20,9 +20,10 @@ W rows, then gemm) or dW = Q(A)^T Q(dY) (quantize_weight on A and on dY, then
 gemm with K' = M).
 
 --quant mx times the micro-scaled variant of the forward instead: each step is
-the five public calls outlier_select, quantize_act_mx, quantize_weight_mx,
-gemm_mx and sparse_add (32-code blocks along K with E8M0 scales, the block
-scales applied by the matrix core). With --pass dgrad / wgrad it takes the
+one fp4lin_forward_mx call (32-code blocks along K with E8M0 scales, the block
+scales applied by the matrix core); the per-stage breakdown issues its five
+public calls outlier_select, quantize_act_mx, quantize_weight_mx, gemm_mx and
+sparse_add. With --pass dgrad / wgrad it takes the
 micro-scaled quantizers and gemm_mx for the backward GEMMs (blocks along the
 reduction: N for dgrad, M for wgrad).
 """
@@ -152,6 +153,9 @@ class MxStep(Step):
         self.Ws_t = self.torch.empty((self.N * nb,), dtype=self.torch.uint8, device=A.device)
         self.As = ctypes.c_void_p(self.As_t.data_ptr())
         self.Ws = ctypes.c_void_p(self.Ws_t.data_ptr())
+        # fp4lin_forward_mx's own workspace
+        nbytes = int(self.lib.fp4lin_workspace_bytes_mx(self.M, self.K, self.N, self.dt, q))
+        self.mws = self.torch.empty((nbytes,), dtype=self.torch.uint8, device=A.device)
 
     def quant_a(self):
         s = self.lib.fp4lin_quantize_act_mx(self.A, self.dt, self.M, self.K, self.lda, self.tau,
@@ -170,11 +174,17 @@ class MxStep(Step):
         assert s == 0, s
 
     def step(self):
-        self.select(); self.quant_a(); self.quant_w(); self.gemm(); self.sparse()
+        s = self.lib.fp4lin_forward_mx(self.A, self.W, self.dt, self.M, self.K, self.N,
+                                       self.lda, self.ldw, self.q,
+                                       ctypes.c_void_p(self.Y.data_ptr()), self.N,
+                                       ctypes.c_void_p(self.mws.data_ptr()), self.mws.numel(),
+                                       self.stream)
+        assert s == 0, s
 
 
 def run_forward_mx(args):
-    """One JSON line for --quant mx: the micro-scaled forward, step = five calls."""
+    """One JSON line for --quant mx: the micro-scaled forward, step = one
+    fp4lin_forward_mx call."""
     import torch
     import quantized_linear_layer_amd as ql
     import workloads as wl
@@ -186,6 +196,7 @@ def run_forward_mx(args):
     M, K, N = L.M, L.K, L.N
     flops = 2.0 * M * N * K
     for _ in range(max(args.warmup, 1)):
+        st.select(); st.quant_a(); st.quant_w(); st.gemm(); st.sparse()
         st.step()
     torch.cuda.synchronize()
     nnz = int(st.ws[st.offsets.row_ptr + 4 * M: st.offsets.row_ptr + 4 * M + 4]

@@ -291,6 +291,30 @@ fp4lin_status fp4lin_gemm_mx(const uint8_t* Aq, const uint8_t* As, const uint8_t
                              const fp4lin_coo* dA, const void* W, fp4lin_dtype wdt,
                              int64_t ldw, float* Y, int64_t ldy, hipStream_t stream);
 
+/* Workspace of fp4lin_forward_mx and where it keeps its intermediates: the
+ * layout of fp4lin_forward_layout with the sA / sW offsets holding the
+ * step-major E8M0 scales of A (M * mx_scales_ld(K) bytes) and of W
+ * (N * mx_scales_ld(K) bytes). 0 (or an error) for invalid arguments. */
+size_t fp4lin_workspace_bytes_mx(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt, double q);
+fp4lin_status fp4lin_forward_layout_mx(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt,
+                                       double q, fp4lin_forward_offsets* out /* host */);
+
+/* The whole micro-scaled layer forward: what fp4lin_outlier_select,
+ * fp4lin_quantize_act_mx (with the selected tau), fp4lin_quantize_weight_mx
+ * and fp4lin_gemm_mx (with dA) compute, in that order on `stream`, keeping
+ * every intermediate in `ws` at the offsets fp4lin_forward_layout_mx reports.
+ * For bf16 A with 16-byte aligned rows and K <= 8192 the outlier compaction
+ * and the block quantization of A run as one kernel over one read of A; every
+ * intermediate and Y are bit-identical to those of the separate calls.
+ *   A, W     device inputs (same dtype dt), leading dimensions lda, ldw
+ *   Y        device output, M x N floats, leading dimension ldy
+ *   ws       device workspace of >= fp4lin_workspace_bytes_mx(M, K, N, dt, q)
+ * Errors: any of the calls it makes. */
+fp4lin_status fp4lin_forward_mx(const void* A, const void* W, fp4lin_dtype dt, int64_t M,
+                                int64_t K, int64_t N, int64_t lda, int64_t ldw, double q,
+                                float* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
 /* The whole layer forward (forward-start paragraph: W and A are quantized when
  * the layer's forward begins). Computes what fp4lin_outlier_select,
  * fp4lin_quantize_act (with the selected tau), fp4lin_quantize_weight and

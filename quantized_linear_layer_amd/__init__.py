@@ -21,6 +21,7 @@ __all__ = [
     "fp4lin_sparse_add", "fp4lin_forward", "outlier_select", "quantize_act", "quantize_weight", "gemm", "forward",
     "CooBuffers", "mx_scales_ld", "fp4lin_quantize_act_mx", "fp4lin_quantize_weight_mx",
     "fp4lin_gemm_mx", "quantize_act_mx", "quantize_weight_mx", "gemm_mx",
+    "fp4lin_forward_mx", "forward_mx", "forward_layout_mx",
 ]
 
 
@@ -218,6 +219,20 @@ def fp4lin_gemm_mx(Aq, As, Bq, Bs, M, N, K, coo: CooBuffers | None, W, Y, stream
            "fp4lin_gemm_mx")
 
 
+def fp4lin_forward_mx(A, W, q, Y, ws, stream=None):
+    M, K, lda = _matrix(A, "A")
+    K2, N, ldw = _matrix(W, "W")
+    if K2 != K:
+        raise ValueError(f"A is {M}x{K} but W is {K2}x{N}")
+    if A.dtype != W.dtype:
+        raise TypeError("A and W must have the same dtype")
+    _, _, ldy = _matrix(Y, "Y")
+    _check(lib().fp4lin_forward_mx(_dev(A, "A"), _dev(W, "W"), _dtype_code(A), M, K, N, lda, ldw,
+                                   float(q), _dev(Y, "Y"), ldy, _dev(ws, "ws"),
+                                   ws.numel() * ws.element_size(), _stream(stream)),
+           "fp4lin_forward_mx")
+
+
 # ---- allocating helpers --------------------------------------------------------------
 def _empty(shape, dtype, device):
     return _torch().empty(shape, dtype=dtype, device=device)
@@ -311,3 +326,24 @@ def gemm_mx(Aq, As, Bq, Bs, M, N, K, coo=None, W=None, stream=None):
     Y = _empty((M, N), _torch().float32, Aq.device)
     fp4lin_gemm_mx(Aq, As, Bq, Bs, M, N, K, coo, W, Y, stream)
     return Y
+
+
+def forward_layout_mx(M: int, K: int, N: int, dtype_code: int, q: float) -> ForwardOffsets:
+    o = ForwardOffsets()
+    _check(lib().fp4lin_forward_layout_mx(M, K, N, dtype_code, float(q), ctypes.byref(o)),
+           "fp4lin_forward_layout_mx")
+    return o
+
+
+def forward_mx(A, W, q, stream=None, return_workspace=False):
+    """Micro-scaled forward; returns Y float32 M x N (and the workspace)."""
+    torch = _torch()
+    M, K, _ = _matrix(A, "A")
+    N = W.shape[1]
+    nbytes = lib().fp4lin_workspace_bytes_mx(M, K, N, _dtype_code(A), float(q))
+    if nbytes == 0:
+        raise Fp4linError(_lib.ERR_SHAPE, "forward_mx")
+    ws = _empty((nbytes,), torch.uint8, A.device)
+    Y = _empty((M, N), torch.float32, A.device)
+    fp4lin_forward_mx(A, W, q, Y, ws, stream)
+    return (Y, ws) if return_workspace else Y

@@ -60,6 +60,11 @@ SIGNATURES = {
                                           c_ptr]),
     "fp4lin_gemm_mx": (c_int, [c_ptr, c_ptr, c_ptr, c_ptr, c_i64, c_i64, c_i64,
                                ctypes.POINTER(Coo), c_ptr, c_int, c_i64, c_ptr, c_i64, c_ptr]),
+    "fp4lin_workspace_bytes_mx": (c_size, [c_i64, c_i64, c_i64, c_int, c_dbl]),
+    "fp4lin_forward_layout_mx": (c_int, [c_i64, c_i64, c_i64, c_int, c_dbl,
+                                         ctypes.POINTER(ForwardOffsets)]),
+    "fp4lin_forward_mx": (c_int, [c_ptr, c_ptr, c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl,
+                                  c_ptr, c_i64, c_ptr, c_size, c_ptr]),
 }
 
 _lib = None

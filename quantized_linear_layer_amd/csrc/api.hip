@@ -73,8 +73,15 @@ size_t fp4lin_weight_workspace_bytes(int64_t K, int64_t N) {
   return weight_ws(N);
 }
 
-fp4lin_status fp4lin_forward_layout(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt, double q,
-                                    fp4lin_forward_offsets* out) {
+}  // extern "C"
+
+namespace {
+
+// The forward's workspace: tau, the COO, the packed operands with their
+// scales (fp32 vectors, or with mx the step-major E8M0 block scales), then
+// scratch.
+fp4lin_status forward_layout(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt, double q, bool mx,
+                             fp4lin_forward_offsets* out) {
   if (out == nullptr) return FP4LIN_ERR_NULL;
   if (!ok_dim(M) || !ok_dim(K) || !ok_dim(N)) return FP4LIN_ERR_SHAPE;
   if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
@@ -98,22 +105,43 @@ fp4lin_status fp4lin_forward_layout(int64_t M, int64_t K, int64_t N, fp4lin_dtyp
   o.coo_col = take(slots * 4);
   o.coo_val = take(slots * 4);
   o.row_ptr = take(size_t(M + 1) * 4);
+  const size_t nblk = ldq / 16;
   o.Aq = take(size_t(M) * ldq);
-  o.sA = take(size_t(M) * 4);
+  o.sA = take(size_t(M) * (mx ? nblk : 4));
   o.Wq = take(size_t(N) * ldq);
-  o.sW = take(size_t(N) * 4);
-  // the select's workspace, then the column maxima of W's quantization (the
-  // forward keeps both live at once)
-  o.scratch = take(select_ws(M, dt) + weight_ws(N));
+  o.sW = take(size_t(N) * (mx ? nblk : 4));
+  // the select's workspace, then (token-wise) the column maxima of W's
+  // quantization: the forward keeps both live at once
+  o.scratch = take(select_ws(M, dt) + (mx ? 0 : weight_ws(N)));
   o.capacity = cap;
   o.total = off;
   *out = o;
   return FP4LIN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+fp4lin_status fp4lin_forward_layout(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt, double q,
+                                    fp4lin_forward_offsets* out) {
+  return forward_layout(M, K, N, dt, q, false, out);
+}
+
+fp4lin_status fp4lin_forward_layout_mx(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt,
+                                       double q, fp4lin_forward_offsets* out) {
+  return forward_layout(M, K, N, dt, q, true, out);
+}
+
 size_t fp4lin_workspace_bytes(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt, double q) {
   fp4lin_forward_offsets o;
   if (fp4lin_forward_layout(M, K, N, dt, q, &o) != FP4LIN_OK) return 0;
+  return o.total;
+}
+
+size_t fp4lin_workspace_bytes_mx(int64_t M, int64_t K, int64_t N, fp4lin_dtype dt, double q) {
+  fp4lin_forward_offsets o;
+  if (fp4lin_forward_layout_mx(M, K, N, dt, q, &o) != FP4LIN_OK) return 0;
   return o.total;
 }
 
@@ -145,7 +173,8 @@ namespace {
 // it, and *quantized says whether it was.
 fp4lin_status select_impl(const void* A, fp4lin_dtype dt, int64_t M, int64_t K, int64_t lda,
                           double q, float* tau, fp4lin_coo dA, void* ws, size_t ws_bytes,
-                          hipStream_t stream, uint8_t* Xq, float* sX, bool* quantized) {
+                          hipStream_t stream, uint8_t* Xq, float* sX, bool* quantized,
+                          uint8_t* Xs = nullptr) {
   if (A == nullptr || tau == nullptr || dA.row == nullptr || dA.col == nullptr ||
       dA.val == nullptr || dA.row_ptr == nullptr || ws == nullptr)
     return FP4LIN_ERR_NULL;
@@ -162,7 +191,7 @@ fp4lin_status select_impl(const void* A, fp4lin_dtype dt, int64_t M, int64_t K, 
   if (ws_bytes < select_ws(M, dt)) return FP4LIN_ERR_WORKSPACE;
   return launch_status(fp4lin::launch_outlier_select(
       A, dt == FP4LIN_BF16, M, K, lda, k, tau, dA.capacity, dA.row, dA.col, dA.val, dA.row_ptr,
-      ws, stream, Xq, fp4lin_packed_ld(K), sX, quantized));
+      ws, stream, Xq, fp4lin_packed_ld(K), sX, quantized, Xs));
 }
 
 }  // namespace
@@ -349,6 +378,54 @@ fp4lin_status fp4lin_forward(const void* A, const void* W, fp4lin_dtype dt, int6
     if (s != FP4LIN_OK) return s;
   }
   return fp4lin_gemm(Aq, sA, Wq, sW, M, N, K, &coo, W, dt, ldw, Y, ldy, stream);
+}
+
+fp4lin_status fp4lin_forward_mx(const void* A, const void* W, fp4lin_dtype dt, int64_t M,
+                                int64_t K, int64_t N, int64_t lda, int64_t ldw, double q,
+                                float* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (A == nullptr || W == nullptr || Y == nullptr || ws == nullptr) return FP4LIN_ERR_NULL;
+  if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
+  if (!ok_dim(M) || !ok_dim(K) || !ok_dim(N) || lda < K || ldw < N || ldy < N)
+    return FP4LIN_ERR_SHAPE;
+  fp4lin_forward_offsets o;
+  const fp4lin_status ls = fp4lin_forward_layout_mx(M, K, N, dt, q, &o);
+  if (ls != FP4LIN_OK) return ls;
+  if (!aligned16(ws)) return FP4LIN_ERR_ALIGN;
+  if (ws_bytes < o.total) return FP4LIN_ERR_WORKSPACE;
+  // the limits of the GEMM and of W's quantizer, checked before anything is
+  // enqueued
+  const int64_t ldq = fp4lin_packed_ld(K);
+  if ((M + 1) * ldq >= kMaxDim || (N + 1) * ldq >= kMaxDim || !weight_addressable(K, ldw, dt) ||
+      K > kMaxColK)
+    return FP4LIN_ERR_SHAPE;
+  char* base = static_cast<char*>(ws);
+  float* tau = reinterpret_cast<float*>(base + o.tau);
+  fp4lin_coo coo;
+  coo.row = reinterpret_cast<int32_t*>(base + o.coo_row);
+  coo.col = reinterpret_cast<int32_t*>(base + o.coo_col);
+  coo.val = reinterpret_cast<float*>(base + o.coo_val);
+  coo.row_ptr = reinterpret_cast<int32_t*>(base + o.row_ptr);
+  coo.capacity = o.capacity;
+  uint8_t* Aq = reinterpret_cast<uint8_t*>(base + o.Aq);
+  uint8_t* As = reinterpret_cast<uint8_t*>(base + o.sA);
+  uint8_t* Wq = reinterpret_cast<uint8_t*>(base + o.Wq);
+  uint8_t* Ws = reinterpret_cast<uint8_t*>(base + o.sW);
+  void* scratch = base + o.scratch;
+  const size_t scratch_bytes = o.total - o.scratch;
+  // bfloat16 rows that fit one slab are block-quantized by the select's
+  // compaction, which reads A anyway
+  bool a_done = false;
+  fp4lin_status s = select_impl(A, dt, M, K, lda, q, tau, coo, scratch, scratch_bytes, stream, Aq,
+                                nullptr, &a_done, As);
+  if (s != FP4LIN_OK) return s;
+  if (!a_done) {
+    s = fp4lin_quantize_act_mx(A, dt, M, K, lda, tau, Aq, As, stream);
+    if (s != FP4LIN_OK) return s;
+  }
+  s = fp4lin_quantize_weight_mx(W, dt, K, N, ldw, Wq, Ws, stream);
+  if (s != FP4LIN_OK) return s;
+  return fp4lin_gemm_mx(Aq, As, Wq, Ws, M, N, K, &coo, W, dt, ldw, Y, ldy, stream);
 }
 
 }  // extern "C"

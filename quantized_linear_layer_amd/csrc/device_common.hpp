@@ -268,4 +268,72 @@ __device__ inline void quantize_bf16_row(const uint4 (&w)[CH], int64_t Kp, float
   }
 }
 
+// ---------------------------------------------------------------------------
+// Micro-scaled (MXFP4) blocks: 32 consecutive codes along K, one E8M0 scale.
+// ---------------------------------------------------------------------------
+// Least e >= -127 with 6 * 2^e >= amax (amax >= 0, finite). With
+// amax = m * 2^E, 1 <= m < 2: 1.5 * 2^E = 6 * 2^(E-2) covers amax exactly when
+// m <= 1.5, else 3 * 2^E = 6 * 2^(E-1) does. Zero and subnormal amax (and
+// every normal one below 6 * 2^-127) give -127.
+__device__ inline int mx_exponent(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int biased = int(b >> 23);
+  int e = ((b & 0x7fffffu) <= 0x400000u) ? biased - 129 : biased - 128;
+  if (biased == 0) e = -127;
+  return e < -127 ? -127 : e;
+}
+
+// Magnitude index of y = ax / 2^e: 4y = ax * 2^(2-e) is exact (ldexp never
+// rounds a result that reaches a midpoint; 4y <= 24), and the index is the
+// table lookup of the token-wise encoder at n = min(floor(4y), 20).
+__device__ inline uint32_t mx_magnitude(float ax, int e) {
+  uint32_t n = cvt_u32_sat(ldexpf(ax, 2 - e));
+  n = n < 20u ? n : 20u;
+  return uint32_t(e2m1_lut() >> (3u * n)) & 7u;
+}
+
+__device__ inline float quad_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, kWave));
+  return fmaxf(v, __shfl_xor(v, 2, kWave));
+}
+
+// Micro-scaled quantization of one bfloat16 row of the M-row matrix held in
+// registers as raw 16-byte words (chunk j of lane l: columns (64j + l) * 8 ..
+// +7, zero past K), clamped to tau: the codes of the columns below Kp go to
+// qrow, 8 per 32-bit store, and the first lane of each block writes the
+// block's E8M0 byte to the step-major scale array xs (row r of M).
+template <int CH>
+__device__ inline void quantize_bf16_row_mx(const uint4 (&w)[CH], int64_t Kp, float tau,
+                                            uint8_t* __restrict__ qrow, uint8_t* __restrict__ xs,
+                                            int64_t M, int64_t r) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int64_t c = (int64_t(j) * kWave + lane) * 8;
+    const uint32_t q[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+    float ax[8];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ax[2 * i] = fminf(fabsf(__uint_as_float(q[i] << 16)), tau);
+      ax[2 * i + 1] = fminf(fabsf(__uint_as_float(q[i] & 0xffff0000u)), tau);
+      m = fmaxf(m, fmaxf(ax[2 * i], ax[2 * i + 1]));
+    }
+    // every lane takes part in the exchange; a block (four lanes) lies wholly
+    // below Kp or wholly past it
+    const int e = mx_exponent(quad_max(m));
+    if (c < Kp) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        word |= (mx_magnitude(ax[2 * i], e) | ((q[i] >> 12) & 0x8u)) << (8 * i);
+        word |= (mx_magnitude(ax[2 * i + 1], e) | ((q[i] >> 28) & 0x8u)) << (8 * i + 4);
+      }
+      *reinterpret_cast<uint32_t*>(qrow + c / 2) = word;
+      const int64_t b = c / 32;  // block of this chunk
+      if ((lane & 3) == 0) xs[(b / 4) * 4 * M + 4 * r + (b & 3)] = uint8_t(e + 127);
+    }
+  }
+}
+
 }  // namespace fp4lin

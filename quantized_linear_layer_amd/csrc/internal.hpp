@@ -19,11 +19,14 @@ hipError_t launch_quantize_weight_cleared(const uint16_t* W, int64_t K, int64_t 
 // With quantized set, rows that allow it are also quantized token-wise (Xq
 // with row stride ldq, scales sX, clamped to tau) by the compaction, and
 // *quantized says whether that happened; with quantized null, Xq is ignored.
+// With Xs set, that quantization is the micro-scaled one instead (block
+// scales into the step-major array Xs; sX unused).
 hipError_t launch_outlier_select(const void* A, bool bf16, int64_t M, int64_t K, int64_t lda,
                                  int64_t k, float* tau, int64_t capacity, int32_t* row,
                                  int32_t* col, float* val, int32_t* row_ptr, void* ws,
                                  hipStream_t stream, uint8_t* Xq = nullptr, int64_t ldq = 0,
-                                 float* sX = nullptr, bool* quantized = nullptr);
+                                 float* sX = nullptr, bool* quantized = nullptr,
+                                 uint8_t* Xs = nullptr);
 
 // Whole-layer forward, front half (select, quantization of A and of W) for
 // bf16 A and W with 16-byte aligned rows, K % 8 == 0 and K up to 8192

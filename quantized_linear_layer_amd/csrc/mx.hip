@@ -38,32 +38,6 @@ namespace {
 
 constexpr int kMxThreads = 256;
 
-// Least e >= -127 with 6 * 2^e >= amax (amax >= 0, finite). With
-// amax = m * 2^E, 1 <= m < 2: 1.5 * 2^E = 6 * 2^(E-2) covers amax exactly when
-// m <= 1.5, else 3 * 2^E = 6 * 2^(E-1) does. Zero and subnormal amax (and
-// every normal one below 6 * 2^-127) give -127.
-__device__ inline int mx_exponent(float amax) {
-  const uint32_t b = __float_as_uint(amax);
-  const int biased = int(b >> 23);
-  int e = ((b & 0x7fffffu) <= 0x400000u) ? biased - 129 : biased - 128;
-  if (biased == 0) e = -127;
-  return e < -127 ? -127 : e;
-}
-
-// Magnitude index of y = ax / 2^e: 4y = ax * 2^(2-e) is exact (ldexp never
-// rounds a result that reaches a midpoint; 4y <= 24), and the index is the
-// table lookup of the token-wise encoder at n = min(floor(4y), 20).
-__device__ inline uint32_t mx_magnitude(float ax, int e) {
-  uint32_t n = cvt_u32_sat(ldexpf(ax, 2 - e));
-  n = n < 20u ? n : 20u;
-  return uint32_t(e2m1_lut() >> (3u * n)) & 7u;
-}
-
-__device__ inline float quad_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, kWave));
-  return fmaxf(v, __shfl_xor(v, 2, kWave));
-}
-
 // Workgroup (bx, by) takes rows by, by + gridDim.y, ... and in each the chunks
 // c = bx * 256 + t, c + 256 * gridDim.x, ... (cpr = ldq / 4 chunks of 8 codes
 // per padded row, a multiple of 16). Four consecutive t hold one block and sit

@@ -650,14 +650,16 @@ __device__ inline void compact_words(const uint4 (&wv)[CH], int64_t r, uint32_t 
 // Forward path, 16-byte aligned bfloat16 rows with K % 8 == 0 whose padded
 // length fits one slab: the compaction of compact_rows_kernel and the
 // token-wise quantization of the row clamped to tau (quantize_bf16_row) from
-// one read of A.
-template <int CH>
+// one read of A; with kMx, its micro-scaled quantization instead
+// (quantize_bf16_row_mx, block scales into the step-major array Xs).
+template <int CH, bool kMx = false>
 __device__ __attribute__((always_inline)) inline void compact_quantize_rows_body(
     int64_t bid, const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
     const SelState* __restrict__ st, const float* __restrict__ tau_p,
     const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
-    float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX) {
+    float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX,
+    uint8_t* __restrict__ Xs = nullptr) {
   __shared__ uint32_t wsum[kRowWaves];
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);  // wave-uniform
   const int lane = threadIdx.x & (kWave - 1);
@@ -700,22 +702,27 @@ __device__ __attribute__((always_inline)) inline void compact_quantize_rows_body
       }
       uint32_t pos = base + before;
       compact_words<CH>(wv, r, tkey, tau, pos, cap, out_row, out_col, out_val);
-      quantize_bf16_row<CH>(wv, ldq * 2, tau, Xq + r * ldq, sX + r);
+      if constexpr (kMx)
+        quantize_bf16_row_mx<CH>(wv, ldq * 2, tau, Xq + r * ldq, Xs, M, r);
+      else
+        quantize_bf16_row<CH>(wv, ldq * 2, tau, Xq + r * ldq, sX + r);
       if (lane == 0) row_ptr[r + 1] = int32_t(base + before + own);
     }
     base += all;
   }
 }
 
-template <int CH>
+template <int CH, bool kMx = false>
 __global__ __launch_bounds__(kRowWaves * kWave) void compact_quantize_rows_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
     const SelState* __restrict__ st, const float* __restrict__ tau_p,
     const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
-    float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX) {
-  compact_quantize_rows_body<CH>(blockIdx.x, A, M, K, lda, rpw, st, tau_p, cnt, gsum, capacity,
-                                 row_ptr, out_row, out_col, out_val, Xq, ldq, sX);
+    float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX,
+    uint8_t* __restrict__ Xs) {
+  compact_quantize_rows_body<CH, kMx>(blockIdx.x, A, M, K, lda, rpw, st, tau_p, cnt, gsum,
+                                      capacity, row_ptr, out_row, out_col, out_val, Xq, ldq, sX,
+                                      Xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -796,12 +803,14 @@ __global__ void select_init_kernel(SelState* st, uint32_t* hist, int64_t nwords,
 }
 
 // Quantization outputs of the forward path: when Xq is set and the rows
-// qualify, the compaction also quantizes A and sets *done.
+// qualify, the compaction also quantizes A and sets *done; token-wise into sX,
+// or micro-scaled into the block scales Xs when Xs is set.
 struct RowQuant {
   uint8_t* Xq;
   int64_t ldq;
   float* sX;
   bool* done;
+  uint8_t* Xs;
 };
 
 template <class In, bool kFast, int CH, bool kPick>
@@ -820,9 +829,14 @@ void launch_rows(const typename In::T* A, int64_t M, int64_t K, int64_t lda, Sel
       switch (chunks_per_lane(rq.ldq * 2, 16)) {
 #define FP4LIN_CQ(CQ)                                                                            \
   case CQ:                                                                                       \
-    compact_quantize_rows_kernel<CQ><<<g, kRowWaves * kWave, 0, stream>>>(                       \
-        A16, M, K, lda, rpw, st, tau, cnt, gsum, capacity, row_ptr, row, col, val, rq.Xq,        \
-        rq.ldq, rq.sX);                                                                          \
+    if (rq.Xs != nullptr)                                                                        \
+      compact_quantize_rows_kernel<CQ, true><<<g, kRowWaves * kWave, 0, stream>>>(               \
+          A16, M, K, lda, rpw, st, tau, cnt, gsum, capacity, row_ptr, row, col, val, rq.Xq,      \
+          rq.ldq, rq.sX, rq.Xs);                                                                 \
+    else                                                                                         \
+      compact_quantize_rows_kernel<CQ><<<g, kRowWaves * kWave, 0, stream>>>(                     \
+          A16, M, K, lda, rpw, st, tau, cnt, gsum, capacity, row_ptr, row, col, val, rq.Xq,      \
+          rq.ldq, rq.sX, nullptr);                                                               \
     *rq.done = true;                                                                             \
     return;
         FP4LIN_CQ(1)
@@ -970,9 +984,9 @@ hipError_t launch_outlier_select(const void* A, bool bf16, int64_t M, int64_t K,
                                  int64_t k, float* tau, int64_t capacity, int32_t* row,
                                  int32_t* col, float* val, int32_t* row_ptr, void* ws,
                                  hipStream_t stream, uint8_t* Xq, int64_t ldq, float* sX,
-                                 bool* quantized) {
+                                 bool* quantized, uint8_t* Xs) {
   bool done = false;
-  const RowQuant rq{quantized != nullptr ? Xq : nullptr, ldq, sX, &done};
+  const RowQuant rq{quantized != nullptr ? Xq : nullptr, ldq, sX, &done, Xs};
   const int esz = bf16 ? 2 : 4;
   const bool fast = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && ((lda * esz) % 16 == 0) &&
                     (K % 8 == 0);
@@ -1008,7 +1022,7 @@ hipError_t forward_front(const uint16_t* A, int64_t M, int64_t K, int64_t lda, i
                                                           w.cnt, w.gsum);
     compact_quantize_rows_kernel<CH><<<dim3(unsigned(na)), kRowWaves * kWave, 0, stream>>>(
         A, M, K, lda, rpw, w.st, tau, w.cnt, w.gsum, capacity, row_ptr, row, col, val, Aq, ldq,
-        sA);
+        sA, nullptr);
     *w_done = false;
     return hipGetLastError();
   } else {

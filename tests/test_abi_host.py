@@ -257,6 +257,45 @@ def test_gemm_mx_errors():
     assert g(dA=c, W=FAKE, ldw=3) == _lib.ERR_SHAPE
 
 
+def test_workspace_layout_mx():
+    """The micro-scaled forward's layout: scale regions of rows * mx_scales_ld(K)
+    bytes, no overlap, 256-byte alignment, and no column-maxima scratch."""
+    for (M, K, N, dt, q) in [(256, 512, 512, 0, 0.99), (8192, 4096, 11008, 1, 0.99),
+                             (3, 5, 7, 1, 1.0)]:
+        o = _lib.ForwardOffsets()
+        assert L.fp4lin_forward_layout_mx(M, K, N, dt, q, ctypes.byref(o)) == 0
+        nb = L.fp4lin_mx_scales_ld(K)
+        ldq = O.packed_ld(K)
+        regions = sorted([
+            (o.tau, 4), (o.coo_row, 4 * max(o.capacity, 1)), (o.coo_col, 4 * max(o.capacity, 1)),
+            (o.coo_val, 4 * max(o.capacity, 1)), (o.row_ptr, 4 * (M + 1)), (o.Aq, M * ldq),
+            (o.sA, M * nb), (o.Wq, N * ldq), (o.sW, N * nb),
+            (o.scratch, L.fp4lin_select_workspace_bytes(M, K, dt))])
+        for (a, na), (b, _) in zip(regions, regions[1:]):
+            assert a + na <= b
+        for off, _ in regions:
+            assert off % 256 == 0
+        assert regions[-1][0] + regions[-1][1] <= o.total
+        assert L.fp4lin_workspace_bytes_mx(M, K, N, dt, q) == o.total
+    assert L.fp4lin_workspace_bytes_mx(0, 5, 7, 1, 0.5) == 0
+
+
+def test_forward_mx_errors():
+    def f(A=FAKE, W=FAKE, dt=1, M=4, K=8, N=4, lda=8, ldw=4, q=0.5, Y=FAKE, ldy=4, ws=FAKE,
+          wsb=1 << 30):
+        return L.fp4lin_forward_mx(A, W, dt, M, K, N, lda, ldw, q, Y, ldy, ws, wsb, None)
+    assert f(A=None) == _lib.ERR_NULL
+    assert f(ws=None) == _lib.ERR_NULL
+    assert f(dt=4) == _lib.ERR_DTYPE
+    assert f(N=0) == _lib.ERR_SHAPE
+    assert f(lda=2) == _lib.ERR_SHAPE
+    assert f(q=1.5) == _lib.ERR_QUANTILE
+    assert f(ws=MISALIGNED) == _lib.ERR_ALIGN
+    need = L.fp4lin_workspace_bytes_mx(4, 8, 4, 1, 0.5)
+    assert f(wsb=need - 1) == _lib.ERR_WORKSPACE
+    assert f(M=2 ** 20 - 1, K=2 ** 12, lda=2 ** 12, q=1.0, wsb=1 << 40) == _lib.ERR_SHAPE
+
+
 def forward(A=FAKE, W=FAKE, dt=1, M=4, K=8, N=4, lda=8, ldw=4, q=0.5, Y=FAKE, ldy=4, ws=FAKE,
             wsb=1 << 30):
     return L.fp4lin_forward(A, W, dt, M, K, N, lda, ldw, q, Y, ldy, ws, wsb, None)

@@ -155,7 +155,10 @@ def test_full_llama7b_ffn_up_mx(ql):
     Aq, As = ql.quantize_act_mx(A, tau)
     Wq, Ws = ql.quantize_weight_mx(W)
     Y = ql.gemm_mx(Aq, As, Wq, Ws, L.M, L.N, L.K, coo, W)
+    Yf = ql.forward_mx(A, W, L.q)          # the one-call forward, as bench.py times it
     torch.cuda.synchronize()
+    assert_bits_equal(host(Yf), host(Y), "forward_mx Y against the separate calls")
+    del Yf
     rows = sample_rows(L.M, seed=7)
     log(f"[full] {L.name} (micro-scaled): oracle")
     want, mag, otau, delta, qa, qw = O.forward_mx(L.A.f32, L.W.f32, L.q, rows=rows)

@@ -329,3 +329,58 @@ def test_wgrad_mx_public_calls(ql, dtype, M, K, N):
     assert_bits_equal(host(dq), qd[0], "dY codes")
     assert_bits_equal(scales_to_rows(host(ds), N), qd[1], "dY scale bytes")
     assert_within_accumulation_bound(host(dW).astype(np.float64), want, mag, M)
+
+
+# ---------------------------------------------------------------------------
+# fp4lin_forward_mx: the whole micro-scaled layer in one call
+# ---------------------------------------------------------------------------
+def forward_mx_views(ql, ws, M, K, N, dt, q):
+    o = ql.forward_layout_mx(M, K, N, dt, q)
+    nb = ql.mx_scales_ld(K)
+    ldq = ql.packed_ld(K)
+    b = ws
+    tau = b[o.tau:o.tau + 4].view(torch().float32)
+    rp = b[o.row_ptr:o.row_ptr + 4 * (M + 1)].view(torch().int32)
+    Aq = b[o.Aq:o.Aq + M * ldq].view(M, ldq)
+    As = b[o.sA:o.sA + M * nb]
+    Wq = b[o.Wq:o.Wq + N * ldq].view(N, ldq)
+    Ws = b[o.sW:o.sW + N * nb]
+    return o, tau, rp, Aq, As, Wq, Ws
+
+
+@pytest.mark.parametrize("dtype,ld", [(wl.BF16, None), (wl.BF16, 4104), (wl.F32, None)])
+@pytest.mark.parametrize("M,K,N", [(37, 1000, 300), (300, 4096, 520), (70, 8192, 129),
+                                   (33, 8200, 64)])
+def test_forward_mx_matches_stage_calls(ql, dtype, ld, M, K, N):
+    """Every intermediate and Y of fp4lin_forward_mx are bit-identical to the
+    separate calls (the fused compaction + block quantization for aligned bf16
+    rows up to 8192 columns, the separate quantizer otherwise), and Y matches
+    the oracle."""
+    if ld is not None and ld < K:
+        pytest.skip("leading dimension below K")
+    log(f"forward_mx {dtype} ld={ld} {M}x{K}x{N}")
+    t = torch()
+    rng = np.random.default_rng(M + K + N)
+    A = wl.random_matrix(rng, M, K, dtype, dist="t3")
+    W = wl.random_matrix(rng, K, N, dtype, scale=0.02)
+    Ad, Wd = to_device(A), to_device(W)
+    if ld is not None:
+        Ad = padded(Ad, ld)
+    q = 0.98
+    Y, ws = ql.forward_mx(Ad, Wd, q, return_workspace=True)
+    tau, coo = ql.outlier_select(Ad, q)
+    Aq, As = ql.quantize_act_mx(Ad, tau)
+    Wq, Ws = ql.quantize_weight_mx(Wd)
+    Y2 = ql.gemm_mx(Aq, As, Wq, Ws, M, N, K, coo, Wd)
+    t.cuda.synchronize()
+    dt = ql.BF16 if dtype == wl.BF16 else ql.F32
+    o, ftau, rp, fAq, fAs, fWq, fWs = forward_mx_views(ql, ws, M, K, N, dt, q)
+    assert_bits_equal(host(ftau), host(tau), "tau")
+    assert_bits_equal(host(rp), host(coo.row_ptr), "row_ptr")
+    assert_bits_equal(host(fAq), host(Aq), "A codes")
+    assert_bits_equal(host(fAs), host(As).reshape(-1), "A scale bytes")
+    assert_bits_equal(host(fWq), host(Wq), "W codes")
+    assert_bits_equal(host(fWs), host(Ws).reshape(-1), "W scale bytes")
+    assert_bits_equal(host(Y), host(Y2), "Y")
+    want, _, _, _, _, _ = O.forward_mx(A.f32, W.f32, q)
+    assert O.rel_fro(host(Y), want) <= Y_TOL
