@@ -18,7 +18,11 @@
 // row (per column of W) holds the bytes of its blocks 4s .. 4s+3, low byte
 // first, and the words of consecutive rows are adjacent: the byte of block b
 // of row i (of R rows) is at (b / 4) * 4R + 4i + b % 4. The GEMM then reads the
-// scales of 32 consecutive rows for one step as 128 contiguous bytes.
+// scales of 64 consecutive rows for one step as 256 contiguous bytes.
+//
+// The block exponent and the element encoder (mx_exponent, mx_magnitude) are
+// in device_common.hpp, shared with the forward's compaction kernel, which
+// block-quantizes the rows of A it already holds (quantize_bf16_row_mx).
 //
 // Rows (activations): one thread per 8-code chunk of a padded row, so four
 //   consecutive lanes hold one block and its max is two lane exchanges away;
