@@ -8,6 +8,7 @@ import math
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -334,3 +335,13 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(hip) == 1, sorted(hip)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: --gpus 2 exits with status 2 and says so,
+    before touching any device."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
