@@ -566,3 +566,130 @@ def test_mx_dgrad_wgrad_exact_on_grid():
     dW, _, _, _ = O.wgrad_mx(A, dY2)
     assert np.array_equal(dW, A.astype(np.float64).T @ dY2.astype(np.float64))
     assert dW.shape == (K, N) and dX.shape == (M, K)
+
+
+# ---------------------------------------------------------------------------
+# The micro-scaled whole-layer forward: clamp at tau, block quantization of the
+# clamped A, the block-scaled product and the compensation term (reading R11
+# with the outlier and compensation paragraphs of the FP4 training write-up)
+# ---------------------------------------------------------------------------
+def _mx_hand_case():
+    """2 x 64 A with two outliers, 64 x 2 W, q = 126/128 (worked in the test)."""
+    A = np.zeros((2, 64), np.float32)
+    A[0, 0], A[0, 1], A[0, 2], A[0, 40] = 10.0, 1.0, -0.75, 2.5
+    A[1, 5], A[1, 33], A[1, 63] = -3.0, 0.625, -7.0
+    W = np.zeros((64, 2), np.float32)
+    for k, (w0, w1) in {0: (1, 2), 1: (0.5, -1), 2: (2, 0.25), 5: (1, 1), 33: (4, -0.5),
+                        40: (-1, 3), 63: (0.5, 2)}.items():
+        W[k] = (w0, w1)
+    return A, W, 126 / 128
+
+
+def test_mx_clamped_activation_quantizer_by_hand():
+    """quantize_act_mx with tau: the block exponents and codes of the clamped
+    rows, worked by hand, and how they differ from the unclamped rows."""
+    A, _, _ = _mx_hand_case()
+    Aq, sb, codes, e = O.quantize_act_mx(A, np.float32(3.0))
+    # clamped row 0, block 0: 10 -> 3, so max 3 = 6 * 2^-1 -> e = -1 and
+    # y = 2|x|: 3 -> 6 (mag 7), 1 -> 2 (mag 4), -0.75 -> 1.5 (mag 3, sign set);
+    # block 1: max 2.5, 6 * 2^-2 = 1.5 < 2.5 <= 3 -> e = -1, y = 5 ties -> 6
+    assert e.tolist() == [[-1, -1, -127, -127], [-1, -1, -127, -127]]
+    assert sb.tolist() == [[126, 126, 0, 0], [126, 126, 0, 0]]
+    assert codes[0, [0, 1, 2, 40]].tolist() == [7, 4, 11, 7]
+    # row 1: -3 (== tau, kept) -> y = 6 -> 15; 0.625 -> y = 1.25 ties -> 1.5
+    # (mag 3); -7 -> -3 -> 15
+    assert codes[1, [5, 33, 63]].tolist() == [15, 3, 15]
+    assert np.count_nonzero(codes) == 7
+    assert Aq[0, 0] == 0x47 and Aq[0, 1] == 0x0B and Aq[1, 31] == 0xF0
+    # unclamped: block 0 of row 0 has max 10 -> e = 1 (6 < 10 <= 12), y = |x|/2:
+    # 10 -> 5 ties -> 6 (7), 1 -> 0.5 (1), -0.75 -> 0.375 -> 0.5 (1, sign set)
+    _, sb_u, codes_u, e_u = O.quantize_act_mx(A)
+    assert e_u[0, 0] == 1 and sb_u[0, 0] == 128
+    assert codes_u[0, [0, 1, 2]].tolist() == [7, 1, 9]
+    # row 1 block 1 unclamped: max 7 -> e = 1, 0.625 / 2 = 0.3125 -> 0.5 (1),
+    # 7 / 2 = 3.5 ties -> 4 (6)
+    assert e_u[1, 1] == 1 and codes_u[1, [33, 63]].tolist() == [1, 14]
+
+
+def test_mx_forward_hand_worked():
+    """The whole micro-scaled forward on the 2 x 64 x 2 case, worked by hand:
+    n = 128, k = ceil(126) - 1 = 125; sorted |A| is 121 zeros, .625, .75, 1,
+    2.5, 3, 7, 10, so tau = 3 and the clamped set is {10, -7} (strict: -3 stays)."""
+    A, W, q = _mx_hand_case()
+    Y, mag, tau, delta, qa, qw = O.forward_mx(A, W, q)
+    assert tau == 3.0
+    assert delta.row.tolist() == [0, 1] and delta.col.tolist() == [0, 63]
+    assert delta.val64.tolist() == [7.0, -4.0] and delta.row_ptr.tolist() == [0, 1, 2]
+    # W is block-exact: column 0 blocks max 2 (e = -1) and 4 (e = 0); column 1
+    # max 2 (e = -1) and 3 (e = -1); every value is a grid value times 2^e
+    assert qw[3].tolist() == [[-1, 0, -127, -127], [-1, -1, -127, -127]]
+    deq_w = O.decode(qw[2]) * np.repeat(np.exp2(qw[3]), 32, axis=1)[:, :64]
+    assert np.array_equal(deq_w.T, W.astype(np.float64))
+    # Q(A_c): row 0 = 3 (k0), 1 (k1), -0.75 (k2), 3 (k40, 2.5 rounded up);
+    # row 1 = -3 (k5), 0.75 (k33), -3 (k63)
+    # Y0 row 0: 3*1 + 1*.5 - .75*2 + 3*(-1) = -1;  3*2 - 1 - .1875 + 9 = 13.8125
+    # Y0 row 1: -3 + .75*4 - 3*.5 = -1.5;  -3 - .375 - 6 = -9.375
+    # dA W: row 0 += 7 * W[0] = (7, 14); row 1 += -4 * W[63] = (-2, -8)
+    assert Y.tolist() == [[6.0, 27.8125], [-3.5, -17.375]]
+    # the exact product differs by the roundings 2.5 -> 3 (row 0, times W[40])
+    # and 0.625 -> 0.75 (row 1, times W[33])
+    exact = A.astype(np.float64) @ W.astype(np.float64)
+    assert np.array_equal(exact - Y, np.array([[0.5, -1.5], [-0.5, 0.0625]]))
+    assert np.all(mag >= np.abs(Y - np.array([[7.0, 14.0], [-2.0, -8.0]])))
+
+
+def _mx_block_exact_with_outliers(rng, M, K, n_out):
+    """M x K values whose clamp at tau = 6 is block-exact for the micro-scaled
+    quantizer: grid values times 2^e per 32-block (e <= 0, so nothing but the
+    planted outliers exceeds 6), every block holding +-6 * 2^e, and n_out
+    outliers (|a| > 6, dyadic) planted in blocks with e = 0."""
+    grid = np.array(GRID)
+    nb = K // 32
+    v = grid[rng.integers(0, 8, (M, K))] * rng.choice([-1.0, 1.0], (M, K))
+    e = rng.integers(-5, 1, (M, nb))
+    v.reshape(M, nb, 32)[:, :, 3] = 6.0
+    pos = rng.choice(M * K, n_out, replace=False)
+    r, c = np.divmod(pos, K)
+    e[r, c // 32] = 0                       # outlier blocks clamp to +-6 * 2^0
+    v = (v.reshape(M, nb, 32) * np.exp2(e)[:, :, None]).reshape(M, K)
+    out = (6.0 + rng.integers(1, 400, n_out) / 4.0) * rng.choice([-1.0, 1.0], n_out)
+    keep = (c % 32) != 3                    # never overwrite a block's +-6 anchor
+    v[r[keep], c[keep]] = out[keep]
+    return v.astype(np.float32), int(keep.sum())
+
+
+@pytest.mark.parametrize("M,K,N,n_out", [(16, 96, 40, 9), (40, 256, 24, 30)])
+def test_mx_forward_exact_on_block_exact_clamp(M, K, N, n_out):
+    """With tau = 6 placed by q and A_clamped block-exact, Q(A_clamped) is
+    A_clamped and Q(W) is W, so Y = A_c W + dA W = A W exactly. Quantizing the
+    unclamped A, a tau that differs between the clamp and dA, a dropped or
+    negated dA, or a transposed operand each break the equality."""
+    rng = np.random.default_rng(M + K + N)
+    A, n_clamped = _mx_block_exact_with_outliers(rng, M, K, n_out)
+    W = _mx_grid_exact(rng, K, N, along_rows=False)
+    n = M * K
+    q = (n - n_clamped) / n                 # k = n - n_clamped - 1: the largest |a| <= 6
+    Y, _, tau, delta, qa, _ = O.forward_mx(A, W, q)
+    assert tau == 6.0
+    big = np.abs(A) > 6.0
+    assert delta.nnz == n_clamped == int(big.sum())
+    assert np.array_equal(delta.row * K + delta.col, np.flatnonzero(big))
+    # every outlier block's exponent is that of the clamped block (0), not of
+    # the outlier (e >= 1)
+    assert np.all(qa[3][np.nonzero(big)[0], np.nonzero(big)[1] // 32] == 0)
+    assert np.array_equal(Y, A.astype(np.float64) @ W.astype(np.float64))
+    # the clamp matters: without it the outlier blocks get coarser exponents
+    Y_noclamp, *_ = O.forward_mx(A, W, 1.0)
+    assert not np.array_equal(Y_noclamp, Y)
+
+
+def test_mx_forward_q1_block_exact_is_plain_product():
+    """q = 1 clamps nothing (tau = max |a|, dA empty): block-exact A and W give
+    Y = A W exactly, on a non-square shape with a ragged K."""
+    rng = np.random.default_rng(12)
+    M, K, N = 24, 160, 36
+    A = _mx_grid_exact(rng, M, K, along_rows=True)
+    W = _mx_grid_exact(rng, K, N, along_rows=False)
+    Y, _, tau, delta, _, _ = O.forward_mx(A, W, 1.0)
+    assert delta.nnz == 0 and tau == np.abs(A).max()
+    assert np.array_equal(Y, A.astype(np.float64) @ W.astype(np.float64))
