@@ -45,8 +45,9 @@
  *   - Pointers are device pointers owned by the caller unless marked "host".
  *     The library never allocates, frees or keeps a pointer after return, holds
  *     no global state (apart from each host thread's record of its last HIP
- *     launch result, see fp4lin_last_hip_error) and is safe to call from
- *     several host threads.
+ *     launch result, see fp4lin_last_hip_error, and the static device scratch
+ *     of fp4lin_outlier_select_noalloc) and is safe to call from several host
+ *     threads.
  *   - All device work is enqueued asynchronously, in order, on `stream`
  *     (0 = the null stream). Nothing is read back and there is no host
  *     synchronisation: results are valid once the caller synchronises the
@@ -78,7 +79,8 @@ typedef enum {
   FP4LIN_ERR_CAPACITY = 5,   /* COO capacity < M*K - 1 - k                      */
   FP4LIN_ERR_ALIGN = 6,      /* a pointer that must be 16-byte aligned is not   */
   FP4LIN_ERR_WORKSPACE = 7,  /* workspace smaller than the *_workspace_bytes   */
-  FP4LIN_ERR_LAUNCH = 8      /* the HIP runtime rejected a kernel launch        */
+  FP4LIN_ERR_LAUNCH = 8,     /* the HIP runtime rejected a kernel launch        */
+  FP4LIN_ERR_SCRATCH = 9     /* beyond the allocation-free call's static scratch */
 } fp4lin_status;
 
 typedef enum { FP4LIN_F32 = 0, FP4LIN_BF16 = 1 } fp4lin_dtype;
@@ -163,6 +165,28 @@ const char* fp4lin_last_hip_error_name(void);
 fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, int64_t K,
                                     int64_t lda, double q, float* tau, fp4lin_coo dA,
                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Allocation-free variant of fp4lin_outlier_select, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same operation and outputs, with the
+ * select's scratch taken from a static device array of 8 MiB that the library
+ * holds on every GPU it runs on until the process ends, instead of a workspace
+ * argument. The call allocates and frees nothing; on its first call for a
+ * device it looks up that device's copy of the array (the device of `stream`,
+ * or the current device for the null stream).
+ *   A, dt, M, K, lda, q, tau, dA, stream   as in fp4lin_outlier_select
+ * The select must fit the scratch: fp4lin_select_workspace_bytes(M, K, dt) at
+ * most 8 MiB, i.e. M up to 1 865 152 rows for bfloat16 and 2 088 896 rows for
+ * float32, else FP4LIN_ERR_SCRATCH (checked before anything is enqueued).
+ * Every call on a GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (on different streams, or from several host threads without ordering) race
+ * and give undefined results; calls ordered on one stream are safe. No kernel
+ * relies on the scratch's contents from an earlier call.
+ * Errors: NULL, SHAPE, DTYPE, QUANTILE, CAPACITY, SCRATCH, LAUNCH (also when
+ * the device or its scratch address cannot be determined). */
+fp4lin_status fp4lin_outlier_select_noalloc(const void* A, fp4lin_dtype dt, int64_t M,
+                                            int64_t K, int64_t lda, double q, float* tau,
+                                            fp4lin_coo dA, hipStream_t stream);
 
 /* Token-wise activation quantization (granularity, rounding and ScaleShift
  * paragraphs): each row of X, clamped to [-tau, tau] when tau is given, is

@@ -17,7 +17,7 @@ from ._lib import BF16, F32, Coo, ForwardOffsets
 __all__ = [
     "Fp4linError", "lib", "packed_ld", "quantile_rank", "select_workspace_bytes",
     "weight_workspace_bytes", "workspace_bytes", "forward_layout",
-    "fp4lin_outlier_select", "fp4lin_quantize_act", "fp4lin_quantize_weight", "fp4lin_gemm",
+    "fp4lin_outlier_select", "fp4lin_outlier_select_noalloc", "fp4lin_quantize_act", "fp4lin_quantize_weight", "fp4lin_gemm",
     "fp4lin_sparse_add", "fp4lin_forward", "outlier_select", "quantize_act", "quantize_weight", "gemm", "forward",
     "CooBuffers", "mx_scales_ld", "fp4lin_quantize_act_mx", "fp4lin_quantize_weight_mx",
     "fp4lin_gemm_mx", "quantize_act_mx", "quantize_weight_mx", "gemm_mx",
@@ -137,6 +137,15 @@ def fp4lin_outlier_select(A, q, tau, coo: CooBuffers, ws, stream=None):
                                        _dev(tau, "tau"), coo.struct(), _dev(ws, "ws"),
                                        ws.numel() * ws.element_size(), _stream(stream)),
            "fp4lin_outlier_select")
+
+
+def fp4lin_outlier_select_noalloc(A, q, tau, coo: CooBuffers, stream=None):
+    M, K, lda = _matrix(A, "A")
+    _dev(coo.row, "coo")
+    _check(lib().fp4lin_outlier_select_noalloc(_dev(A, "A"), _dtype_code(A), M, K, lda,
+                                               float(q), _dev(tau, "tau"), coo.struct(),
+                                               _stream(stream)),
+           "fp4lin_outlier_select_noalloc")
 
 
 def fp4lin_quantize_act(X, tau, Xq, sX, stream=None):

@@ -14,7 +14,7 @@ c_int = ctypes.c_int
 
 # enum values of fp4lin_status / fp4lin_dtype
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_QUANTILE, ERR_CAPACITY, ERR_ALIGN, ERR_WORKSPACE, \
-    ERR_LAUNCH = range(9)
+    ERR_LAUNCH, ERR_SCRATCH = range(10)
 F32, BF16 = 0, 1
 
 
@@ -43,6 +43,8 @@ SIGNATURES = {
     "fp4lin_last_hip_error_name": (ctypes.c_char_p, []),
     "fp4lin_outlier_select": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_dbl, c_ptr, Coo,
                                       c_ptr, c_size, c_ptr]),
+    "fp4lin_outlier_select_noalloc": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_dbl, c_ptr,
+                                              Coo, c_ptr]),
     "fp4lin_quantize_act": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr, c_ptr,
                                     c_ptr]),
     "fp4lin_quantize_weight": (c_int, [c_ptr, c_int, c_i64, c_i64, c_i64, c_ptr, c_ptr, c_ptr,

@@ -3,6 +3,7 @@
 // frees, synchronises or reads device memory.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fp4lin.h"
 #include "internal.hpp"
@@ -160,6 +161,7 @@ const char* fp4lin_status_str(fp4lin_status s) {
     case FP4LIN_ERR_ALIGN: return "pointer not 16-byte aligned";
     case FP4LIN_ERR_WORKSPACE: return "workspace too small";
     case FP4LIN_ERR_LAUNCH: return "kernel launch failed";
+    case FP4LIN_ERR_SCRATCH: return "input needs more than the static scratch of the allocation-free call";
   }
   return "unknown status";
 }
@@ -168,15 +170,11 @@ const char* fp4lin_status_str(fp4lin_status s) {
 
 namespace {
 
-// fp4lin_outlier_select; with quantized set, the forward path's token-wise
-// quantization of A (Xq, sX) is done by the same kernels where the rows allow
-// it, and *quantized says whether it was.
-fp4lin_status select_impl(const void* A, fp4lin_dtype dt, int64_t M, int64_t K, int64_t lda,
-                          double q, float* tau, fp4lin_coo dA, void* ws, size_t ws_bytes,
-                          hipStream_t stream, uint8_t* Xq, float* sX, bool* quantized,
-                          uint8_t* Xs = nullptr) {
+// The select's argument checks apart from the workspace.
+fp4lin_status select_check(const void* A, fp4lin_dtype dt, int64_t M, int64_t K, int64_t lda,
+                           double q, const float* tau, const fp4lin_coo& dA) {
   if (A == nullptr || tau == nullptr || dA.row == nullptr || dA.col == nullptr ||
-      dA.val == nullptr || dA.row_ptr == nullptr || ws == nullptr)
+      dA.val == nullptr || dA.row_ptr == nullptr)
     return FP4LIN_ERR_NULL;
   if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
   if (!ok_dim(M) || !ok_dim(K) || lda < K) return FP4LIN_ERR_SHAPE;
@@ -187,11 +185,70 @@ fp4lin_status select_impl(const void* A, fp4lin_dtype dt, int64_t M, int64_t K, 
   const int64_t cap = needed_capacity(n, k);
   if (cap >= kMaxDim) return FP4LIN_ERR_SHAPE;
   if (dA.capacity < cap) return FP4LIN_ERR_CAPACITY;
+  return FP4LIN_OK;
+}
+
+// fp4lin_outlier_select; with quantized set, the forward path's token-wise
+// quantization of A (Xq, sX) is done by the same kernels where the rows allow
+// it, and *quantized says whether it was.
+fp4lin_status select_impl(const void* A, fp4lin_dtype dt, int64_t M, int64_t K, int64_t lda,
+                          double q, float* tau, fp4lin_coo dA, void* ws, size_t ws_bytes,
+                          hipStream_t stream, uint8_t* Xq, float* sX, bool* quantized,
+                          uint8_t* Xs = nullptr) {
+  if (ws == nullptr) return FP4LIN_ERR_NULL;
+  const fp4lin_status c = select_check(A, dt, M, K, lda, q, tau, dA);
+  if (c != FP4LIN_OK) return c;
   if (!aligned16(ws)) return FP4LIN_ERR_ALIGN;
   if (ws_bytes < select_ws(M, dt)) return FP4LIN_ERR_WORKSPACE;
   return launch_status(fp4lin::launch_outlier_select(
-      A, dt == FP4LIN_BF16, M, K, lda, k, tau, dA.capacity, dA.row, dA.col, dA.val, dA.row_ptr,
-      ws, stream, Xq, fp4lin_packed_ld(K), sX, quantized, Xs));
+      A, dt == FP4LIN_BF16, M, K, lda, fp4lin_quantile_rank(M * K, q), tau, dA.capacity,
+      dA.row, dA.col, dA.val, dA.row_ptr, ws, stream, Xq, fp4lin_packed_ld(K), sX, quantized,
+      Xs));
+}
+
+// ---- allocation-free select ---------------------------------------------------
+// fp4lin_outlier_select_noalloc keeps the select's scratch (selection state,
+// histograms, per-row counts) in this array: one copy per GPU the library
+// runs on, held until the process ends. In host code its name is only a
+// host-side stand-in; the device address of each GPU's copy is looked up once
+// per device, with that device current, and only that address is used.
+// None of the select's kernels relies on the scratch being cleared, so the
+// contents a previous call left are harmless.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];
+
+// This GPU's copy of the scratch: the device of `stream` (the current device
+// for the null stream), looked up on the first call for that device.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_addr[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev) {
+      e = hipSetDevice(dev);
+      if (e != hipSuccess) return e;
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -203,6 +260,19 @@ fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, i
                                     size_t ws_bytes, hipStream_t stream) {
   return select_impl(A, dt, M, K, lda, q, tau, dA, ws, ws_bytes, stream, nullptr, nullptr,
                      nullptr);
+}
+
+fp4lin_status fp4lin_outlier_select_noalloc(const void* A, fp4lin_dtype dt, int64_t M,
+                                            int64_t K, int64_t lda, double q, float* tau,
+                                            fp4lin_coo dA, hipStream_t stream) {
+  const fp4lin_status c = select_check(A, dt, M, K, lda, q, tau, dA);
+  if (c != FP4LIN_OK) return c;
+  if (select_ws(M, dt) > kNoAllocScratchBytes) return FP4LIN_ERR_SCRATCH;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(stream, &ws);
+  if (e != hipSuccess) return launch_status(e);
+  return select_impl(A, dt, M, K, lda, q, tau, dA, ws, kNoAllocScratchBytes, stream, nullptr,
+                     nullptr, nullptr);
 }
 
 fp4lin_status fp4lin_quantize_act(const void* X, fp4lin_dtype dt, int64_t M, int64_t K,

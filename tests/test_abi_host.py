@@ -138,6 +138,31 @@ def test_select_errors():
     assert select(wsb=16) == _lib.ERR_WORKSPACE
 
 
+def select_noalloc(A=FAKE, dt=1, M=4, K=8, lda=8, q=0.5, tau=FAKE, dA=None):
+    dA = coo(100) if dA is None else dA
+    return L.fp4lin_outlier_select_noalloc(A, dt, M, K, lda, q, tau, dA, None)
+
+
+def test_select_noalloc_errors():
+    """The allocation-free select checks its arguments like the workspace one,
+    then refuses inputs whose scratch exceeds its 8 MiB static array, before it
+    looks up the device or enqueues anything."""
+    assert select_noalloc(A=None) == _lib.ERR_NULL
+    assert select_noalloc(tau=None) == _lib.ERR_NULL
+    assert select_noalloc(dA=coo(100, null="row_ptr")) == _lib.ERR_NULL
+    assert select_noalloc(dt=5) == _lib.ERR_DTYPE
+    assert select_noalloc(M=0) == _lib.ERR_SHAPE
+    assert select_noalloc(q=1.5) == _lib.ERR_QUANTILE
+    assert select_noalloc(dA=coo(15)) == _lib.ERR_CAPACITY
+    scratch = 8 << 20
+    for dt, rows in ((1, 1_865_152), (0, 2_088_896)):
+        assert L.fp4lin_select_workspace_bytes(rows, 16, dt) == scratch
+        assert L.fp4lin_select_workspace_bytes(rows + 1, 16, dt) > scratch
+        assert select_noalloc(dt=dt, M=rows + 1, K=16, lda=16, dA=coo((rows + 1) * 16)) == \
+            _lib.ERR_SCRATCH
+    assert "static scratch" in L.fp4lin_status_str(_lib.ERR_SCRATCH).decode()
+
+
 def quant_act(X=FAKE, dt=1, M=4, K=8, ldx=8, tau=None, Xq=FAKE, sX=FAKE):
     return L.fp4lin_quantize_act(X, dt, M, K, ldx, tau, Xq, sX, None)
 
