@@ -220,10 +220,15 @@ fp4lin_status fp4lin_quantize_weight(const void* W, fp4lin_dtype dt, int64_t K, 
  *   acc[i,j] = sum_k v(Aq[i,k]) v(Bq[j,k])            (exact in fp32)
  *   Y[i,j]   = RN32(RN32(acc*sA[i])*sB[j]) + s[i,j],
  *   s[i,j]   = sum_{(i,k) in dA} val*W[k,j], accumulated from 0 in ascending k
- *              with fp32 fused multiply-add, then added once to the product.
+ *              with fp32 fused multiply-add, then added once to the product
+ *              (rows without non-zeros: the product as it is).
+ * The compensation runs in the same kernel's epilogue (compensation
+ * paragraph: dA W added back), so Y is written once.
  *   Aq, sA   device, M x packed_ld(K) bytes, M floats
  *   Bq, sB   device, N x packed_ld(K) bytes (N-major), N floats
- *   dA       host pointer to a COO descriptor, or NULL for no compensation
+ *   dA       host pointer to a COO descriptor, or NULL for no compensation;
+ *            its row, col, val and row_ptr arrays are read and must describe
+ *            one row-major matrix, as fp4lin_outlier_select writes them
  *   W        device K x N (dtype wdt, leading dimension ldw), required exactly
  *            when dA is given (the unquantized weight dA multiplies);
  *            K*ldw*sizeof(dtype) must be below 2^31
@@ -240,7 +245,9 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
  * write-up): Y[i,:] = Y[i,:] + s[i,:], where s is the sum over row i's
  * non-zeros of dA, ascending k, of val * W[k,:], accumulated from 0 with fp32
  * fused multiply-add. Rows without non-zeros are not touched. fp4lin_gemm with
- * a non-NULL dA is exactly fp4lin_gemm with dA = NULL followed by this call.
+ * a non-NULL dA gives bit for bit what fp4lin_gemm with dA = NULL followed by
+ * this call gives (it computes the same sum in its epilogue, without reading
+ * Y back).
  *   dA       host pointer to a COO descriptor (device arrays; row is not read)
  *   W        device K x N weight (dtype wdt, leading dimension ldw); column
  *            indices of dA must be < K

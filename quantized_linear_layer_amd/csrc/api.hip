@@ -305,13 +305,15 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
   if (Aq == nullptr || sA == nullptr || Bq == nullptr || sB == nullptr || Y == nullptr)
     return FP4LIN_ERR_NULL;
   if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldy < N) return FP4LIN_ERR_SHAPE;
-  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, false, 0, 0};
+  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, nullptr, false, 0, 0, 0};
   if (dA != nullptr) {
-    if (dA->row_ptr == nullptr || dA->col == nullptr || dA->val == nullptr || W == nullptr)
+    if (dA->row_ptr == nullptr || dA->row == nullptr || dA->col == nullptr ||
+        dA->val == nullptr || W == nullptr)
       return FP4LIN_ERR_NULL;
     if (bad_dtype(wdt)) return FP4LIN_ERR_DTYPE;
     if (ldw < N || !weight_addressable(K, ldw, wdt)) return FP4LIN_ERR_SHAPE;
-    sp = fp4lin::SparseArgs{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K};
+    sp = fp4lin::SparseArgs{dA->row_ptr, dA->row, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K,
+                            dA->capacity};
   }
   // packed operands are addressed with 32-bit byte offsets
   const int64_t ldq = fp4lin_packed_ld(K);
@@ -331,7 +333,8 @@ fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtyp
   if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldw < N || ldy < N ||
       !weight_addressable(K, ldw, wdt))
     return FP4LIN_ERR_SHAPE;
-  const fp4lin::SparseArgs sp{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K};
+  const fp4lin::SparseArgs sp{dA->row_ptr, dA->row, dA->col, dA->val, W, wdt == FP4LIN_BF16,
+                              ldw,         K,       dA->capacity};
   return launch_status(fp4lin::launch_sparse_add(sp, M, N, Y, ldy, stream));
 }
 
@@ -369,13 +372,15 @@ fp4lin_status fp4lin_gemm_mx(const uint8_t* Aq, const uint8_t* As, const uint8_t
   if (Aq == nullptr || As == nullptr || Bq == nullptr || Bs == nullptr || Y == nullptr)
     return FP4LIN_ERR_NULL;
   if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldy < N) return FP4LIN_ERR_SHAPE;
-  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, false, 0, 0};
+  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, nullptr, false, 0, 0, 0};
   if (dA != nullptr) {
-    if (dA->row_ptr == nullptr || dA->col == nullptr || dA->val == nullptr || W == nullptr)
+    if (dA->row_ptr == nullptr || dA->row == nullptr || dA->col == nullptr ||
+        dA->val == nullptr || W == nullptr)
       return FP4LIN_ERR_NULL;
     if (bad_dtype(wdt)) return FP4LIN_ERR_DTYPE;
     if (ldw < N || !weight_addressable(K, ldw, wdt)) return FP4LIN_ERR_SHAPE;
-    sp = fp4lin::SparseArgs{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K};
+    sp = fp4lin::SparseArgs{dA->row_ptr, dA->row, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K,
+                            dA->capacity};
   }
   // packed operands and scale rows are addressed with 32-bit byte offsets
   const int64_t ldq = fp4lin_packed_ld(K);

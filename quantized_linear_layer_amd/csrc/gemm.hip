@@ -14,7 +14,14 @@
 // Epilogue (the granularity paragraph: row scales of A and column scales of W
 // factor out of the K reduction, so they are applied once, after it):
 //   Y[i,j] = RN32(RN32(acc[i,j] * sA[i]) * sB[j])
-// The sparse compensation term is added afterwards by spmm.hip.
+// With the sparse compensation matrix dA (the outlier and compensation
+// paragraphs: dA = A - A_clamped, non-zero only where A was clamped, its
+// product with the unquantized weight added back), the same epilogue adds
+//   s[i,j] = sum over row i's non-zeros, k ascending, of val * W[k,j]
+// (fp32 fused multiply-add from 0) to each element of a row that has
+// non-zeros, before Y's only store: Y = Y0 + s. The result is bit-identical to
+// the scaled product followed by the separate compensation kernel (spmm.hip),
+// without reading Y back.
 //
 // Micro-scaled variant (kMx; the micro-scaling lecture "FP4量化训练的硬件挑战：
 // NVIDIA Blackwell架构上的微缩放格式（Micro-scaling）实现", section 3, with the E8M0
@@ -54,6 +61,17 @@
 //    instructions than storing from the MFMA layout). The stores are
 //    non-temporal: the output stream is not kept in L2 at the expense of the
 //    operand tiles that concurrent workgroups re-read.
+//  * With the compensation, the tile leaves in four chunks of 32 rows x all
+//    256 columns (each wave row's 16 x 256 block in its own stage buffer).
+//    After a barrier each wave finishes 8 whole rows of a chunk: a lane owns 4
+//    consecutive columns, so a non-zero costs one 8-byte (bf16 W) or 16-byte
+//    (fp32 W) gather per lane, addressed with the W row offset in the scalar
+//    operand of a buffer load, and its column and value come from scalar
+//    loads. The non-zeros of a wave's 8 consecutive rows are one contiguous
+//    range of the row-major COO; they are gathered in groups of 8, two groups
+//    in flight, across row boundaries. Each row is stored once, 1 KiB per
+//    wave instruction. While one workgroup gathers, the other workgroup on the
+//    CU keeps the matrix core busy.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -107,11 +125,20 @@ __device__ inline int swz(int r, int c) {
 
 // Tile order: groups of G tile rows sweeping across N; each XCD takes a
 // contiguous run of that order (a bijection from workgroup id to tile).
+// kColumns: the tile columns one after another instead, each swept down M, so
+// that the tiles an XCD runs together share one 256-column strip of the
+// operands and of W (the compensation's gathers then stay in that XCD's L2).
+template <bool kColumns = false>
 __device__ inline void tile_coords(int bid, int nblocks, int tiles_m, int& tm, int& tn) {
   const int xcd = bid & 7;
   const int idx = bid >> 3;
   const int base = nblocks >> 3, rem = nblocks & 7;
   const int t = xcd * base + (xcd < rem ? xcd : rem) + idx;
+  if constexpr (kColumns) {
+    tn = t / tiles_m;
+    tm = t - tn * tiles_m;
+    return;
+  }
   const int tiles_n = nblocks / tiles_m;
   constexpr int G = 4;
   const int per_group = G * tiles_n;
@@ -134,12 +161,329 @@ __device__ inline void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int v
 // the caller waits for the counters it needs first.
 __device__ inline void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <class C, bool kMx>
+
+// The weight operand of the fused epilogue's compensation. The COO arrays
+// are separate __restrict__ kernel arguments, which lets the compiler read a
+// wave's entries with scalar loads (Y's stores cannot alias them).
+struct CompArgs {
+  const void* W;           // K x N weight, bf16 or fp32, row stride ldw elements
+  int ldw;
+  int w_bytes;             // K * ldw * element size (< 2^31)
+  int w_vec;               // W rows allow 4-column vector loads
+};
+
+// One compensation gather: this lane's 4 columns of W row k (bf16: 8 bytes,
+// fp32: 16 bytes), the row offset k * ldw in the scalar operand and the
+// column offsets in vo (byte offsets of the lane's columns, each clamped into
+// [0, N) so that every address lies inside row k whatever the lane: the
+// buffer range check does not cover the scalar offset). With vector access
+// (W and its row stride aligned to 4 elements and N a multiple of 4, so a
+// lane's 4 columns are all below N or all past it, and lanes past N read the
+// row's last 4) one load moves the 4 columns, vo[0] being their start;
+// otherwise the 4 elements are loaded one by one.
+template <bool kBf16W>
+struct WSeg {
+  uint32_t d[kBf16W ? 2 : 4];
+};
+
+template <bool kBf16W, bool kVec>
+__device__ inline WSeg<kBf16W> load_wseg(__amdgpu_buffer_rsrc_t rs, const int (&vo)[4], int soff) {
+  WSeg<kBf16W> w;
+  if constexpr (kBf16W) {
+    if constexpr (kVec) {
+      const auto u = __builtin_amdgcn_raw_buffer_load_b64(rs, vo[0], soff, 0);
+      w.d[0] = u[0];
+      w.d[1] = u[1];
+    } else {
+      const uint32_t h0 = __builtin_amdgcn_raw_buffer_load_b16(rs, vo[0], soff, 0);
+      const uint32_t h1 = __builtin_amdgcn_raw_buffer_load_b16(rs, vo[1], soff, 0);
+      const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b16(rs, vo[2], soff, 0);
+      const uint32_t h3 = __builtin_amdgcn_raw_buffer_load_b16(rs, vo[3], soff, 0);
+      w.d[0] = h0 | (h1 << 16);
+      w.d[1] = h2 | (h3 << 16);
+    }
+  } else {
+    if constexpr (kVec) {
+      const auto u = __builtin_amdgcn_raw_buffer_load_b128(rs, vo[0], soff, 0);
+      w.d[0] = u[0];
+      w.d[1] = u[1];
+      w.d[2] = u[2];
+      w.d[3] = u[3];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w.d[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo[c], soff, 0);
+    }
+  }
+  return w;
+}
+
+// s[c] = fma(v, W[k, col + c], s[c]) for the lane's 4 columns.
+template <bool kBf16W>
+__device__ inline void fma_wseg(float v, const WSeg<kBf16W>& w, float (&s)[4]) {
+  if constexpr (kBf16W) {
+    s[0] = fmaf(v, __uint_as_float(w.d[0] << 16), s[0]);
+    s[1] = fmaf(v, __uint_as_float(w.d[0] & 0xffff0000u), s[1]);
+    s[2] = fmaf(v, __uint_as_float(w.d[1] << 16), s[2]);
+    s[3] = fmaf(v, __uint_as_float(w.d[1] & 0xffff0000u), s[3]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[c] = fmaf(v, __uint_as_float(w.d[c]), s[c]);
+  }
+}
+
+// Epilogue with the sparse compensation (see the header). The tile (BM x BN =
+// 128 x 256, four waves of 64 x 128) leaves in four chunks; chunk c holds the
+// rows wm * 64 + (c >> 1) * 32 + (c & 1) * 16 + [0, 16) of both wave rows wm,
+// all 256 columns, wave row wm's block in stage wm. Wave w then finishes the
+// 8 rows (w & 1) * 8 + [0, 8) of wave row w >> 1's block.
+template <class C, bool kMx, bool kBf16W, bool kWVec>
+__device__ __attribute__((always_inline)) inline void fused_epilogue(
+    v16f (&acc)[C::FM][C::FN], const float (&sa)[C::FM][16], const float (&sb)[C::FN],
+    uint8_t* st0, uint8_t* st1, int wave, int wm, int wn, int lane, int m0, int n0, int M, int N,
+    float* __restrict__ Y, int64_t ldy, const CompArgs& cp, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ coo_row, const int32_t* __restrict__ col,
+    const float* __restrict__ val) {
+  constexpr int FM = C::FM, FN = C::FN, BN = C::BN;
+  static_assert(C::BM == 128 && BN == 256 && C::WM == 2 && C::WN == 2 && FM == 2 && FN == 4,
+                "chunk layout of the fused epilogue");
+  constexpr int kPitch = BN + 8;  // floats; lanes 32..63 (4 rows down) hit the other 32 banks
+  static_assert(16 * kPitch * 4 <= C::kStageBytes, "a wave row's 16-row block fits one stage");
+  // non-zeros per gather group and groups in flight (the element-load path,
+  // 4 loads per non-zero, keeps 8 x 2 within the vmcnt range)
+  constexpr int G = kWVec ? 8 : 8;
+  constexpr int D = kWVec ? 2 : 2;
+
+  // scales applied once, in place (the accumulators are then the output)
+  if constexpr (!kMx) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[fm][fn][r] = __fmul_rn(__fmul_rn(acc[fm][fn][r], sa[fm][r]), sb[fn]);
+  }
+  float* const wblk = reinterpret_cast<float*>(wm == 0 ? st0 : st1);
+  const int pr = wave >> 1, ph = wave & 1;
+  const float* const rblk = reinterpret_cast<const float*>(pr == 0 ? st0 : st1) + ph * 8 * kPitch;
+  const int c4 = 4 * lane;
+  const int gc = n0 + c4;
+  constexpr int esz = kBf16W ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rsW =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(cp.W), 0, cp.w_bytes, kBufferFlags);
+  const int row_bytes = cp.ldw * esz;
+  // byte offsets of this lane's 4 columns inside a W row, clamped below N
+  // (vector access: the 4-column group itself, the last one for lanes past N)
+  int voffW[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int cc = kWVec ? (gc + 4 <= N ? gc : N - 4) + c : (gc + c < N ? gc + c : N - 1);
+    voffW[c] = cc * esz;
+  }
+  // the whole tile width lies below N and Y takes 16-byte stores (uniform)
+  const bool y_full = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy & 3) == 0) &&
+                      n0 + BN <= N;
+  // The COO is read-only while the kernel runs: reading it through the
+  // constant address space lets every (wave-uniform) entry load be a scalar
+  // load into SGPRs, also after the epilogue's stores to Y. (Through generic
+  // pointers the compiler used vector loads for some of them, and its wait
+  // counting then made each gather group wait for every load in flight.)
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cint32* const rp_c = (cint32*)row_ptr;
+  cint32* const row_c = (cint32*)coo_row;
+  cint32* const col_c = (cint32*)col;
+  cfloat* const val_c = (cfloat*)val;
+
+  // Rows g0 .. g0+7 of the chunk just staged (their LDS rows at rblk, which
+  // only this wave touches until the next barrier). The non-zeros are taken
+  // in groups of G that start at a row's first non-zero; a row's last group
+  // gives its unused slots weight 0 (0 * w adds nothing, so the sum stays the
+  // same fp32 value), so every group is G unconditional multiply-adds and only
+  // a row's last group branches, to put Y0 + s into its LDS row. The groups go
+  // through a ring of D buffers (D groups in flight); the loop runs a count of
+  // groups fixed beforehand, padded with all-zero groups to a multiple of D,
+  // so that every iteration is the same code. No store is issued in the loop:
+  // the 8 rows leave for Y after it. A wave issues one instruction per 4
+  // cycles, so the scalar work per non-zero is kept to a few instructions.
+  auto finish_rows = [&](int g0) {
+    float* const rows = const_cast<float*>(rblk);
+    // the 9 row boundaries (rows past M have no entries)
+    int rp[9];
+#pragma unroll
+    for (int j = 0; j < 9; ++j) rp[j] = rp_c[g0 + j < M ? g0 + j : M];
+    const int eb = rp[0], ee = rp[8];
+    if (eb < ee) {
+      // groups in all: a row of n non-zeros takes ceil(n / G)
+      int ngroups = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ngroups += (rp[j + 1] - rp[j] + G - 1) / G;
+      // the next group to load: first non-zero gb, end of its row rend, row ri
+      int gb = eb, rend = 0, ri = 0;
+      // row of entry e (0..7) and the end of that row, from the boundaries in
+      // scalar registers (no indexing of registers)
+      auto locate = [&](int e) {
+        int i = 0, r = rp[8];
+#pragma unroll
+        for (int t = 7; t >= 1; --t) {
+          const bool above = rp[t] > e;
+          r = above ? rp[t] : r;      // boundaries ascend: the last one kept is the least above e
+          i = (!above && i == 0) ? t : i;
+        }
+        ri = __builtin_amdgcn_readfirstlane(i);
+        rend = __builtin_amdgcn_readfirstlane(r);
+      };
+      locate(eb);
+      WSeg<kBf16W> wq[D][G];
+      float vq[D][G];
+      int rq[D];     // row of the group, or -1: not its row's last group
+      // load the group at (gb, rend, ri), then step to the next one; past the
+      // last group the loads repeat entry ee - 1 with weight 0
+      auto load_group = [&](int d) {
+        int k[G];
+        float v[G];
+        if (gb + G <= ee) {
+#pragma unroll
+          for (int u = 0; u < G; ++u) {
+            k[u] = col_c[gb + u];
+            v[u] = val_c[gb + u];
+          }
+        } else {
+          // near the range's end: global-pointer loads, which the compiler
+          // cannot fold into the whole-group loads above (they would lose
+          // their 8-dword form)
+#pragma unroll
+          for (int u = 0; u < G; ++u) {
+            const int e = gb + u < ee ? gb + u : ee - 1;
+            k[u] = __builtin_amdgcn_readfirstlane(col[e]);
+            v[u] = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(val[e])));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < G; ++u) wq[d][u] = load_wseg<kBf16W, kWVec>(rsW, voffW, k[u] * row_bytes);
+        const bool last = gb + G >= rend;
+        if (last) {
+          // the row's last group: slots past its end weigh 0
+#pragma unroll
+          for (int u = 0; u < G; ++u) vq[d][u] = gb + u < rend ? v[u] : 0.0f;
+        } else {
+#pragma unroll
+          for (int u = 0; u < G; ++u) vq[d][u] = v[u];
+        }
+        rq[d] = (last && gb < ee) ? ri : -1;
+        // the gathers stay where they are issued (the scheduler would sink
+        // them towards their use to save registers, which undoes the prefetch)
+        __builtin_amdgcn_sched_barrier(0);
+        if (!last) {
+          gb += G;
+        } else {
+          gb = rend;
+          if (gb < ee) locate(gb);
+          else rend = ee + G;  // past the end: zero groups from here on
+        }
+      };
+      float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      // gathers issued after a group's own when it is consumed: the D - 1
+      // groups behind it (nothing else in the loop counts in vmcnt), so one
+      // wait per group covers its G gathers
+      constexpr int kLoadsAfter = (D - 1) * G * (kWVec ? 1 : 4);
+      static_assert(kLoadsAfter < 64, "vmcnt immediate");
+      auto consume = [&](int d) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kLoadsAfter, 15));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < G; ++u) fma_wseg<kBf16W>(vq[d][u], wq[d][u], acc4);
+        if (rq[d] >= 0) {
+          float* const p = rows + rq[d] * kPitch + c4;
+          f32x4 y = *reinterpret_cast<const f32x4*>(p);
+          y[0] = __fadd_rn(y[0], acc4[0]);
+          y[1] = __fadd_rn(y[1], acc4[1]);
+          y[2] = __fadd_rn(y[2], acc4[2]);
+          y[3] = __fadd_rn(y[3], acc4[3]);
+          *reinterpret_cast<f32x4*>(p) = y;
+          acc4[0] = acc4[1] = acc4[2] = acc4[3] = 0.0f;
+        }
+      };
+#pragma unroll
+      for (int d = 0; d < D; ++d) load_group(d);
+      for (int it = (ngroups + D - 1) / D; it > 0; --it) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          consume(d);
+          load_group(d);
+        }
+      }
+      // the groups issued past the end have landed before their registers are
+      // reused (one wait here instead of one per store below)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, 15));
+    }
+    // the 8 rows, Y0 + s (rows without non-zeros: Y0 as it is), to Y
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int gr = g0 + i;
+      const f32x4 y = *reinterpret_cast<const f32x4*>(rows + i * kPitch + c4);
+      if (gr < M) {
+        float* dst = Y + int64_t(gr) * ldy + gc;
+        if (y_full) {
+          __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(dst));
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (gc + c < N) dst[c] = y[c];
+        }
+      }
+    }
+  };
+
+  // acc element r of fragment row fm holds row 8 * (r >> 2) + 4 * (lane >> 5)
+  // + (r & 3) of the fragment: elements h * 8 .. h * 8 + 7 are its rows
+  // h * 16 + [0, 16)
+  auto stage_chunk = [&](auto fm_c, auto h_c) {
+    constexpr int fm = decltype(fm_c)::value, h = decltype(h_c)::value;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int rl = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+        wblk[rl * kPitch + wn * (FN * 32) + fn * 32 + (lane & 31)] = acc[fm][fn][h * 8 + rr];
+      }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+#pragma nounroll
+  for (int c = 0; c < 4; ++c) {
+    switch (c) {
+      case 0: stage_chunk(I0{}, I0{}); break;
+      case 1: stage_chunk(I0{}, I1{}); break;
+      case 2: stage_chunk(I1{}, I0{}); break;
+      default: stage_chunk(I1{}, I1{}); break;
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(63, 0));
+    raw_barrier();
+    finish_rows(m0 + pr * 64 + (c >> 1) * 32 + (c & 1) * 16 + ph * 8);
+    // every wave's LDS reads of this chunk are done before the next is staged
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(63, 0));
+    raw_barrier();
+  }
+}
+
+// Tile order of the kernels with the fused compensation (see tile_coords).
+constexpr bool kFusedColumns = true;
+
+// Largest COO capacity per row of A for which the compensation runs in the
+// GEMM's epilogue (see run_gemm).
+constexpr int64_t kFusedMaxPerRow = 16;
+
+// kComp: 0 no compensation; with it, 1 + (W is float32) + 2 * (W rows allow
+// 4-column vector gathers): 1 / 3 bfloat16 W, 2 / 4 float32 W.
+template <class C, bool kMx, int kComp>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
     const uint8_t* __restrict__ Aq, const float* __restrict__ sA,
     const uint8_t* __restrict__ Bq, const float* __restrict__ sB, int M, int N, int ldq,
     int tiles_m, float* __restrict__ Y, int64_t ldy, const uint8_t* __restrict__ As,
-    const uint8_t* __restrict__ Bs) {
+    const uint8_t* __restrict__ Bs, CompArgs cp, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ coo_row, const int32_t* __restrict__ col,
+    const float* __restrict__ val) {
   constexpr int BM = C::BM, BN = C::BN, WN = C::WN, BKB = C::BKB, CPR = C::CPR;
   constexpr int FM = C::FM, FN = C::FN, NT = C::kThreads;
   constexpr int SB = C::kStageBytes;
@@ -155,7 +499,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   const int wm = wave / WN;
   const int wn = wave % WN;
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tm, tn);
+  tile_coords<(kComp != 0) && kFusedColumns>(blockIdx.x, gridDim.x, tiles_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int nkt = (ldq + BKB - 1) / BKB;
 
@@ -393,6 +737,12 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
         sa[fm][r] = (gr < M) ? sA[gr] : 0.0f;
       }
   }
+  if constexpr (kComp != 0) {
+    fused_epilogue<C, kMx, (kComp & 1) != 0, kComp >= 3>(acc, sa, sb, st0, st1, wave, wm, wn,
+                                                          lane, m0, n0, M, N, Y, ldy, cp,
+                                                          row_ptr, coo_row, col, val);
+    return;
+  }
   // Output through a wave-private LDS block (the stage buffers are free after
   // the main loop's last barrier): two 32x32 fragments at a time are written
   // in the MFMA layout, read back as rows and stored 16 bytes per lane.
@@ -451,11 +801,47 @@ hipError_t run_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const
   if (ldq % C::BKB != 0) return hipErrorInvalidValue;
   const int tiles_m = int((M + C::BM - 1) / C::BM);
   const int tiles_n = int((N + C::BN - 1) / C::BN);
-  fp4_gemm_kernel<C, kMx><<<dim3(unsigned(tiles_m * tiles_n)), C::kThreads, 0, stream>>>(
-      Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || sp.row_ptr == nullptr) return e;
-  return launch_sparse_add(sp, M, N, Y, ldy, stream);
+  const dim3 grid(unsigned(tiles_m * tiles_n));
+  CompArgs cp{nullptr, 0, 0, 0};
+  // The two schedules of the compensation give the same bits. The fused
+  // epilogue saves the read-modify-write of Y (8 bytes per output), but its
+  // gathers run in the GEMM's waves (two per SIMD), which hide memory latency
+  // worse than the separate kernel's eight; measured on the LLaMA-shaped
+  // workloads it wins up to ~14 non-zeros per row and loses from ~20 (13B up
+  // 5.1/row: 543 against 656 us; 13B down 13.8/row: 446 against 492; 1.3B up
+  // 20/row: 156 against 111; 7B up 41/row: 797 against 732). The COO's
+  // capacity bounds the non-zeros (for the select's own COO it is M*K*(1-q)).
+  const bool fused = sp.row_ptr != nullptr && sp.capacity <= kFusedMaxPerRow * M;
+  if (!fused) {
+    fp4_gemm_kernel<C, kMx, 0><<<grid, C::kThreads, 0, stream>>>(
+        Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs, cp, nullptr, nullptr,
+        nullptr, nullptr);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sp.row_ptr == nullptr) return e;
+    return launch_sparse_add(sp, M, N, Y, ldy, stream);
+  }
+  const int64_t esz = sp.w_bf16 ? 2 : 4;
+  // 4-column vector gathers need every W row start aligned to 4 elements
+  // (8 bytes for bf16, 16 for fp32) and N a multiple of 4 (no lane straddles N)
+  const bool w_vec = (reinterpret_cast<uintptr_t>(sp.W) % (4 * esz) == 0) && (sp.ldw % 4 == 0) &&
+                     (N % 4 == 0);
+  cp = CompArgs{sp.W, int(sp.ldw), int(sp.w_rows * sp.ldw * esz), w_vec ? 1 : 0};
+  const int mode = (sp.w_bf16 ? 1 : 2) + (w_vec ? 2 : 0);
+#define FP4LIN_GEMM_COMP(MODE)                                                                  \
+  case MODE:                                                                                    \
+    fp4_gemm_kernel<C, kMx, MODE><<<grid, C::kThreads, 0, stream>>>(                            \
+        Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs, cp, sp.row_ptr,      \
+        sp.row, sp.col, sp.val);                                                                \
+    break;
+  switch (mode) {
+    FP4LIN_GEMM_COMP(1)
+    FP4LIN_GEMM_COMP(2)
+    FP4LIN_GEMM_COMP(3)
+    FP4LIN_GEMM_COMP(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef FP4LIN_GEMM_COMP
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -54,12 +54,14 @@ hipError_t launch_quantize_weight(const void* W, bool bf16, int64_t K, int64_t N
 
 struct SparseArgs {
   const int32_t* row_ptr;  // nullptr: no compensation term
+  const int32_t* row;      // row of each entry (read by the GEMM's fused epilogue)
   const int32_t* col;
   const float* val;
   const void* W;
   bool w_bf16;
   int64_t ldw;
   int64_t w_rows;  // K: rows of W (W is addressed with 32-bit byte offsets)
+  int64_t capacity;  // COO entries allocated: bounds the non-zeros (picks the GEMM's schedule)
 };
 
 // Y[i, :] += sum over row i's non-zeros of val * W[col, :] (ascending col).

@@ -127,7 +127,12 @@ __global__ __launch_bounds__(64) void sparse_add_kernel(
   const int valid = N - col0;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W), 0, w_bytes, kBufferFlags);
-  const int voff = col0 * esz;
+  // Column byte offset of the lane's 8 columns inside a W row. The buffer's
+  // range check does not cover the row offset in the scalar operand, so in the
+  // vector path (N a multiple of 8, or a strip wholly below N) a lane past N
+  // reads the row's last 8 columns instead of memory past the row; it stores
+  // nothing.
+  const int voff = (col0 + kCPL <= N ? col0 : N - kCPL) * esz;
   const int row_bytes = int(ldw) * esz;
   const bool y_full = y_vec && valid >= kCPL;
 
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(64) void sparse_add_kernel(
 
   // Every lane holds 8 columns or none (no lane straddles N), and W rows are
   // 16-byte aligned: one 16-byte buffer load per entry and lane. Lanes past N
-  // load harmlessly (inside the buffer, or zero past its end) and store nothing.
+  // load the row's last 8 columns and store nothing.
   const bool vec_path = w_vec != 0 && ((N % kCPL) == 0 || (strip + 1) * kStrip <= N);
   if (vec_path) {
     // Software pipeline over groups, two W buffers used in turn: the entries

@@ -205,7 +205,7 @@ def test_gemm_errors():
     assert gemm(sB=None) == _lib.ERR_NULL
     assert gemm(Y=None) == _lib.ERR_NULL
     assert gemm(dA=coo(10), W=None) == _lib.ERR_NULL
-    for fld in ("col", "val", "row_ptr"):
+    for fld in ("row", "col", "val", "row_ptr"):
         assert gemm(dA=coo(10, null=fld), W=FAKE) == _lib.ERR_NULL
     assert gemm(dA=coo(10), W=FAKE, wdt=3) == _lib.ERR_DTYPE
     assert gemm(dA=coo(10), W=FAKE, ldw=3) == _lib.ERR_SHAPE

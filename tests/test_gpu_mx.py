@@ -159,11 +159,13 @@ def test_quantize_weight_mx_leading_dimension(ql, dtype):
 # ---------------------------------------------------------------------------
 # GEMM with block scales
 # ---------------------------------------------------------------------------
-def run_gemm_mx(ql, codesA, eA, codesB, eB, K, delta=None, W=None):
+def run_gemm_mx(ql, codesA, eA, codesB, eB, K, delta=None, W=None, capacity=None):
+    """capacity: length of the COO arrays (at least nnz); at most 16 per row of
+    A runs the compensation in the GEMM's epilogue, more as a second kernel."""
     M, N = codesA.shape[0], codesB.shape[0]
     coo, Wd = None, None
     if delta is not None:
-        nz = max(delta.nnz, 1)
+        nz = max(delta.nnz, 1, capacity or 0)
         pad = lambda a, dt: np.concatenate([np.asarray(a, dt), np.zeros(nz - len(a), dt)])
         coo = ql.CooBuffers(upload(pad(delta.row, np.int32)), upload(pad(delta.col, np.int32)),
                             upload(pad(delta.val32, np.float32)),
@@ -256,6 +258,11 @@ def test_gemm_mx_quantized_operands(ql, dtype, M, K, N):
     assert_within_accumulation_bound(Y0, want0, mag0, K)
     Y = run_gemm_mx(ql, qa[2], qa[3], qw[2], qw[3], K, delta, W)
     assert O.rel_fro(Y, want) <= Y_TOL
+    # both schedules of the compensation give the same bits
+    fused = run_gemm_mx(ql, qa[2], qa[3], qw[2], qw[3], K, delta, W, capacity=delta.nnz)
+    separate = run_gemm_mx(ql, qa[2], qa[3], qw[2], qw[3], K, delta, W,
+                           capacity=max(delta.nnz, 16 * M + 1))
+    assert np.array_equal(fused.view(np.uint64), separate.view(np.uint64))
 
 
 # ---------------------------------------------------------------------------

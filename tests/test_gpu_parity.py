@@ -634,30 +634,46 @@ def test_gemm_equals_gemm_then_sparse_add(ql):
 # ---------------------------------------------------------------------------
 # output and weight layouts: padded / unaligned leading dimensions, ragged N
 # ---------------------------------------------------------------------------
-def upload_coo(ql, delta):
-    nz = max(delta.nnz, 1)
+def upload_coo(ql, delta, capacity=None):
+    """The COO on the device, its arrays `capacity` entries long (at least
+    nnz). fp4lin_gemm runs the compensation in its epilogue when the capacity
+    is at most 16 entries per row of A, else as a second kernel: the capacity
+    picks the schedule, and both give the same bits."""
+    nz = max(delta.nnz, 1, capacity or 0)
     pad = lambda a, dt: np.concatenate([np.asarray(a, dt), np.zeros(nz - len(a), dt)])
     return ql.CooBuffers(upload_i32(pad(delta.row, np.int32)), upload_i32(pad(delta.col, np.int32)),
                          upload_f32(pad(delta.val32, np.float32)), upload_i32(delta.row_ptr))
 
 
+FUSED_MAX_PER_ROW = 16
+
+
+def schedule_capacity(schedule, M, nnz):
+    if schedule == "fused":
+        assert nnz <= FUSED_MAX_PER_ROW * M
+        return nnz
+    return max(nnz, FUSED_MAX_PER_ROW * M + 1)
+
+
+@pytest.mark.parametrize("schedule", ["fused", "separate"])
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 @pytest.mark.parametrize("N,ldy_pad,ldw_pad", [(203, 5, 3), (256, 4, 0), (130, 2, 1),
                                                (517, 3, 8), (8, 0, 5)])
-def test_gemm_compensation_padded_layouts(ql, dtype, N, ldy_pad, ldw_pad):
+def test_gemm_compensation_padded_layouts(ql, dtype, N, ldy_pad, ldw_pad, schedule):
     """fp4lin_gemm with dA into a padded (possibly unaligned) Y, with a padded
-    (possibly unaligned) W: the element paths of the epilogue and of the
-    compensation run, the result matches the oracle, and no padding column of
-    Y is written."""
+    (possibly unaligned) W, under both schedules of the compensation (in the
+    GEMM's epilogue, or as a second kernel): the element paths of the epilogue
+    and of the compensation run, the result matches the oracle, and no padding
+    column of Y is written."""
     t = torch()
     M, K = 150, 300
-    log(f"gemm layouts {dtype} N={N} ldy=N+{ldy_pad} ldw=N+{ldw_pad}")
+    log(f"gemm layouts {schedule} {dtype} N={N} ldy=N+{ldy_pad} ldw=N+{ldw_pad}")
     rng = np.random.default_rng(N * 7 + ldy_pad * 3 + ldw_pad)
     A = wl.random_matrix(rng, M, K, dtype, dist="t3")
     W = wl.random_matrix(rng, K, N, dtype, scale=0.02)
     ops = O.forward_operands(A.f32, W.f32, 0.97)
     Aq, Bq = upload_u8(O.pack_rows(ops.codesA)), upload_u8(O.pack_rows(ops.codesW))
-    coo = upload_coo(ql, ops.delta)
+    coo = upload_coo(ql, ops.delta, schedule_capacity(schedule, M, ops.delta.nnz))
     Wd = padded(to_device(W), N + ldw_pad)
     sentinel = float("nan")
     Ybuf = t.full((M, N + ldy_pad), sentinel, dtype=t.float32, device="cuda:0")
@@ -676,6 +692,81 @@ def test_gemm_compensation_padded_layouts(ql, dtype, N, ldy_pad, ldw_pad):
     ql.fp4lin_sparse_add(coo, Wd, Y2)
     t.cuda.synchronize()
     assert np.array_equal(host(Ybuf2).view(np.uint32), full.view(np.uint32))
+
+
+def synthetic_delta(rng, M, K, lengths):
+    """A COO with the given number of non-zeros per row (distinct ascending
+    columns, values of mixed sign and magnitude), as the oracle's SparseDelta."""
+    rows, cols = [], []
+    for i, n in enumerate(lengths):
+        c = np.sort(rng.choice(K, int(n), replace=False))
+        rows.append(np.full(c.size, i))
+        cols.append(c)
+    row = np.concatenate(rows).astype(np.int32) if rows else np.zeros(0, np.int32)
+    col = np.concatenate(cols).astype(np.int32) if cols else np.zeros(0, np.int32)
+    val32 = (rng.standard_normal(row.size) * np.exp2(rng.integers(-3, 6, row.size))).astype(np.float32)
+    row_ptr = np.zeros(M + 1, np.int64)
+    row_ptr[1:] = np.cumsum(lengths)
+    return O.SparseDelta(row, col, val32, val32.astype(np.float64), row_ptr.astype(np.int32), (M, K))
+
+
+U32 = 2.0 ** -24
+
+
+@pytest.mark.parametrize("wdtype", [wl.BF16, wl.F32])
+@pytest.mark.parametrize("M,N,ldw_pad,pattern", [
+    (300, 256, 0, "mixed"),       # ragged M (rows past M in the last tile)
+    (200, 520, 0, "mixed"),       # ragged N, N % 4 == 0: vector gathers
+    (130, 203, 0, "mixed"),       # N % 4 != 0: element gathers
+    (257, 264, 3, "mixed"),       # unaligned W rows: element gathers
+    (384, 512, 0, "dense-rows"),  # a few long rows among empty ones
+    (128, 256, 0, "empty"),       # no non-zero at all
+])
+def test_gemm_compensation_row_structures(ql, wdtype, M, N, ldw_pad, pattern):
+    """The compensation under both schedules on COOs built to reach the fused
+    epilogue's corners: rows with 0, 1, 7, 8, 9, 16, 17 and 40 non-zeros (its
+    gathers go in groups of 8 from each row's first non-zero), long rows next to
+    empty ones, wholly empty tiles, rows past M, ragged N and unaligned W. The
+    two schedules give the same bits, and every element of Y is within the fp32
+    bound 3u|Y0| + (n_i + 2) u sum_k |dA[i,k] W[k,j]| of the oracle's float64
+    value."""
+    t = torch()
+    K = 300
+    log(f"gemm compensation structures {wdtype} {M}x{N} ldw=N+{ldw_pad} {pattern}")
+    rng = np.random.default_rng(M * 31 + N + ldw_pad)
+    if pattern == "mixed":
+        cycle = np.array([0, 1, 7, 8, 9, 16, 17, 40, 0, 0, 3])
+        lengths = cycle[np.arange(M) % cycle.size]
+    elif pattern == "dense-rows":
+        lengths = np.zeros(M, np.int64)
+        lengths[[5, 6, 130, 131, 300, 383]] = [90, 1, 64, 33, 120, 15]
+    else:
+        lengths = np.zeros(M, np.int64)
+    delta = synthetic_delta(rng, M, K, lengths)
+    ca = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    cb = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    sa = np.exp2(rng.integers(-4, 4, M)).astype(np.float32)
+    sb = (rng.random(N) + 0.5).astype(np.float32)
+    W = wl.random_matrix(rng, K, N, wdtype, scale=0.02)
+    Aq, Bq = upload_u8(O.pack_rows(ca)), upload_u8(O.pack_rows(cb))
+    Wd = padded(to_device(W), N + ldw_pad) if ldw_pad else to_device(W)
+    Ys = {}
+    for schedule in ("fused", "separate"):
+        coo = upload_coo(ql, delta, schedule_capacity(schedule, M, delta.nnz))
+        Y = t.full((M, N), float("nan"), dtype=t.float32, device="cuda:0")
+        ql.fp4lin_gemm(Aq, upload_f32(sa), Bq, upload_f32(sb), M, N, K, coo, Wd, Y)
+        t.cuda.synchronize()
+        Ys[schedule] = host(Y)
+    assert np.array_equal(Ys["fused"].view(np.uint32), Ys["separate"].view(np.uint32))
+    y0 = O.scaled_product(O.integer_product(ca, cb), sa, sb)
+    W64 = W.f32.astype(np.float64)
+    want = y0 + O.sparse_times_dense(delta, W64)
+    D = delta.dense64()
+    T = np.abs(D) @ np.abs(W64)
+    n_i = np.asarray(lengths, np.float64)[:, None]
+    bound = (3 * U32 * np.abs(y0) + (n_i + 2) * U32 * T) * (1 + 1e-6)
+    bad = np.abs(Ys["fused"].astype(np.float64) - want) > bound
+    assert not bad.any(), f"{int(bad.sum())} elements beyond the fp32 bound"
 
 
 # ---------------------------------------------------------------------------
