@@ -67,7 +67,43 @@ def parse():
                    choices=("forward", "dgrad", "wgrad"))
     p.add_argument("--quant", default="token", choices=("token", "mx"),
                    help="token: the vector-wise forward (default); mx: the micro-scaled one")
+    p.add_argument("--no-13b", action="store_true",
+                   help="skip the 13B FFN up/down forwards the default run reports beside 7B")
     return p.parse_args()
+
+
+# the GEMM runs the compensation in its epilogue up to this many COO entries
+# per row of A (the COO capacity bounds them), else as a second kernel
+FUSED_MAX_PER_ROW = 16
+
+
+def forward_rate(L, dev, steps, warmup):
+    """Back-to-back fp4lin_forward calls on layer L (inputs resident in HBM):
+    ms per forward from HIP events on the stream the kernels run on."""
+    import torch
+    import quantized_linear_layer_amd as ql
+    import workloads as wl
+    A, W = upload(L.A, dev), upload(L.W, dev)
+    stream = torch.cuda.current_stream()
+    st = Step(ql, A, W, L.q, stream)
+    for _ in range(max(warmup, 1)):
+        st.forward_call()
+    torch.cuda.synchronize()
+    nnz = int(st.ws[st.offsets.row_ptr + 4 * L.M: st.offsets.row_ptr + 4 * L.M + 4]
+              .cpu().numpy().view(np.int32)[0])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        st.forward_call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * L.M * L.N * L.K
+    tf = flops / (ms * 1e-3) / 1e12
+    fused = st.offsets.capacity <= FUSED_MAX_PER_ROW * L.M
+    return {"M": L.M, "K": L.K, "N": L.N, "q": L.q, "nnz_dA": nnz, "ms": round(ms, 5),
+            "TFLOP/s": round(tf, 1), "pct_fp4_peak": round(100.0 * tf / FP4_PEAK_TFLOPS, 2),
+            "compensation": "gemm epilogue" if fused else "separate kernel", "steps": steps}
 
 
 def file_sha(path):
@@ -728,6 +764,18 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.seed, args.cpu_rows)
+    if args.workload == "llama7b_ffn_up" and not args.no_13b:
+        # the 13B FFN shapes beside the 7B headline (one layer at a time)
+        del st, A, W
+        torch.cuda.empty_cache()
+        up, down = wl.make_13b_pair(seed=args.seed)
+        n13 = max(1, min(args.steps, 10))
+        out["llama13b_ffn_up"] = forward_rate(up, dev, n13, 3)
+        del up
+        torch.cuda.empty_cache()
+        out["llama13b_ffn_down"] = forward_rate(down, dev, n13, 3)
+        del down
+        torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 
