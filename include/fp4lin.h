@@ -227,8 +227,8 @@ fp4lin_status fp4lin_quantize_weight(const void* W, fp4lin_dtype dt, int64_t K, 
  *   Aq, sA   device, M x packed_ld(K) bytes, M floats
  *   Bq, sB   device, N x packed_ld(K) bytes (N-major), N floats
  *   dA       host pointer to a COO descriptor, or NULL for no compensation;
- *            its row, col, val and row_ptr arrays are read and must describe
- *            one row-major matrix, as fp4lin_outlier_select writes them
+ *            its col, val and row_ptr arrays are read (row is not) and must
+ *            describe one row-major matrix, as fp4lin_outlier_select writes them
  *   W        device K x N (dtype wdt, leading dimension ldw), required exactly
  *            when dA is given (the unquantized weight dA multiplies);
  *            K*ldw*sizeof(dtype) must be below 2^31
@@ -334,8 +334,8 @@ fp4lin_status fp4lin_forward_layout_mx(int64_t M, int64_t K, int64_t N, fp4lin_d
  * fp4lin_quantize_act_mx (with the selected tau), fp4lin_quantize_weight_mx
  * and fp4lin_gemm_mx (with dA) compute, in that order on `stream`, keeping
  * every intermediate in `ws` at the offsets fp4lin_forward_layout_mx reports.
- * For bf16 A with 16-byte aligned rows and K <= 8192 the outlier compaction
- * and the block quantization of A run as one kernel over one read of A; every
+ * The outlier compaction also block-quantizes the rows of A it reads, and the
+ * quantization of W shares the launch of the select's row count; every
  * intermediate and Y are bit-identical to those of the separate calls.
  *   A, W     device inputs (same dtype dt), leading dimensions lda, ldw
  *   Y        device output, M x N floats, leading dimension ldy
@@ -350,12 +350,12 @@ fp4lin_status fp4lin_forward_mx(const void* A, const void* W, fp4lin_dtype dt, i
  * the layer's forward begins). Computes what fp4lin_outlier_select,
  * fp4lin_quantize_act (with the selected tau), fp4lin_quantize_weight and
  * fp4lin_gemm (with dA) compute, in that order on `stream`, keeping every
- * intermediate in `ws` at the offsets fp4lin_forward_layout reports. For bf16
- * A and W with 16-byte aligned rows and K <= 8192, the outlier compaction and
- * the token-wise quantization of A run as one kernel over one read of A, and
- * the passes over W that fp4lin_quantize_weight makes share launches with the
- * select's kernels (K <= 4096) or follow them; every intermediate and Y are
- * bit-identical to those of the separate calls.
+ * intermediate in `ws` at the offsets fp4lin_forward_layout reports. One
+ * route for every dtype, K and layout: the select's row count also takes each
+ * row's amax clamped to tau, its compaction quantizes the rows of A it reads
+ * with the scales that follow, and the two passes over W that
+ * fp4lin_quantize_weight makes share the launches of those two row kernels;
+ * every intermediate and Y are bit-identical to those of the separate calls.
  *   A, W     device inputs (same dtype dt), leading dimensions lda, ldw
  *   Y        device output, M x N floats, leading dimension ldy
  *   ws       device workspace of >= fp4lin_workspace_bytes(M, K, N, dt, q)

@@ -28,9 +28,17 @@ fp4lin_status launch_status(hipError_t e) {
   return e == hipSuccess ? FP4LIN_OK : FP4LIN_ERR_LAUNCH;
 }
 
-// The column quantizers launch one workgroup row per 128 codes of K along the
-// grid's second dimension, which holds at most 65535.
+// The micro-scaled column quantizer launches one workgroup row per 128 codes
+// of K along the grid's second dimension, which holds at most 65535; the
+// token-wise one keeps the same limit.
 constexpr int64_t kMaxColK = int64_t(65535) * 128;
+
+// The column quantizers' one-dimensional grids (128-column tiles by 64 rows at
+// the finest, plus the select's row workgroups when they share a launch) fit
+// the 32-bit workgroup count.
+bool col_grids_fit(int64_t K, int64_t N) {
+  return ((N + 127) / 128) * ((K + 63) / 64) < (int64_t(1) << 32) - 4096;
+}
 
 // COO entries the select can produce for rank k: #{|a| > tau} <= n - 1 - k.
 int64_t needed_capacity(int64_t n, int64_t k) { return n - 1 - k; }
@@ -191,10 +199,39 @@ fp4lin_status select_check(const void* A, fp4lin_dtype dt, int64_t M, int64_t K,
 // fp4lin_outlier_select; with quantized set, the forward path's token-wise
 // quantization of A (Xq, sX) is done by the same kernels where the rows allow
 // it, and *quantized says whether it was.
+fp4lin::FrontArgs front_args(const void* A, fp4lin_dtype dt, bool mx, int64_t M, int64_t K,
+                             int64_t lda, double q, float* tau, const fp4lin_coo& coo,
+                             void* scratch, uint8_t* Aq, int64_t ldq, void* sA, const void* W,
+                             int64_t N, int64_t ldw, uint8_t* Wq, void* sW, uint32_t* colmax) {
+  fp4lin::FrontArgs f;
+  f.A = A;
+  f.bf16 = dt == FP4LIN_BF16;
+  f.mx = mx;
+  f.M = M;
+  f.K = K;
+  f.lda = lda;
+  f.k = fp4lin_quantile_rank(M * K, q);
+  f.tau = tau;
+  f.capacity = coo.capacity;
+  f.row = coo.row;
+  f.col = coo.col;
+  f.val = coo.val;
+  f.row_ptr = coo.row_ptr;
+  f.ws = scratch;
+  f.Aq = Aq;
+  f.ldq = ldq;
+  f.sA = sA;
+  f.W = W;
+  f.N = N;
+  f.ldw = ldw;
+  f.Wq = Wq;
+  f.sW = sW;
+  f.colmax = colmax;
+  return f;
+}
 fp4lin_status select_impl(const void* A, fp4lin_dtype dt, int64_t M, int64_t K, int64_t lda,
                           double q, float* tau, fp4lin_coo dA, void* ws, size_t ws_bytes,
-                          hipStream_t stream, uint8_t* Xq, float* sX, bool* quantized,
-                          uint8_t* Xs = nullptr) {
+                          hipStream_t stream) {
   if (ws == nullptr) return FP4LIN_ERR_NULL;
   const fp4lin_status c = select_check(A, dt, M, K, lda, q, tau, dA);
   if (c != FP4LIN_OK) return c;
@@ -202,8 +239,7 @@ fp4lin_status select_impl(const void* A, fp4lin_dtype dt, int64_t M, int64_t K, 
   if (ws_bytes < select_ws(M, dt)) return FP4LIN_ERR_WORKSPACE;
   return launch_status(fp4lin::launch_outlier_select(
       A, dt == FP4LIN_BF16, M, K, lda, fp4lin_quantile_rank(M * K, q), tau, dA.capacity,
-      dA.row, dA.col, dA.val, dA.row_ptr, ws, stream, Xq, fp4lin_packed_ld(K), sX, quantized,
-      Xs));
+      dA.row, dA.col, dA.val, dA.row_ptr, ws, stream));
 }
 
 // ---- allocation-free select ---------------------------------------------------
@@ -258,8 +294,7 @@ extern "C" {
 fp4lin_status fp4lin_outlier_select(const void* A, fp4lin_dtype dt, int64_t M, int64_t K,
                                     int64_t lda, double q, float* tau, fp4lin_coo dA, void* ws,
                                     size_t ws_bytes, hipStream_t stream) {
-  return select_impl(A, dt, M, K, lda, q, tau, dA, ws, ws_bytes, stream, nullptr, nullptr,
-                     nullptr);
+  return select_impl(A, dt, M, K, lda, q, tau, dA, ws, ws_bytes, stream);
 }
 
 fp4lin_status fp4lin_outlier_select_noalloc(const void* A, fp4lin_dtype dt, int64_t M,
@@ -271,8 +306,7 @@ fp4lin_status fp4lin_outlier_select_noalloc(const void* A, fp4lin_dtype dt, int6
   void* ws = nullptr;
   const hipError_t e = scratch_address(stream, &ws);
   if (e != hipSuccess) return launch_status(e);
-  return select_impl(A, dt, M, K, lda, q, tau, dA, ws, kNoAllocScratchBytes, stream, nullptr,
-                     nullptr, nullptr);
+  return select_impl(A, dt, M, K, lda, q, tau, dA, ws, kNoAllocScratchBytes, stream);
 }
 
 fp4lin_status fp4lin_quantize_act(const void* X, fp4lin_dtype dt, int64_t M, int64_t K,
@@ -291,7 +325,8 @@ fp4lin_status fp4lin_quantize_weight(const void* W, fp4lin_dtype dt, int64_t K, 
                                      size_t ws_bytes, hipStream_t stream) {
   if (W == nullptr || Wq == nullptr || sW == nullptr || ws == nullptr) return FP4LIN_ERR_NULL;
   if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
-  if (!ok_dim(K) || !ok_dim(N) || ldw < N || K > kMaxColK) return FP4LIN_ERR_SHAPE;
+  if (!ok_dim(K) || !ok_dim(N) || ldw < N || K > kMaxColK || !col_grids_fit(K, N))
+    return FP4LIN_ERR_SHAPE;
   if (!aligned16(Wq) || !aligned16(ws)) return FP4LIN_ERR_ALIGN;
   if (ws_bytes < weight_ws(N)) return FP4LIN_ERR_WORKSPACE;
   return launch_status(fp4lin::launch_quantize_weight(W, dt == FP4LIN_BF16, K, N, ldw, Wq,
@@ -305,14 +340,13 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
   if (Aq == nullptr || sA == nullptr || Bq == nullptr || sB == nullptr || Y == nullptr)
     return FP4LIN_ERR_NULL;
   if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldy < N) return FP4LIN_ERR_SHAPE;
-  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, nullptr, false, 0, 0, 0};
+  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, false, 0, 0, 0};
   if (dA != nullptr) {
-    if (dA->row_ptr == nullptr || dA->row == nullptr || dA->col == nullptr ||
-        dA->val == nullptr || W == nullptr)
+    if (dA->row_ptr == nullptr || dA->col == nullptr || dA->val == nullptr || W == nullptr)
       return FP4LIN_ERR_NULL;
     if (bad_dtype(wdt)) return FP4LIN_ERR_DTYPE;
     if (ldw < N || !weight_addressable(K, ldw, wdt)) return FP4LIN_ERR_SHAPE;
-    sp = fp4lin::SparseArgs{dA->row_ptr, dA->row, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K,
+    sp = fp4lin::SparseArgs{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K,
                             dA->capacity};
   }
   // packed operands are addressed with 32-bit byte offsets
@@ -333,7 +367,7 @@ fp4lin_status fp4lin_sparse_add(const fp4lin_coo* dA, const void* W, fp4lin_dtyp
   if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldw < N || ldy < N ||
       !weight_addressable(K, ldw, wdt))
     return FP4LIN_ERR_SHAPE;
-  const fp4lin::SparseArgs sp{dA->row_ptr, dA->row, dA->col, dA->val, W, wdt == FP4LIN_BF16,
+  const fp4lin::SparseArgs sp{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16,
                               ldw,         K,       dA->capacity};
   return launch_status(fp4lin::launch_sparse_add(sp, M, N, Y, ldy, stream));
 }
@@ -359,7 +393,8 @@ fp4lin_status fp4lin_quantize_weight_mx(const void* W, fp4lin_dtype dt, int64_t 
                                         hipStream_t stream) {
   if (W == nullptr || Wq == nullptr || Ws == nullptr) return FP4LIN_ERR_NULL;
   if (bad_dtype(dt)) return FP4LIN_ERR_DTYPE;
-  if (!ok_dim(K) || !ok_dim(N) || ldw < N || K > kMaxColK) return FP4LIN_ERR_SHAPE;
+  if (!ok_dim(K) || !ok_dim(N) || ldw < N || K > kMaxColK || !col_grids_fit(K, N))
+    return FP4LIN_ERR_SHAPE;
   if (!aligned16(Wq) || !aligned16(Ws)) return FP4LIN_ERR_ALIGN;
   return launch_status(fp4lin::launch_quantize_cols_mx(W, dt == FP4LIN_BF16, K, N, ldw, Wq,
                                                        fp4lin_packed_ld(K), Ws, stream));
@@ -372,14 +407,13 @@ fp4lin_status fp4lin_gemm_mx(const uint8_t* Aq, const uint8_t* As, const uint8_t
   if (Aq == nullptr || As == nullptr || Bq == nullptr || Bs == nullptr || Y == nullptr)
     return FP4LIN_ERR_NULL;
   if (!ok_dim(M) || !ok_dim(N) || !ok_dim(K) || ldy < N) return FP4LIN_ERR_SHAPE;
-  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, nullptr, false, 0, 0, 0};
+  fp4lin::SparseArgs sp{nullptr, nullptr, nullptr, nullptr, false, 0, 0, 0};
   if (dA != nullptr) {
-    if (dA->row_ptr == nullptr || dA->row == nullptr || dA->col == nullptr ||
-        dA->val == nullptr || W == nullptr)
+    if (dA->row_ptr == nullptr || dA->col == nullptr || dA->val == nullptr || W == nullptr)
       return FP4LIN_ERR_NULL;
     if (bad_dtype(wdt)) return FP4LIN_ERR_DTYPE;
     if (ldw < N || !weight_addressable(K, ldw, wdt)) return FP4LIN_ERR_SHAPE;
-    sp = fp4lin::SparseArgs{dA->row_ptr, dA->row, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K,
+    sp = fp4lin::SparseArgs{dA->row_ptr, dA->col, dA->val, W, wdt == FP4LIN_BF16, ldw, K,
                             dA->capacity};
   }
   // packed operands and scale rows are addressed with 32-bit byte offsets
@@ -421,37 +455,14 @@ fp4lin_status fp4lin_forward(const void* A, const void* W, fp4lin_dtype dt, int6
   uint8_t* Wq = reinterpret_cast<uint8_t*>(base + o.Wq);
   float* sW = reinterpret_cast<float*>(base + o.sW);
   void* scratch = base + o.scratch;
-  const size_t scratch_bytes = o.total - o.scratch;
-  fp4lin_status s;
-  if (fp4lin::forward_front_supported(A, W, dt == FP4LIN_BF16, K, lda, ldw)) {
-    // bf16, aligned rows, K <= 8192: select, quantization of A (in the
-    // compaction) and of W (for K <= 4096 sharing launches with the select's
-    // row kernels; W's column maxima are cleared by the select's first pass)
-    uint32_t* colmax = reinterpret_cast<uint32_t*>(static_cast<char*>(scratch) + select_ws(M, dt));
-    bool w_done = false;
-    s = launch_status(fp4lin::launch_forward_front(
-        A, M, K, lda, fp4lin_quantile_rank(M * K, q), tau, coo.capacity, coo.row, coo.col,
-        coo.val, coo.row_ptr, scratch, Aq, ldq, sA, W, N, ldw, Wq, sW, colmax, &w_done, stream));
-    if (s != FP4LIN_OK) return s;
-    if (!w_done) {
-      s = launch_status(fp4lin::launch_quantize_weight_cleared(
-          static_cast<const uint16_t*>(W), K, N, ldw, Wq, ldq, sW, colmax, stream));
-      if (s != FP4LIN_OK) return s;
-    }
-  } else {
-    // bfloat16 rows that fit one slab are quantized by the select's
-    // compaction, which reads A anyway
-    bool a_done = false;
-    s = select_impl(A, dt, M, K, lda, q, tau, coo, scratch, scratch_bytes, stream, Aq, sA,
-                    &a_done);
-    if (s != FP4LIN_OK) return s;
-    if (!a_done) {
-      s = fp4lin_quantize_act(A, dt, M, K, lda, tau, Aq, sA, stream);
-      if (s != FP4LIN_OK) return s;
-    }
-    s = fp4lin_quantize_weight(W, dt, K, N, ldw, Wq, sW, scratch, scratch_bytes, stream);
-    if (s != FP4LIN_OK) return s;
-  }
+  // select, quantization of A (in the select's compaction) and of W (in the
+  // select's row launches); W's column maxima follow the select's workspace
+  const fp4lin::FrontArgs f = front_args(A, dt, false, M, K, lda, q, tau, coo, scratch, Aq, ldq, sA,
+                                         W, N, ldw, Wq, sW,
+                                         reinterpret_cast<uint32_t*>(static_cast<char*>(scratch) +
+                                                                     select_ws(M, dt)));
+  const fp4lin_status s = launch_status(fp4lin::launch_forward_front(f, stream));
+  if (s != FP4LIN_OK) return s;
   return fp4lin_gemm(Aq, sA, Wq, sW, M, N, K, &coo, W, dt, ldw, Y, ldy, stream);
 }
 
@@ -487,18 +498,11 @@ fp4lin_status fp4lin_forward_mx(const void* A, const void* W, fp4lin_dtype dt, i
   uint8_t* Wq = reinterpret_cast<uint8_t*>(base + o.Wq);
   uint8_t* Ws = reinterpret_cast<uint8_t*>(base + o.sW);
   void* scratch = base + o.scratch;
-  const size_t scratch_bytes = o.total - o.scratch;
-  // bfloat16 rows that fit one slab are block-quantized by the select's
-  // compaction, which reads A anyway
-  bool a_done = false;
-  fp4lin_status s = select_impl(A, dt, M, K, lda, q, tau, coo, scratch, scratch_bytes, stream, Aq,
-                                nullptr, &a_done, As);
-  if (s != FP4LIN_OK) return s;
-  if (!a_done) {
-    s = fp4lin_quantize_act_mx(A, dt, M, K, lda, tau, Aq, As, stream);
-    if (s != FP4LIN_OK) return s;
-  }
-  s = fp4lin_quantize_weight_mx(W, dt, K, N, ldw, Wq, Ws, stream);
+  // select, micro-scaled quantization of A (in the select's compaction) and
+  // of W (in the select's row-count launch)
+  const fp4lin::FrontArgs f = front_args(A, dt, true, M, K, lda, q, tau, coo, scratch, Aq, ldq, As,
+                                         W, N, ldw, Wq, Ws, nullptr);
+  const fp4lin_status s = launch_status(fp4lin::launch_forward_front(f, stream));
   if (s != FP4LIN_OK) return s;
   return fp4lin_gemm_mx(Aq, As, Wq, Ws, M, N, K, &coo, W, dt, ldw, Y, ldy, stream);
 }

@@ -1,8 +1,10 @@
 // Channel-wise (per column) quantization of a K x N row-major matrix into
 // E2M1 codes packed N-major, as device bodies of 256-thread workgroups that
 // take their workgroup coordinates as arguments: the column-max pass and the
-// encode pass. The quantize_weight kernels launch them directly; the forward
-// pairs them with the select's row kernels in shared launches.
+// encode pass of the token-wise format, and the one pass of the micro-scaled
+// format (blocks of 32 codes along K). The quantize_weight kernels launch
+// them directly; the forward pairs them with the select's row kernels in
+// shared launches.
 #pragma once
 
 #include "device_common.hpp"
@@ -119,6 +121,59 @@ __device__ __attribute__((always_inline)) inline void quantize_cols_body(int64_t
       word |= code << (4 * u);
     }
     *reinterpret_cast<uint32_t*>(Wq + (c + j) * ldq + kr / 2) = word;
+  }
+}
+
+// Micro-scaled tile (bx, by): columns bx*128 .. +127, rows by*128 .. +127
+// (rows past K read as zero and give the zero padding). Thread (kg, g) =
+// (t % 16, t / 16) owns rows k0 + 8kg .. +7 of columns n0 + 8g .. +7: the 8
+// codes of one column are one 32-bit word of its packed row, and lanes
+// 4q .. 4q+3 share block q. Block scales go to the step-major array Ws (the
+// byte of block b of column n at (b / 4) * 4N + 4n + b % 4).
+constexpr int kMxTK = 128;  // codes along K per column tile
+constexpr int kMxTN = 128;  // columns per tile
+
+template <class In, bool kAligned>
+__device__ __attribute__((always_inline)) inline void quantize_cols_mx_body(
+    int64_t bx, int64_t by, const typename In::T* __restrict__ W, int64_t K, int64_t N,
+    int64_t ldw, uint8_t* __restrict__ Wq, int64_t ldq, uint8_t* __restrict__ Ws) {
+  const int t = threadIdx.x;
+  const int kg = t & 15, g = t >> 4;
+  const int64_t n0 = bx * kMxTN;
+  const int64_t k0 = by * kMxTK;
+  const int64_t c = n0 + g * 8;
+  const int64_t valid = N - c;
+  const int64_t kr = k0 + kg * 8;
+  Vec8<In> v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (kr + u < K && valid > 0) {
+      load8<In, kAligned>(W + (kr + u) * ldw + c, valid, v[u]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[u].v[j] = typename In::T(0);
+    }
+  }
+  int e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float m = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(In::widen(v[u].v[j])));
+    e[j] = mx_exponent(quad_max(m));
+  }
+  if (valid <= 0) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= valid) break;
+    uint32_t word = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      word |= (mx_magnitude(fabsf(In::widen(v[u].v[j])), e[j]) | (In::sign_bit(v[u].v[j]) << 3))
+              << (4 * u);
+    *reinterpret_cast<uint32_t*>(Wq + (c + j) * ldq + kr / 2) = word;
+    // rows kr .. kr+7: block kr / 32 of K step kr / 128 (the tile's step by)
+    if ((kg & 3) == 0) Ws[(kr / 128) * 4 * N + 4 * (c + j) + ((kr / 32) & 3)] = uint8_t(e[j] + 127);
   }
 }
 

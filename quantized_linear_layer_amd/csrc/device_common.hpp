@@ -297,43 +297,4 @@ __device__ inline float quad_max(float v) {
   return fmaxf(v, __shfl_xor(v, 2, kWave));
 }
 
-// Micro-scaled quantization of one bfloat16 row of the M-row matrix held in
-// registers as raw 16-byte words (chunk j of lane l: columns (64j + l) * 8 ..
-// +7, zero past K), clamped to tau: the codes of the columns below Kp go to
-// qrow, 8 per 32-bit store, and the first lane of each block writes the
-// block's E8M0 byte to the step-major scale array xs (row r of M).
-template <int CH>
-__device__ inline void quantize_bf16_row_mx(const uint4 (&w)[CH], int64_t Kp, float tau,
-                                            uint8_t* __restrict__ qrow, uint8_t* __restrict__ xs,
-                                            int64_t M, int64_t r) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const int64_t c = (int64_t(j) * kWave + lane) * 8;
-    const uint32_t q[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
-    float ax[8];
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ax[2 * i] = fminf(fabsf(__uint_as_float(q[i] << 16)), tau);
-      ax[2 * i + 1] = fminf(fabsf(__uint_as_float(q[i] & 0xffff0000u)), tau);
-      m = fmaxf(m, fmaxf(ax[2 * i], ax[2 * i + 1]));
-    }
-    // every lane takes part in the exchange; a block (four lanes) lies wholly
-    // below Kp or wholly past it
-    const int e = mx_exponent(quad_max(m));
-    if (c < Kp) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        word |= (mx_magnitude(ax[2 * i], e) | ((q[i] >> 12) & 0x8u)) << (8 * i);
-        word |= (mx_magnitude(ax[2 * i + 1], e) | ((q[i] >> 28) & 0x8u)) << (8 * i + 4);
-      }
-      *reinterpret_cast<uint32_t*>(qrow + c / 2) = word;
-      const int64_t b = c / 32;  // block of this chunk
-      if ((lane & 3) == 0) xs[(b / 4) * 4 * M + 4 * r + (b & 3)] = uint8_t(e + 127);
-    }
-  }
-}
-
 }  // namespace fp4lin

@@ -241,8 +241,7 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
     v16f (&acc)[C::FM][C::FN], const float (&sa)[C::FM][16], const float (&sb)[C::FN],
     uint8_t* st0, uint8_t* st1, int wave, int wm, int wn, int lane, int m0, int n0, int M, int N,
     float* __restrict__ Y, int64_t ldy, const CompArgs& cp, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ coo_row, const int32_t* __restrict__ col,
-    const float* __restrict__ val) {
+    const int32_t* __restrict__ col, const float* __restrict__ val) {
   constexpr int FM = C::FM, FN = C::FN, BN = C::BN;
   static_assert(C::BM == 128 && BN == 256 && C::WM == 2 && C::WN == 2 && FM == 2 && FN == 4,
                 "chunk layout of the fused epilogue");
@@ -291,7 +290,6 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
   typedef const __attribute__((address_space(4))) int32_t cint32;
   typedef const __attribute__((address_space(4))) float cfloat;
   cint32* const rp_c = (cint32*)row_ptr;
-  cint32* const row_c = (cint32*)coo_row;
   cint32* const col_c = (cint32*)col;
   cfloat* const val_c = (cfloat*)val;
 
@@ -482,8 +480,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
     const uint8_t* __restrict__ Bq, const float* __restrict__ sB, int M, int N, int ldq,
     int tiles_m, float* __restrict__ Y, int64_t ldy, const uint8_t* __restrict__ As,
     const uint8_t* __restrict__ Bs, CompArgs cp, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ coo_row, const int32_t* __restrict__ col,
-    const float* __restrict__ val) {
+    const int32_t* __restrict__ col, const float* __restrict__ val) {
   constexpr int BM = C::BM, BN = C::BN, WN = C::WN, BKB = C::BKB, CPR = C::CPR;
   constexpr int FM = C::FM, FN = C::FN, NT = C::kThreads;
   constexpr int SB = C::kStageBytes;
@@ -740,7 +737,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   if constexpr (kComp != 0) {
     fused_epilogue<C, kMx, (kComp & 1) != 0, kComp >= 3>(acc, sa, sb, st0, st1, wave, wm, wn,
                                                           lane, m0, n0, M, N, Y, ldy, cp,
-                                                          row_ptr, coo_row, col, val);
+                                                          row_ptr, col, val);
     return;
   }
   // Output through a wave-private LDS block (the stage buffers are free after
@@ -815,7 +812,7 @@ hipError_t run_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const
   if (!fused) {
     fp4_gemm_kernel<C, kMx, 0><<<grid, C::kThreads, 0, stream>>>(
         Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs, cp, nullptr, nullptr,
-        nullptr, nullptr);
+        nullptr);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || sp.row_ptr == nullptr) return e;
     return launch_sparse_add(sp, M, N, Y, ldy, stream);
@@ -831,7 +828,7 @@ hipError_t run_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const
   case MODE:                                                                                    \
     fp4_gemm_kernel<C, kMx, MODE><<<grid, C::kThreads, 0, stream>>>(                            \
         Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs, cp, sp.row_ptr,      \
-        sp.row, sp.col, sp.val);                                                                \
+        sp.col, sp.val);                                                                        \
     break;
   switch (mode) {
     FP4LIN_GEMM_COMP(1)

@@ -22,7 +22,9 @@
 //
 // The block exponent and the element encoder (mx_exponent, mx_magnitude) are
 // in device_common.hpp, shared with the forward's compaction kernel, which
-// block-quantizes the rows of A it already holds (quantize_bf16_row_mx).
+// block-quantizes the rows of A it already holds; the column pass is
+// quantize_cols_mx_body (colquant.hpp), which the forward pairs with the
+// select's row count.
 //
 // Rows (activations): one thread per 8-code chunk of a padded row, so four
 //   consecutive lanes hold one block and its max is two lane exchanges away;
@@ -33,6 +35,7 @@
 //   encode pass; a thread holds 8 consecutive rows of 8 columns, so the four
 //   lanes with the same columns and consecutive row groups hold one block of
 //   each of those columns.
+#include "colquant.hpp"
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -77,55 +80,12 @@ __global__ __launch_bounds__(kMxThreads) void quantize_rows_mx_kernel(
   }
 }
 
-constexpr int kMxTK = 128;  // codes along K per column tile
-constexpr int kMxTN = 128;  // columns per tile
-
-// Tile (bx, by): columns bx*128 .. +127, rows by*128 .. +127 (rows past K read
-// as zero and give the zero padding). Thread (kg, g) = (t % 16, t / 16) owns
-// rows k0 + 8kg .. +7 of columns n0 + 8g .. +7: the 8 codes of one column are
-// one 32-bit word of its packed row, and lanes 4q .. 4q+3 share block q.
+// One workgroup per 128 x 128 tile of W (quantize_cols_mx_body).
 template <class In, bool kAligned>
 __global__ __launch_bounds__(kMxThreads) void quantize_cols_mx_kernel(
     const typename In::T* __restrict__ W, int64_t K, int64_t N, int64_t ldw,
     uint8_t* __restrict__ Wq, int64_t ldq, uint8_t* __restrict__ Ws) {
-  const int t = threadIdx.x;
-  const int kg = t & 15, g = t >> 4;
-  const int64_t n0 = int64_t(blockIdx.x) * kMxTN;
-  const int64_t k0 = int64_t(blockIdx.y) * kMxTK;
-  const int64_t c = n0 + g * 8;
-  const int64_t valid = N - c;
-  const int64_t kr = k0 + kg * 8;
-  Vec8<In> v[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (kr + u < K && valid > 0) {
-      load8<In, kAligned>(W + (kr + u) * ldw + c, valid, v[u]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[u].v[j] = typename In::T(0);
-    }
-  }
-  int e[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float m = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(In::widen(v[u].v[j])));
-    e[j] = mx_exponent(quad_max(m));
-  }
-  if (valid <= 0) return;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= valid) break;
-    uint32_t word = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      word |= (mx_magnitude(fabsf(In::widen(v[u].v[j])), e[j]) | (In::sign_bit(v[u].v[j]) << 3))
-              << (4 * u);
-    *reinterpret_cast<uint32_t*>(Wq + (c + j) * ldq + kr / 2) = word;
-    // rows kr .. kr+7: block kr / 32 of K step kr / 128 (the tile's step by)
-    if ((kg & 3) == 0) Ws[(kr / 128) * 4 * N + 4 * (c + j) + ((kr / 32) & 3)] = uint8_t(e[j] + 127);
-  }
+  quantize_cols_mx_body<In, kAligned>(blockIdx.x, blockIdx.y, W, K, N, ldw, Wq, ldq, Ws);
 }
 
 // chunks of a row across x (at most 64 workgroups), rows across y (at most 65535)

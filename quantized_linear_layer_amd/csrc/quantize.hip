@@ -102,29 +102,36 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
     p[i] = v;
 }
 
+// One-dimensional grids over gx column tiles x row tiles (workgroup b takes
+// tile (b % gx, b / gx)), so the number of row tiles along K is not held to
+// the 65535 of a grid's second dimension.
 template <class In, bool kAligned>
 __global__ __launch_bounds__(256) void colmax_kernel(const typename In::T* __restrict__ W,
                                                      int64_t K, int64_t N, int64_t ldw,
-                                                     uint32_t* __restrict__ colmax) {
-  colmax_body<In, kAligned>(blockIdx.x, blockIdx.y, W, K, N, ldw, colmax);
+                                                     uint32_t* __restrict__ colmax, int64_t gx) {
+  colmax_body<In, kAligned>(blockIdx.x % gx, blockIdx.x / gx, W, K, N, ldw, colmax);
 }
 
 template <class In, bool kAligned>
 __global__ __launch_bounds__(256) void quantize_cols_kernel(
     const typename In::T* __restrict__ W, int64_t K, int64_t N, int64_t ldw,
     const uint32_t* __restrict__ colmax, uint8_t* __restrict__ Wq, int64_t ldq,
-    float* __restrict__ sW) {
-  quantize_cols_body<In, kAligned>(blockIdx.x, blockIdx.y, W, K, N, ldw, colmax, Wq, ldq, sW);
+    float* __restrict__ sW, int64_t gx) {
+  quantize_cols_body<In, kAligned>(blockIdx.x % gx, blockIdx.x / gx, W, K, N, ldw, colmax, Wq,
+                                   ldq, sW);
 }
 
 // the column maxima (into colmax, which starts at zero) and the codes
 template <class In, bool kAligned>
 void launch_col_passes(const typename In::T* W, int64_t K, int64_t N, int64_t ldw, uint8_t* Wq,
                        int64_t ldq, float* sW, uint32_t* colmax, hipStream_t stream) {
-  dim3 g1(unsigned((N + kColStrip - 1) / kColStrip), unsigned((K + kColRows - 1) / kColRows));
-  colmax_kernel<In, kAligned><<<g1, 256, 0, stream>>>(W, K, N, ldw, colmax);
-  dim3 g2(unsigned((N + kTN - 1) / kTN), unsigned((ldq * 2) / kTK));
-  quantize_cols_kernel<In, kAligned><<<g2, 256, 0, stream>>>(W, K, N, ldw, colmax, Wq, ldq, sW);
+  const int64_t gx1 = (N + kColStrip - 1) / kColStrip;
+  const int64_t g1 = gx1 * ((K + kColRows - 1) / kColRows);
+  colmax_kernel<In, kAligned><<<dim3(unsigned(g1)), 256, 0, stream>>>(W, K, N, ldw, colmax, gx1);
+  const int64_t gx2 = (N + kTN - 1) / kTN;
+  const int64_t g2 = gx2 * ((ldq * 2) / kTK);
+  quantize_cols_kernel<In, kAligned><<<dim3(unsigned(g2)), 256, 0, stream>>>(W, K, N, ldw, colmax,
+                                                                             Wq, ldq, sW, gx2);
 }
 
 template <class In, bool kAligned>
@@ -242,13 +249,6 @@ hipError_t launch_quantize_weight(const void* W, bool bf16, int64_t K, int64_t N
                    : run_quantize_weight<BF16In, false>(W, K, N, ldw, Wq, ldq, sW, ws, stream);
   return aligned ? run_quantize_weight<F32In, true>(W, K, N, ldw, Wq, ldq, sW, ws, stream)
                  : run_quantize_weight<F32In, false>(W, K, N, ldw, Wq, ldq, sW, ws, stream);
-}
-
-hipError_t launch_quantize_weight_cleared(const uint16_t* W, int64_t K, int64_t N, int64_t ldw,
-                                          uint8_t* Wq, int64_t ldq, float* sW, uint32_t* colmax,
-                                          hipStream_t stream) {
-  launch_col_passes<BF16In, true>(W, K, N, ldw, Wq, ldq, sW, colmax, stream);
-  return hipGetLastError();
 }
 
 }  // namespace fp4lin

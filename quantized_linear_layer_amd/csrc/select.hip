@@ -33,8 +33,11 @@
 // Then the entries with |a| > tau are counted per row, with one total per
 // workgroup of rows; the compaction adds up the totals of the workgroups before
 // its own, which gives row_ptr and the row-major positions without a separate
-// scan. In the whole-layer forward, bfloat16 rows that fit one slab are also
-// quantized token-wise by the compaction kernel, from the same registers.
+// scan. In the whole-layer forward the count also records each row's amax
+// clamped to tau and the compaction quantizes A from the slabs it holds, while
+// W's quantization runs in the same launches.
+#include <type_traits>
+
 #include "colquant.hpp"
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -419,6 +422,18 @@ __device__ inline uint32_t fine_pick(const SelState* st, const uint32_t* __restr
 // [g*R, min(M, (g+1)*R)), R = kRowWaves * rpw; wave w takes rows
 // g*R + w + kRowWaves*i, so the workgroup walks its range in batches of
 // kRowWaves consecutive rows.
+//
+// A row streams through in slabs (for_row_slabs): slabs of 8 chunks of 8
+// elements per lane while they fit, then one slab each of 4, 2 and 1 chunks
+// where it fits, then one 1-chunk slab over the ragged end. Only that last
+// slab reaches past K, so only its loads need bounds, and all loads of a slab
+// are issued before the first is used.
+//
+// In the whole-layer forward the count also takes each row's amax clamped to
+// tau, and the compaction encodes every slab it compacts with the scale that
+// follows from that amax: A is read once by each kernel and its quantization
+// needs no pass of its own, for any K, dtype and row alignment. The
+// micro-scaled format needs no row amax (a block lies inside one chunk sweep).
 // ---------------------------------------------------------------------------
 constexpr int64_t kMaxRowGroups = 2048;
 
@@ -431,82 +446,175 @@ __host__ inline int64_t row_groups(int64_t M) {
   return (M + R - 1) / R;
 }
 
-template <class In, int CH>
-__device__ inline uint32_t count_above(const Vec8<In> (&v)[CH], uint32_t tkey) {
-  // chunks past K are zero and a zero key never exceeds tkey
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int j = 0; j < CH; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cnt += In::key(v[j].v[i]) > tkey ? 1u : 0u;
-  return cnt;
+template <int N>
+struct Ch {
+  static constexpr int value = N;
+};
+template <bool B>
+using Full = std::integral_constant<bool, B>;
+
+// f(Ch<CH>, Full<inside>, c0) for each slab of a row of K elements.
+template <class F>
+__device__ __attribute__((always_inline)) inline void for_row_slabs(int64_t K, F&& f) {
+  constexpr int64_t S = int64_t(kWave) * 8;  // columns of one chunk sweep
+  int64_t c0 = 0;
+  for (; c0 + 8 * S <= K; c0 += 8 * S) f(Ch<8>{}, Full<true>{}, c0);
+  if (c0 + 4 * S <= K) {
+    f(Ch<4>{}, Full<true>{}, c0);
+    c0 += 4 * S;
+  }
+  if (c0 + 2 * S <= K) {
+    f(Ch<2>{}, Full<true>{}, c0);
+    c0 += 2 * S;
+  }
+  if (c0 + S <= K) {
+    f(Ch<1>{}, Full<true>{}, c0);
+    c0 += S;
+  }
+  if (c0 < K) f(Ch<1>{}, Full<false>{}, c0);
 }
 
-// Per-row count of |a| > tau into cnt[r], and the workgroup's total into
-// gsum[blockIdx.x]. kPick (bfloat16): tau's key comes from the fine histogram
-// and workgroup 0 records it in st and tau; otherwise it is read from st.
-// (Looking the key up between the first row's loads and their use measured
-// slower: it costs registers.)
-template <class In, bool kFast, int CH, bool kPick>
-__device__ __attribute__((always_inline)) inline void count_rows_body(
-    int64_t bid, const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda,
-    int64_t rpw, SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
-    uint32_t* __restrict__ cnt, uint32_t* __restrict__ gsum) {
-  __shared__ uint32_t wsum[kRowWaves];
-  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);  // wave-uniform
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t R = int64_t(kRowWaves) * rpw;
-  const int64_t r0 = bid * R;
-  const int64_t r1 = (r0 + R < M) ? r0 + R : M;
-  const int64_t slab = int64_t(kWave) * CH * 8;
-  uint32_t tkey;
-  if constexpr (kPick) {
-    tkey = fine_pick(st, fine);
-    if (bid == 0 && threadIdx.x == 0) {
-      st->tau_key = tkey;
-      *tau = In::key_to_float(tkey);
+// A chunk of 8 consecutive elements as loaded: bfloat16 as its raw 16-byte
+// word (element i is the low half of 32-bit word i / 2 for even i, the high
+// half for odd i), float32 as 8 floats.
+template <class In>
+struct RowChunk;
+template <>
+struct RowChunk<BF16In> {
+  using T = uint4;
+};
+template <>
+struct RowChunk<F32In> {
+  using T = Vec8<F32In>;
+};
+
+// Chunk c (elements c .. c+7) of a row of K elements, zero past K. kFast: the
+// row is 16-byte aligned and K % 8 == 0 (vector loads; a chunk is wholly inside
+// the row or wholly past it). kFull: the chunk lies inside the row.
+template <bool kFast, bool kFull>
+__device__ inline void load_row_chunk(const uint16_t* __restrict__ row, int64_t c, int64_t K,
+                                      uint4& w) {
+  if constexpr (kFast) {
+    if constexpr (kFull) {
+      w = *reinterpret_cast<const uint4*>(row + c);
+    } else {
+      w = *reinterpret_cast<const uint4*>(row + (c < K ? c : K - 8));
+      if (c >= K) w = make_uint4(0, 0, 0, 0);
     }
   } else {
-    tkey = st->tau_key;
-  }
-  uint32_t total = 0;
-  for (int64_t r = r0 + w; r < r1; r += kRowWaves) {
-    const typename In::T* row = A + r * lda;
-    uint32_t c = 0;
-    for (int64_t c0 = 0; c0 < K; c0 += slab) {
-      Vec8<In> v[CH];
-      load_wave_slab<In, kFast, CH>(row, c0, K, v);
-      c += count_above<In, CH>(v, tkey);
-    }
-    c = wave_sum_u32(c);
-    total += c;
-    if (lane == 0) cnt[r] = c;
-  }
-  if (lane == 0) wsum[w] = total;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t s = 0;
+    uint32_t h[8];
 #pragma unroll
-    for (int i = 0; i < kRowWaves; ++i) s += wsum[i];
-    gsum[bid] = s;
+    for (int i = 0; i < 8; ++i) h[i] = (kFull || c + i < K) ? uint32_t(row[c + i]) : 0u;
+    w = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                   h[6] | (h[7] << 16));
   }
 }
 
-template <class In, bool kFast, int CH, bool kPick>
-__global__ __launch_bounds__(kRowWaves * kWave) void count_rows_kernel(
-    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
-    SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
-    uint32_t* __restrict__ cnt, uint32_t* __restrict__ gsum) {
-  count_rows_body<In, kFast, CH, kPick>(blockIdx.x, A, M, K, lda, rpw, st, fine, tau, cnt, gsum);
+template <bool kFast, bool kFull>
+__device__ inline void load_row_chunk(const float* __restrict__ row, int64_t c, int64_t K,
+                                      Vec8<F32In>& v) {
+  if constexpr (kFull)
+    load8<F32In, kFast>(row + c, 8, v);
+  else
+    load_chunk<F32In, kFast>(row, c, K, v);
 }
 
-// Write every |a| > tau entry of a row, ascending column, from position pos.
+// Chunk j of lane l starts at column c0 + (64j + l) * 8.
+template <class In, bool kFast, bool kFull, int CH>
+__device__ inline void load_row_slab(const typename In::T* __restrict__ row, int64_t c0,
+                                     int64_t K, typename RowChunk<In>::T (&v)[CH]) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+    load_row_chunk<kFast, kFull>(row, c0 + (int64_t(j) * kWave + lane) * 8, K, v[j]);
+}
+
+// Count of the entries of a chunk with |a| > tau (chunks past K are zero, and
+// a zero key never exceeds tau's) added to n, and with kMax the running
+// maximum of the magnitude keys folded into m. bfloat16, two keys per 32-bit
+// word: adding bias = 0x7fff - tkey to each 15-bit key sets bit 15 of its half
+// exactly when key > tkey (no carry crosses the halves), so one population
+// count covers both; m holds two 16-bit maxima (one packed integer max per
+// word).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <bool kMax>
+__device__ inline void count_fold(const uint4& w, uint32_t bias2, uint32_t& n, uint32_t& m) {
+  const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+  u16x2 m2 = __builtin_bit_cast(u16x2, m);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t k2 = q[i] & 0x7fff7fffu;
+    n += uint32_t(__popc((k2 + bias2) & 0x80008000u));
+    if constexpr (kMax) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, k2));
+  }
+  m = __builtin_bit_cast(uint32_t, m2);
+}
+
+// float32: adding bias = 0x7fffffff - tkey to a 31-bit key sets bit 31 exactly
+// when key > tkey.
+template <bool kMax>
+__device__ inline void count_fold(const Vec8<F32In>& v, uint32_t bias, uint32_t& n,
+                                  uint32_t& m) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t k = F32In::key(v.v[i]);
+    n += (k + bias) >> 31;
+    if constexpr (kMax) m = m > k ? m : k;
+  }
+}
+
+// The bias of count_fold for tau's key (bfloat16: in both halves).
+template <class In>
+__device__ inline uint32_t count_bias(uint32_t tkey) {
+  if constexpr (In::kBytes == 2)
+    return (0x7fffu - tkey) * 0x00010001u;
+  else
+    return 0x7fffffffu - tkey;
+}
+
+// The row's largest key, from every lane's running maximum.
+template <class In>
+__device__ inline uint32_t row_key_max(uint32_t m) {
+  if constexpr (In::kBytes == 2) {
+    const uint32_t lo = m & 0xffffu, hi = m >> 16;
+    m = lo > hi ? lo : hi;
+  }
+  return wave_max_u32(m);
+}
+
+// Value of element i (0 .. 7, not a compile-time constant) of a chunk, taken
+// from the chunk's 64-bit halves with shifts and selects of whole values, so
+// that the chunk is never indexed through memory.
+__device__ inline float chunk_value(const uint4& w, int i) {
+  const uint64_t lo = (uint64_t(w.y) << 32) | w.x, hi = (uint64_t(w.w) << 32) | w.z;
+  const uint64_t d = (i & 4) ? hi : lo;
+  return __uint_as_float(uint32_t(d >> (16 * (i & 3))) << 16);
+}
+
+__device__ inline float chunk_value(const Vec8<F32In>& v, int i) {
+  uint64_t q[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    q[u] = (uint64_t(__float_as_uint(v.v[2 * u + 1])) << 32) | __float_as_uint(v.v[2 * u]);
+  const uint64_t d = (i & 4) ? ((i & 2) ? q[3] : q[2]) : ((i & 2) ? q[1] : q[0]);
+  return __uint_as_float(uint32_t(d >> (32 * (i & 1))));
+}
+
+__device__ inline uint32_t chunk_key(const uint4& w, int i) {
+  const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+  return ((i & 1) ? (q[i >> 1] >> 16) : q[i >> 1]) & 0x7fffu;
+}
+
+__device__ inline uint32_t chunk_key(const Vec8<F32In>& v, int i) { return F32In::key(v.v[i]); }
+
+// Write every |a| > tau entry of a slab, ascending column, from position pos.
 // The entries of chunk (j, lane) follow those of all chunks (j', *) with
 // j' < j and (j, lane') with lane' < lane; per element position i of a chunk
 // a wave ballot of the predicate gives, through mbcnt, how many entries the
 // lower lanes hold at that position, so the rank needs no LDS and no barrier.
-template <class In, int CH>
-__device__ inline void compact_slab(const Vec8<In> (&v)[CH], int64_t c0, int64_t r, uint32_t tkey,
+template <class C, int CH>
+__device__ inline void compact_slab(const C (&v)[CH], int64_t c0, int64_t r, uint32_t tkey,
                                     float tau, uint32_t& pos, uint32_t cap,
                                     int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
                                     float* __restrict__ out_val) {
@@ -516,7 +624,7 @@ __device__ inline void compact_slab(const Vec8<In> (&v)[CH], int64_t c0, int64_t
     uint32_t lower = 0, total = 0, mine = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bool p = In::key(v[j].v[i]) > tkey;
+      const bool p = chunk_key(v[j], i) > tkey;
       const uint64_t b = __ballot(p);
       lower = __builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32),
                                         __builtin_amdgcn_mbcnt_lo(uint32_t(b), lower));
@@ -531,13 +639,10 @@ __device__ inline void compact_slab(const Vec8<In> (&v)[CH], int64_t c0, int64_t
     while (mine) {
       const int i = __builtin_ctz(mine);
       mine &= mine - 1u;
-      typename In::T x = v[j].v[0];
-#pragma unroll
-      for (int q = 1; q < 8; ++q) x = (i == q) ? v[j].v[q] : x;
       // p < cap always holds when tau is the true order statistic
       // (nnz <= n-1-k); the test only keeps a wrong tau from writing out of bounds.
       if (p < cap) {
-        const float a = In::widen(x);
+        const float a = chunk_value(v[j], i);
         out_row[p] = int32_t(r);
         out_col[p] = c + i;
         out_val[p] = __fsub_rn(a, copysignf(tau, a));
@@ -548,118 +653,154 @@ __device__ inline void compact_slab(const Vec8<In> (&v)[CH], int64_t c0, int64_t
   }
 }
 
-// Row-major COO and row_ptr. The workgroup's first position is the sum of the
-// totals of the workgroups before it; within a batch of kRowWaves rows a wave
-// adds the counts of the lower rows of the batch, so waves need no barrier
-// after the first.
-template <class In, bool kFast, int CH>
-__global__ __launch_bounds__(kRowWaves * kWave) void compact_rows_kernel(
-    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
-    const SelState* __restrict__ st, const float* __restrict__ tau_p,
-    const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
-    int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
-    float* __restrict__ out_val) {
+// Token-wise codes of a chunk clamped to tau, 8 per 32-bit word (low nibble
+// first). bfloat16 with quick (4 * inv finite): two codes per word of the
+// chunk from y4 = RN32(|x| * 4inv) (bf16_pair_code); otherwise, and for
+// float32, the generic encoder.
+__device__ inline uint32_t encode_chunk(const uint4& w, float tau, float inv, float inv4,
+                                        bool quick) {
+  if (quick)
+    return bf16_pair_code(w.x, tau, inv4) | (bf16_pair_code(w.y, tau, inv4) << 8) |
+           (bf16_pair_code(w.z, tau, inv4) << 16) | (bf16_pair_code(w.w, tau, inv4) << 24);
+  return bf16_pair_code_slow(w.x, tau, inv) | (bf16_pair_code_slow(w.y, tau, inv) << 8) |
+         (bf16_pair_code_slow(w.z, tau, inv) << 16) | (bf16_pair_code_slow(w.w, tau, inv) << 24);
+}
+
+__device__ inline uint32_t encode_chunk(const Vec8<F32In>& v, float tau, float inv, float,
+                                        bool) {
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    word |= (e2m1_magnitude(fminf(fabsf(v.v[i]), tau), inv) | (F32In::sign_bit(v.v[i]) << 3))
+            << (4 * i);
+  return word;
+}
+
+// Micro-scaled codes of a chunk clamped to tau and the exponent of its block
+// (four consecutive lanes; every lane of the wave takes part in the exchange).
+__device__ inline uint32_t encode_chunk_mx(const uint4& w, float tau, int& e) {
+  const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+  float ax[8];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ax[2 * i] = fminf(fabsf(__uint_as_float(q[i] << 16)), tau);
+    ax[2 * i + 1] = fminf(fabsf(__uint_as_float(q[i] & 0xffff0000u)), tau);
+    m = fmaxf(m, fmaxf(ax[2 * i], ax[2 * i + 1]));
+  }
+  e = mx_exponent(quad_max(m));
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    word |= (mx_magnitude(ax[2 * i], e) | ((q[i] >> 12) & 0x8u)) << (8 * i);
+    word |= (mx_magnitude(ax[2 * i + 1], e) | ((q[i] >> 28) & 0x8u)) << (8 * i + 4);
+  }
+  return word;
+}
+
+__device__ inline uint32_t encode_chunk_mx(const Vec8<F32In>& v, float tau, int& e) {
+  float ax[8];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ax[i] = fminf(fabsf(v.v[i]), tau);
+    m = fmaxf(m, ax[i]);
+  }
+  e = mx_exponent(quad_max(m));
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    word |= (mx_magnitude(ax[i], e) | (F32In::sign_bit(v.v[i]) << 3)) << (4 * i);
+  return word;
+}
+
+// Per-row count of |a| > tau into cnt[r], and the workgroup's total into
+// gsum[blockIdx.x]. kPick (bfloat16): tau's key comes from the fine histogram
+// and workgroup 0 records it in st and tau; otherwise it is read from st.
+// (Looking the key up between the first row's loads and their use measured
+// slower: it costs registers.) kAmax: also the row's amax clamped to tau into
+// amax[r].
+template <class In, bool kFast, bool kPick, bool kAmax>
+__device__ __attribute__((always_inline)) inline void count_rows_body(
+    int64_t bid, const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda,
+    int64_t rpw, SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
+    uint32_t* __restrict__ cnt, uint32_t* __restrict__ gsum, float* __restrict__ amax) {
+  using C = typename RowChunk<In>::T;
   __shared__ uint32_t wsum[kRowWaves];
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);  // wave-uniform
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t R = int64_t(kRowWaves) * rpw;
-  const int64_t r0 = int64_t(blockIdx.x) * R;
+  const int64_t r0 = bid * R;
   const int64_t r1 = (r0 + R < M) ? r0 + R : M;
-  const int64_t slab = int64_t(kWave) * CH * 8;
-  const uint32_t tkey = st->tau_key;
-  const float tau = *tau_p;
-  const uint32_t cap = uint32_t(capacity < INT32_MAX ? capacity : INT32_MAX);
-  if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
-  // entries of the workgroups before this one
-  uint32_t base = 0;
-  {
+  uint32_t tkey;
+  if constexpr (kPick) {
+    tkey = fine_pick(st, fine);
+    if (bid == 0 && threadIdx.x == 0) {
+      st->tau_key = tkey;
+      *tau = In::key_to_float(tkey);
+    }
+  } else {
+    tkey = st->tau_key;
+  }
+  const uint32_t bias = count_bias<In>(tkey);
+  uint32_t total = 0;
+  for (int64_t r = r0 + w; r < r1; r += kRowWaves) {
+    const typename In::T* row = A + r * lda;
+    uint32_t c = 0, mk = 0;
+    for_row_slabs(K, [&](auto ch, auto full, int64_t c0) __attribute__((always_inline)) {
+      constexpr int CH = decltype(ch)::value;
+      C v[CH];
+      load_row_slab<In, kFast, decltype(full)::value, CH>(row, c0, K, v);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) count_fold<kAmax>(v[j], bias, c, mk);
+    });
+    c = wave_sum_u32(c);
+    total += c;
+    if (lane == 0) cnt[r] = c;
+    if constexpr (kAmax) {
+      const uint32_t k = row_key_max<In>(mk);
+      if (lane == 0) amax[r] = In::key_to_float(k < tkey ? k : tkey);
+    }
+  }
+  if (lane == 0) wsum[w] = total;
+  __syncthreads();
+  if (threadIdx.x == 0) {
     uint32_t s = 0;
-    for (int64_t g = threadIdx.x; g < int64_t(blockIdx.x); g += kRowWaves * kWave) s += gsum[g];
-    s = wave_sum_u32(s);
-    if (lane == 0) wsum[w] = s;
-    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kRowWaves; ++i) base += wsum[i];
-  }
-  for (int64_t rb = r0; rb < r1; rb += kRowWaves) {
-    const int64_t r = rb + w;
-    uint32_t before = 0, all = 0, own = 0;
-#pragma unroll
-    for (int j = 0; j < kRowWaves; ++j) {
-      const uint32_t cj = (rb + j < r1) ? cnt[rb + j] : 0u;
-      before += (j < w) ? cj : 0u;
-      own = (j == w) ? cj : own;
-      all += cj;
-    }
-    if (r < r1) {
-      const typename In::T* row = A + r * lda;
-      uint32_t pos = base + before;
-      for (int64_t c0 = 0; c0 < K; c0 += slab) {
-        Vec8<In> v[CH];
-        load_wave_slab<In, kFast, CH>(row, c0, K, v);
-        compact_slab<In, CH>(v, c0, r, tkey, tau, pos, cap, out_row, out_col, out_val);
-      }
-      if (lane == 0) row_ptr[r + 1] = int32_t(base + before + own);
-    }
-    base += all;
+    for (int i = 0; i < kRowWaves; ++i) s += wsum[i];
+    gsum[bid] = s;
   }
 }
 
-// Compaction from a bfloat16 row held as raw 16-byte words (element i of a
-// chunk is the low half of word i / 2 for even i, the high half for odd i),
-// ranked as in compact_slab.
-template <int CH>
-__device__ inline void compact_words(const uint4 (&wv)[CH], int64_t r, uint32_t tkey, float tau,
-                                     uint32_t& pos, uint32_t cap, int32_t* __restrict__ out_row,
-                                     int32_t* __restrict__ out_col, float* __restrict__ out_val) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const uint32_t q[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
-    uint32_t lower = 0, total = 0, mine = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t key = ((i & 1) ? (q[i >> 1] >> 16) : q[i >> 1]) & 0x7fffu;
-      const bool p = key > tkey;
-      const uint64_t b = __ballot(p);
-      lower = __builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32),
-                                        __builtin_amdgcn_mbcnt_lo(uint32_t(b), lower));
-      total += uint32_t(__popcll(b));
-      mine |= uint32_t(p) << i;
-    }
-    uint32_t p = pos + lower;  // positions below capacity < 2^31, columns below K < 2^31
-    const int c = (j * kWave + lane) * 8;
-    while (mine) {
-      const int i = __builtin_ctz(mine);
-      mine &= mine - 1u;
-      const int h = i >> 1;
-      const uint32_t word = h == 0 ? q[0] : (h == 1 ? q[1] : (h == 2 ? q[2] : q[3]));
-      // p < cap always holds when tau is the true order statistic
-      if (p < cap) {
-        const float a = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
-        out_row[p] = int32_t(r);
-        out_col[p] = c + i;
-        out_val[p] = __fsub_rn(a, copysignf(tau, a));
-      }
-      ++p;
-    }
-    pos += total;
-  }
+template <class In, bool kFast, bool kPick>
+__global__ __launch_bounds__(kRowWaves * kWave) void count_rows_kernel(
+    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+    SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
+    uint32_t* __restrict__ cnt, uint32_t* __restrict__ gsum) {
+  count_rows_body<In, kFast, kPick, false>(blockIdx.x, A, M, K, lda, rpw, st, fine, tau, cnt,
+                                           gsum, nullptr);
 }
 
-// Forward path, 16-byte aligned bfloat16 rows with K % 8 == 0 whose padded
-// length fits one slab: the compaction of compact_rows_kernel and the
-// token-wise quantization of the row clamped to tau (quantize_bf16_row) from
-// one read of A; with kMx, its micro-scaled quantization instead
-// (quantize_bf16_row_mx, block scales into the step-major array Xs).
-template <int CH, bool kMx = false>
-__device__ __attribute__((always_inline)) inline void compact_quantize_rows_body(
-    int64_t bid, const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
-    const SelState* __restrict__ st, const float* __restrict__ tau_p,
+// What the compaction also does with the slabs it holds.
+constexpr int kQuantNone = 0;   // nothing (the select alone)
+constexpr int kQuantToken = 1;  // token-wise codes; sX[r] holds the row's clamped amax on entry
+                                // and its scale on exit
+constexpr int kQuantMx = 2;     // micro-scaled codes and block scales (Xs, step-major)
+
+// Row-major COO and row_ptr. The workgroup's first position is the sum of the
+// totals of the workgroups before it; within a batch of kRowWaves rows a wave
+// adds the counts of the lower rows of the batch, so waves need no barrier
+// after the first. With kQuant, the codes of the row's padded length ldq * 2
+// (zero past K) go to Xq + r * ldq.
+template <class In, bool kFast, int kQuant>
+__device__ __attribute__((always_inline)) inline void compact_rows_body(
+    int64_t bid, const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda,
+    int64_t rpw, const SelState* __restrict__ st, const float* __restrict__ tau_p,
     const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
     float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX,
-    uint8_t* __restrict__ Xs = nullptr) {
+    uint8_t* __restrict__ Xs) {
+  using C = typename RowChunk<In>::T;
   __shared__ uint32_t wsum[kRowWaves];
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);  // wave-uniform
   const int lane = threadIdx.x & (kWave - 1);
@@ -669,6 +810,7 @@ __device__ __attribute__((always_inline)) inline void compact_quantize_rows_body
   const uint32_t tkey = st->tau_key;
   const float tau = *tau_p;
   const uint32_t cap = uint32_t(capacity < INT32_MAX ? capacity : INT32_MAX);
+  const int64_t Kp = ldq * 2;
   if (bid == 0 && threadIdx.x == 0) row_ptr[0] = 0;
   // entries of the workgroups before this one
   uint32_t base = 0;
@@ -692,44 +834,66 @@ __device__ __attribute__((always_inline)) inline void compact_quantize_rows_body
       all += cj;
     }
     if (r < r1) {
-      const uint16_t* row = A + r * lda;
-      uint4 wv[CH];
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const int64_t c = (int64_t(j) * kWave + lane) * 8;
-        wv[j] = *reinterpret_cast<const uint4*>(row + (c < K ? c : K - 8));
-        if (c >= K) wv[j] = make_uint4(0, 0, 0, 0);
+      const typename In::T* row = A + r * lda;
+      uint8_t* qrow = Xq + r * ldq;
+      float inv = 0.0f, inv4 = 0.0f;
+      if constexpr (kQuant == kQuantToken) {
+        float s;
+        vector_scale(sX[r], s, inv);
+        inv4 = __fmul_rn(inv, 4.0f);
+        if (lane == 0) sX[r] = s;
       }
+      const bool quick = inv4 < __builtin_huge_valf();
       uint32_t pos = base + before;
-      compact_words<CH>(wv, r, tkey, tau, pos, cap, out_row, out_col, out_val);
-      if constexpr (kMx)
-        quantize_bf16_row_mx<CH>(wv, ldq * 2, tau, Xq + r * ldq, Xs, M, r);
-      else
-        quantize_bf16_row<CH>(wv, ldq * 2, tau, Xq + r * ldq, sX + r);
+      for_row_slabs(K, [&](auto ch, auto full, int64_t c0) __attribute__((always_inline)) {
+        constexpr int CH = decltype(ch)::value;
+        constexpr bool kFull = decltype(full)::value;
+        C v[CH];
+        load_row_slab<In, kFast, kFull, CH>(row, c0, K, v);
+        compact_slab<C, CH>(v, c0, r, tkey, tau, pos, cap, out_row, out_col, out_val);
+        if constexpr (kQuant != kQuantNone) {
+#pragma unroll
+          for (int j = 0; j < CH; ++j) {
+            // chunks in [K, Kp) are zero and encode to the zero padding
+            const int64_t c = c0 + (int64_t(j) * kWave + lane) * 8;
+            if constexpr (kQuant == kQuantToken) {
+              const uint32_t word = encode_chunk(v[j], tau, inv, inv4, quick);
+              if (kFull || c < Kp) *reinterpret_cast<uint32_t*>(qrow + c / 2) = word;
+            } else {
+              int e;
+              const uint32_t word = encode_chunk_mx(v[j], tau, e);
+              if (kFull || c < Kp) {
+                *reinterpret_cast<uint32_t*>(qrow + c / 2) = word;
+                const int64_t b = c / 32;  // block of this chunk
+                if ((lane & 3) == 0) Xs[(b / 4) * 4 * M + 4 * r + (b & 3)] = uint8_t(e + 127);
+              }
+            }
+          }
+        }
+      });
       if (lane == 0) row_ptr[r + 1] = int32_t(base + before + own);
     }
     base += all;
   }
 }
 
-template <int CH, bool kMx = false>
-__global__ __launch_bounds__(kRowWaves * kWave) void compact_quantize_rows_kernel(
-    const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+template <class In, bool kFast>
+__global__ __launch_bounds__(kRowWaves * kWave) void compact_rows_kernel(
+    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
     const SelState* __restrict__ st, const float* __restrict__ tau_p,
     const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
-    float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX,
-    uint8_t* __restrict__ Xs) {
-  compact_quantize_rows_body<CH, kMx>(blockIdx.x, A, M, K, lda, rpw, st, tau_p, cnt, gsum,
-                                      capacity, row_ptr, out_row, out_col, out_val, Xq, ldq, sX,
-                                      Xs);
+    float* __restrict__ out_val) {
+  compact_rows_body<In, kFast, kQuantNone>(blockIdx.x, A, M, K, lda, rpw, st, tau_p, cnt, gsum,
+                                           capacity, row_ptr, out_row, out_col, out_val, nullptr,
+                                           0, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------------------
-// Whole-layer forward, bfloat16 with aligned rows: the quantization of W has
-// no dependence on the select, so its two passes share launches with the
-// select's row kernels (the column maxima with the row count, the codes with
-// the compaction), and its cleared maxima come from the coarse pass.
+// Whole-layer forward: the quantization of W has no dependence on the select,
+// so its passes share launches with the select's row kernels: the column
+// maxima (micro-scaled: W's only pass) with the row count, the codes with the
+// compaction. The cleared column maxima come from the first histogram pass.
 // ---------------------------------------------------------------------------
 // Launch index b of a pair launch of na + nb workgroups belongs to the first
 // body when floor((b+1)*na/(na+nb)) > floor(b*na/(na+nb)); the two kinds are
@@ -741,42 +905,56 @@ __device__ inline bool pair_first(int64_t b, int64_t na, int64_t nb, int64_t& id
   return hi > lo;
 }
 
-struct ColQuantArgs {
-  const uint16_t* W;
+// W's side of a pair launch: nb workgroups over a gx-wide grid of tiles.
+struct WPass {
+  const void* W;
   int64_t K, N, ldw;
-  uint32_t* colmax;
+  uint32_t* colmax;  // token-wise column maxima (cleared by the first histogram pass)
   uint8_t* Wq;
   int64_t ldq;
-  float* sW;
+  void* sW;  // token-wise: float scales; micro-scaled: step-major E8M0 bytes
+  int64_t gx, nb;
 };
 
-template <int CH>
-__global__ __launch_bounds__(kRowWaves * kWave) void count_colmax_kernel(
-    const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw, SelState* st,
-    const uint32_t* __restrict__ fine, float* __restrict__ tau, uint32_t* __restrict__ cnt,
-    uint32_t* __restrict__ gsum, int64_t na, ColQuantArgs cq, int64_t gx, int64_t nb) {
+template <class In, bool kFast, bool kWAligned, bool kMx>
+__global__ __launch_bounds__(kRowWaves * kWave) void count_wpass_kernel(
+    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+    SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
+    uint32_t* __restrict__ cnt, uint32_t* __restrict__ gsum, float* __restrict__ amax, int64_t na,
+    WPass wp) {
+  using T = typename In::T;
   int64_t i;
-  if (pair_first(blockIdx.x, na, nb, i))
-    count_rows_body<BF16In, true, CH, true>(i, A, M, K, lda, rpw, st, fine, tau, cnt, gsum);
+  if (pair_first(blockIdx.x, na, wp.nb, i))
+    count_rows_body<In, kFast, In::kBytes == 2, !kMx>(i, A, M, K, lda, rpw, st, fine, tau, cnt,
+                                                      gsum, amax);
+  else if constexpr (kMx)
+    quantize_cols_mx_body<In, kWAligned>(i % wp.gx, i / wp.gx, static_cast<const T*>(wp.W), wp.K,
+                                         wp.N, wp.ldw, wp.Wq, wp.ldq,
+                                         static_cast<uint8_t*>(wp.sW));
   else
-    colmax_body<BF16In, true>(i % gx, i / gx, cq.W, cq.K, cq.N, cq.ldw, cq.colmax);
+    colmax_body<In, kWAligned>(i % wp.gx, i / wp.gx, static_cast<const T*>(wp.W), wp.K, wp.N,
+                               wp.ldw, wp.colmax);
 }
 
-template <int CH>
-__global__ __launch_bounds__(kRowWaves * kWave) void compact_qcols_kernel(
-    const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
+template <class In, bool kFast, bool kWAligned, bool kMx>
+__global__ __launch_bounds__(kRowWaves * kWave) void compact_wpass_kernel(
+    const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
     const SelState* __restrict__ st, const float* __restrict__ tau_p,
     const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
     float* __restrict__ out_val, uint8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sX,
-    int64_t na, ColQuantArgs cq, int64_t gx, int64_t nb) {
+    uint8_t* __restrict__ Xs, int64_t na, WPass wp) {
+  using T = typename In::T;
   int64_t i;
-  if (pair_first(blockIdx.x, na, nb, i))
-    compact_quantize_rows_body<CH>(i, A, M, K, lda, rpw, st, tau_p, cnt, gsum, capacity, row_ptr,
-                                   out_row, out_col, out_val, Xq, ldq, sX);
-  else
-    quantize_cols_body<BF16In, true>(i % gx, i / gx, cq.W, cq.K, cq.N, cq.ldw, cq.colmax, cq.Wq,
-                                     cq.ldq, cq.sW);
+  if (pair_first(blockIdx.x, na, wp.nb, i))
+    compact_rows_body<In, kFast, kMx ? kQuantMx : kQuantToken>(i, A, M, K, lda, rpw, st, tau_p,
+                                                               cnt, gsum, capacity, row_ptr,
+                                                               out_row, out_col, out_val, Xq, ldq,
+                                                               sX, Xs);
+  else if constexpr (!kMx)
+    quantize_cols_body<In, kWAligned>(i % wp.gx, i / wp.gx, static_cast<const T*>(wp.W), wp.K,
+                                      wp.N, wp.ldw, wp.colmax, wp.Wq, wp.ldq,
+                                      static_cast<float*>(wp.sW));
 }
 
 // Words after the 256-byte state: bfloat16 has the coarse partial rows, the
@@ -791,10 +969,16 @@ constexpr size_t hist_words() {
     return size_t(F32Digits::kPasses) * kHistBins;
 }
 
-__global__ void select_init_kernel(SelState* st, uint32_t* hist, int64_t nwords, int64_t k) {
+// float32 set-up: clears the histograms (and nclear words at clear) and sets
+// the state to rank k of all keys.
+__global__ void select_init_kernel(SelState* st, uint32_t* hist, int64_t nwords, int64_t k,
+                                   uint32_t* clear, int64_t nclear) {
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nwords;
        i += int64_t(gridDim.x) * blockDim.x)
     hist[i] = 0u;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nclear;
+       i += int64_t(gridDim.x) * blockDim.x)
+    clear[i] = 0u;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     st->prefix = 0u;
     st->tau_key = 0u;
@@ -802,101 +986,31 @@ __global__ void select_init_kernel(SelState* st, uint32_t* hist, int64_t nwords,
   }
 }
 
-// Quantization outputs of the forward path: when Xq is set and the rows
-// qualify, the compaction also quantizes A and sets *done; token-wise into sX,
-// or micro-scaled into the block scales Xs when Xs is set.
-struct RowQuant {
-  uint8_t* Xq;
-  int64_t ldq;
-  float* sX;
-  bool* done;
-  uint8_t* Xs;
+// The select's workspace: state, then the histogram words (hist_words), the
+// row-group totals and the row counts.
+template <class In>
+struct SelWork {
+  SelState* st;
+  uint32_t *hist, *gsum, *cnt;
+  explicit SelWork(void* ws) {
+    st = static_cast<SelState*>(ws);
+    hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 256);
+    gsum = hist + hist_words<In>();
+    cnt = gsum + kMaxRowGroups;
+  }
 };
 
-template <class In, bool kFast, int CH, bool kPick>
-void launch_rows(const typename In::T* A, int64_t M, int64_t K, int64_t lda, SelState* st,
-                 const uint32_t* fine, float* tau, uint32_t* gsum, uint32_t* cnt,
-                 int64_t capacity, int32_t* row, int32_t* col, float* val, int32_t* row_ptr,
-                 const RowQuant& rq, hipStream_t stream) {
-  const int64_t rpw = rows_per_wave(M);
-  const dim3 g(static_cast<unsigned>(row_groups(M)));
-  count_rows_kernel<In, kFast, CH, kPick><<<g, kRowWaves * kWave, 0, stream>>>(
-      A, M, K, lda, rpw, st, fine, tau, cnt, gsum);
-  if constexpr (In::kBytes == 2 && kFast) {
-    // padded row length within one slab of 16 chunks per lane
-    if (rq.Xq != nullptr && rq.ldq * 2 <= int64_t(kWave) * 16 * 8) {
-      const uint16_t* A16 = reinterpret_cast<const uint16_t*>(A);
-      switch (chunks_per_lane(rq.ldq * 2, 16)) {
-#define FP4LIN_CQ(CQ)                                                                            \
-  case CQ:                                                                                       \
-    if (rq.Xs != nullptr)                                                                        \
-      compact_quantize_rows_kernel<CQ, true><<<g, kRowWaves * kWave, 0, stream>>>(               \
-          A16, M, K, lda, rpw, st, tau, cnt, gsum, capacity, row_ptr, row, col, val, rq.Xq,      \
-          rq.ldq, rq.sX, rq.Xs);                                                                 \
-    else                                                                                         \
-      compact_quantize_rows_kernel<CQ><<<g, kRowWaves * kWave, 0, stream>>>(                     \
-          A16, M, K, lda, rpw, st, tau, cnt, gsum, capacity, row_ptr, row, col, val, rq.Xq,      \
-          rq.ldq, rq.sX, nullptr);                                                               \
-    *rq.done = true;                                                                             \
-    return;
-        FP4LIN_CQ(1)
-        FP4LIN_CQ(2)
-        FP4LIN_CQ(4)
-        FP4LIN_CQ(8)
-        FP4LIN_CQ(16)
-#undef FP4LIN_CQ
-        default:
-          break;
-      }
-    }
-  }
-  compact_rows_kernel<In, kFast, CH><<<g, kRowWaves * kWave, 0, stream>>>(
-      A, M, K, lda, rpw, st, tau, cnt, gsum, capacity, row_ptr, row, col, val);
-}
-
-template <class In, bool kFast, bool kPick>
-hipError_t rows_dispatch(const typename In::T* A, int64_t M, int64_t K, int64_t lda,
-                         SelState* st, const uint32_t* fine, float* tau, uint32_t* gsum,
-                         uint32_t* cnt, int64_t capacity, int32_t* row, int32_t* col, float* val,
-                         int32_t* row_ptr, const RowQuant& rq, hipStream_t stream) {
-  // rows up to 512 * CH columns in one slab (bfloat16: 8192, float32: 4096)
-  constexpr int kMaxCh = In::kBytes == 2 ? 16 : 8;
-  switch (chunks_per_lane(K, kMaxCh)) {
-#define FP4LIN_ROWS(CH)                                                                          \
-  case CH:                                                                                       \
-    launch_rows<In, kFast, CH, kPick>(A, M, K, lda, st, fine, tau, gsum, cnt, capacity, row,    \
-                                      col, val, row_ptr, rq, stream);                            \
-    return hipSuccess;
-    FP4LIN_ROWS(1)
-    FP4LIN_ROWS(2)
-    FP4LIN_ROWS(4)
-    FP4LIN_ROWS(8)
-#undef FP4LIN_ROWS
-    case 16:
-      if constexpr (kMaxCh >= 16) {
-        launch_rows<In, kFast, 16, kPick>(A, M, K, lda, st, fine, tau, gsum, cnt, capacity, row,
-                                          col, val, row_ptr, rq, stream);
-        return hipSuccess;
-      }
-      return hipErrorInvalidValue;
-    default:
-      return hipErrorInvalidValue;
-  }
-}
-
-// The bfloat16 select's workspace: state, then the coarse partial rows, the
-// fine histogram, the saved windows, the row-group totals and the row counts.
+// The bfloat16 histogram words: the coarse partial rows, the fine histogram,
+// the saved windows.
 struct H16Work {
   SelState* st;
-  uint32_t *part, *fine, *win, *fwin, *gsum, *cnt;
-  explicit H16Work(void* ws) {
-    st = static_cast<SelState*>(ws);
-    part = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 256);
+  uint32_t *part, *fine, *win, *fwin;
+  explicit H16Work(const SelWork<BF16In>& s) {
+    st = s.st;
+    part = s.hist;
     fine = part + size_t(kMaxH16Groups) * kCoarseBins;
     win = fine + kFineBins;
     fwin = win + kMaxH16Groups;
-    gsum = part + hist_words<BF16In>();
-    cnt = gsum + kMaxRowGroups;
   }
 };
 
@@ -931,45 +1045,121 @@ hipError_t launch_hist16(const uint16_t* A, int64_t M, int64_t K, int64_t lda, i
   }
 }
 
+// The three float32 digit passes (the set-up also clears nclear words at
+// clear); the last pick writes tau and its key.
+template <bool kFast>
+void launch_hist32(const float* A, int64_t M, int64_t K, int64_t lda, int64_t k,
+                   const SelWork<F32In>& w, float* tau, uint32_t* clear, int64_t nclear,
+                   hipStream_t stream) {
+  select_init_kernel<<<1, 256, 0, stream>>>(w.st, w.hist, int64_t(hist_words<F32In>()), k, clear,
+                                            nclear);
+  // Enough workgroups to fill the chip, each with several slabs so that the
+  // per-group histogram merge stays small.
+  const int64_t slab = int64_t(kHistThreads) * kHistCh * 8;
+  const int64_t slabs = M * ((K + slab - 1) / slab);
+  const int64_t g = slabs < 1024 ? slabs : 1024;
+  for (int p = 0; p < F32Digits::kPasses; ++p) {
+    const int shift = F32Digits::shift(p);
+    const int width = F32Digits::width(p);
+    const int hi = shift + width;
+    select_hist_kernel<F32In, kFast><<<dim3(unsigned(g)), kHistThreads, 0, stream>>>(
+        A, M, K, lda, w.st, shift, width, hi >= F32Digits::kKeyBits ? 32 : hi,
+        w.hist + size_t(p) * kHistBins);
+    select_pick_kernel<<<1, 256, 0, stream>>>(w.st, w.hist + size_t(p) * kHistBins, width,
+                                               p == F32Digits::kPasses - 1 ? 1 : 0, 0, tau);
+  }
+}
+
 template <class In, bool kFast>
 hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t k, float* tau,
                       int64_t capacity, int32_t* row, int32_t* col, float* val,
-                      int32_t* row_ptr, void* ws, const RowQuant& rq, hipStream_t stream) {
+                      int32_t* row_ptr, void* ws, hipStream_t stream) {
   using T = typename In::T;
   const T* A = static_cast<const T*>(Ap);
-  SelState* st = static_cast<SelState*>(ws);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 256);
-  uint32_t* gsum = hist + hist_words<In>();
-  uint32_t* cnt = gsum + kMaxRowGroups;
-  hipError_t e = hipSuccess;
+  const SelWork<In> w(ws);
+  const uint32_t* fine = nullptr;
   if constexpr (In::kBytes == 2) {
-    const H16Work w(ws);
-    e = launch_hist16<kFast>(A, M, K, lda, k, w, nullptr, 0, stream);
+    const H16Work h(w);
+    const hipError_t e = launch_hist16<kFast>(A, M, K, lda, k, h, nullptr, 0, stream);
     if (e != hipSuccess) return e;
-    e = rows_dispatch<In, kFast, true>(A, M, K, lda, st, w.fine, tau, gsum, cnt, capacity, row,
-                                       col, val, row_ptr, rq, stream);
+    fine = h.fine;
   } else {
-    select_init_kernel<<<1, 256, 0, stream>>>(st, hist, int64_t(hist_words<In>()), k);
-    // Enough workgroups to fill the chip, each with several slabs so that the
-    // per-group histogram merge stays small.
-    const int64_t slab = int64_t(kHistThreads) * kHistCh * 8;
-    const int64_t slabs = M * ((K + slab - 1) / slab);
-    const int64_t g = slabs < 1024 ? slabs : 1024;
-    for (int p = 0; p < F32Digits::kPasses; ++p) {
-      const int shift = F32Digits::shift(p);
-      const int width = F32Digits::width(p);
-      const int hi = shift + width;
-      select_hist_kernel<In, kFast><<<dim3(unsigned(g)), kHistThreads, 0, stream>>>(
-          A, M, K, lda, st, shift, width, hi >= F32Digits::kKeyBits ? 32 : hi,
-          hist + size_t(p) * kHistBins);
-      select_pick_kernel<<<1, 256, 0, stream>>>(st, hist + size_t(p) * kHistBins, width,
-                                                 p == F32Digits::kPasses - 1 ? 1 : 0, 0, tau);
-    }
-    e = rows_dispatch<In, kFast, false>(A, M, K, lda, st, nullptr, tau, gsum, cnt, capacity, row,
-                                        col, val, row_ptr, rq, stream);
+    launch_hist32<kFast>(A, M, K, lda, k, w, tau, nullptr, 0, stream);
   }
-  if (e != hipSuccess) return e;
+  const int64_t rpw = rows_per_wave(M);
+  const dim3 g(static_cast<unsigned>(row_groups(M)));
+  count_rows_kernel<In, kFast, In::kBytes == 2><<<g, kRowWaves * kWave, 0, stream>>>(
+      A, M, K, lda, rpw, w.st, fine, tau, w.cnt, w.gsum);
+  compact_rows_kernel<In, kFast><<<g, kRowWaves * kWave, 0, stream>>>(
+      A, M, K, lda, rpw, w.st, tau, w.cnt, w.gsum, capacity, row_ptr, row, col, val);
   return hipGetLastError();
+}
+
+bool rows_fast(const void* A, int esz, int64_t K, int64_t lda) {
+  return (reinterpret_cast<uintptr_t>(A) % 16 == 0) && ((lda * esz) % 16 == 0) && (K % 8 == 0);
+}
+
+// Histograms, then the row count with W's first pass, then the compaction
+// (with the quantization of A) with W's codes.
+template <class In, bool kFast, bool kWAligned, bool kMx>
+hipError_t forward_front(const FrontArgs& f, hipStream_t stream) {
+  using T = typename In::T;
+  const T* A = static_cast<const T*>(f.A);
+  const SelWork<In> w(f.ws);
+  uint32_t* clear = kMx ? nullptr : f.colmax;
+  const int64_t nclear = kMx ? 0 : f.N;
+  const uint32_t* fine = nullptr;
+  if constexpr (In::kBytes == 2) {
+    const H16Work h(w);
+    const hipError_t e = launch_hist16<kFast>(A, f.M, f.K, f.lda, f.k, h, clear, nclear, stream);
+    if (e != hipSuccess) return e;
+    fine = h.fine;
+  } else {
+    launch_hist32<kFast>(A, f.M, f.K, f.lda, f.k, w, f.tau, clear, nclear, stream);
+  }
+  const int64_t rpw = rows_per_wave(f.M);
+  const int64_t na = row_groups(f.M);
+  const int64_t Kp = f.ldq * 2;
+  WPass wp{f.W, f.K, f.N, f.ldw, f.colmax, f.Wq, f.ldq, f.sW, 0, 0};
+  // pass 1: column maxima on 512-column strips x 64-row splits, or the
+  // micro-scaled codes on 128 x 128 tiles
+  if constexpr (kMx) {
+    wp.gx = (f.N + kMxTN - 1) / kMxTN;
+    wp.nb = wp.gx * (Kp / kMxTK);
+  } else {
+    wp.gx = (f.N + kColStrip - 1) / kColStrip;
+    wp.nb = wp.gx * ((f.K + kColRows - 1) / kColRows);
+  }
+  count_wpass_kernel<In, kFast, kWAligned, kMx>
+      <<<dim3(unsigned(na + wp.nb)), kRowWaves * kWave, 0, stream>>>(
+          A, f.M, f.K, f.lda, rpw, w.st, fine, f.tau, w.cnt, w.gsum, static_cast<float*>(f.sA),
+          na, wp);
+  // pass 2: the token-wise codes on 128 x 128 tiles (micro-scaled: none)
+  if constexpr (kMx) {
+    wp.gx = 0;
+    wp.nb = 0;
+  } else {
+    wp.gx = (f.N + kTN - 1) / kTN;
+    wp.nb = wp.gx * (Kp / kTK);
+  }
+  compact_wpass_kernel<In, kFast, kWAligned, kMx>
+      <<<dim3(unsigned(na + wp.nb)), kRowWaves * kWave, 0, stream>>>(
+          A, f.M, f.K, f.lda, rpw, w.st, f.tau, w.cnt, w.gsum, f.capacity, f.row_ptr, f.row,
+          f.col, f.val, f.Aq, f.ldq, kMx ? nullptr : static_cast<float*>(f.sA),
+          kMx ? static_cast<uint8_t*>(f.sA) : nullptr, na, wp);
+  return hipGetLastError();
+}
+
+template <class In, bool kMx>
+hipError_t forward_front_dispatch(const FrontArgs& f, hipStream_t stream) {
+  const bool fast = rows_fast(f.A, In::kBytes, f.K, f.lda);
+  const bool w_aligned = (reinterpret_cast<uintptr_t>(f.W) % 16 == 0) &&
+                         ((f.ldw * In::kBytes) % 16 == 0);
+  if (fast)
+    return w_aligned ? forward_front<In, true, true, kMx>(f, stream)
+                     : forward_front<In, true, false, kMx>(f, stream);
+  return w_aligned ? forward_front<In, false, true, kMx>(f, stream)
+                   : forward_front<In, false, false, kMx>(f, stream);
 }
 
 }  // namespace
@@ -983,102 +1173,25 @@ size_t select_workspace_bytes(bool bf16, int64_t M) {
 hipError_t launch_outlier_select(const void* A, bool bf16, int64_t M, int64_t K, int64_t lda,
                                  int64_t k, float* tau, int64_t capacity, int32_t* row,
                                  int32_t* col, float* val, int32_t* row_ptr, void* ws,
-                                 hipStream_t stream, uint8_t* Xq, int64_t ldq, float* sX,
-                                 bool* quantized, uint8_t* Xs) {
-  bool done = false;
-  const RowQuant rq{quantized != nullptr ? Xq : nullptr, ldq, sX, &done, Xs};
-  const int esz = bf16 ? 2 : 4;
-  const bool fast = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && ((lda * esz) % 16 == 0) &&
-                    (K % 8 == 0);
-  hipError_t e;
+                                 hipStream_t stream) {
+  const bool fast = rows_fast(A, bf16 ? 2 : 4, K, lda);
   if (bf16)
-    e = fast ? run_select<BF16In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, rq, stream)
-             : run_select<BF16In, false>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, rq, stream);
-  else
-    e = fast ? run_select<F32In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, rq, stream)
-             : run_select<F32In, false>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, rq, stream);
-  if (quantized != nullptr) *quantized = done && e == hipSuccess;
-  return e;
+    return fast ? run_select<BF16In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr,
+                                           ws, stream)
+                : run_select<BF16In, false>(A, M, K, lda, k, tau, capacity, row, col, val,
+                                            row_ptr, ws, stream);
+  return fast ? run_select<F32In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr,
+                                        ws, stream)
+              : run_select<F32In, false>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr,
+                                         ws, stream);
 }
 
-namespace {
-
-template <int CH>
-hipError_t forward_front(const uint16_t* A, int64_t M, int64_t K, int64_t lda, int64_t k,
-                         float* tau, int64_t capacity, int32_t* row, int32_t* col, float* val,
-                         int32_t* row_ptr, void* ws, uint8_t* Aq, int64_t ldq, float* sA,
-                         const ColQuantArgs& cq, bool* w_done, hipStream_t stream) {
-  const H16Work w(ws);
-  hipError_t e = launch_hist16<true>(A, M, K, lda, k, w, cq.colmax, cq.N, stream);
-  if (e != hipSuccess) return e;
-  const int64_t rpw = rows_per_wave(M);
-  const int64_t na = row_groups(M);
-  if constexpr (CH > 8) {
-    // the 16-chunk row kernels need up to 162 VGPRs (three waves per SIMD),
-    // which would hold the paired column passes to the same occupancy (measured
-    // slower): the row kernels run alone and W is quantized afterwards
-    count_rows_kernel<BF16In, true, CH, true><<<dim3(unsigned(na)), kRowWaves * kWave, 0,
-                                                stream>>>(A, M, K, lda, rpw, w.st, w.fine, tau,
-                                                          w.cnt, w.gsum);
-    compact_quantize_rows_kernel<CH><<<dim3(unsigned(na)), kRowWaves * kWave, 0, stream>>>(
-        A, M, K, lda, rpw, w.st, tau, w.cnt, w.gsum, capacity, row_ptr, row, col, val, Aq, ldq,
-        sA, nullptr);
-    *w_done = false;
-    return hipGetLastError();
-  } else {
-    // column maxima: 512-column strips x 64-row splits
-    const int64_t gx1 = (cq.N + kColStrip - 1) / kColStrip;
-    const int64_t nb1 = gx1 * ((cq.K + kColRows - 1) / kColRows);
-    count_colmax_kernel<CH><<<dim3(unsigned(na + nb1)), kRowWaves * kWave, 0, stream>>>(
-        A, M, K, lda, rpw, w.st, w.fine, tau, w.cnt, w.gsum, na, cq, gx1, nb1);
-    // codes: 128-column x 128-row tiles
-    const int64_t gx2 = (cq.N + kTN - 1) / kTN;
-    const int64_t nb2 = gx2 * ((cq.ldq * 2) / kTK);
-    compact_qcols_kernel<CH><<<dim3(unsigned(na + nb2)), kRowWaves * kWave, 0, stream>>>(
-        A, M, K, lda, rpw, w.st, tau, w.cnt, w.gsum, capacity, row_ptr, row, col, val, Aq, ldq,
-        sA, na, cq, gx2, nb2);
-    *w_done = true;
-    return hipGetLastError();
-  }
-}
-
-}  // namespace
-
-bool forward_front_supported(const void* A, const void* W, bool bf16, int64_t K, int64_t lda,
-                             int64_t ldw) {
-  const bool a_fast = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && ((lda * 2) % 16 == 0) &&
-                      (K % 8 == 0);
-  const bool w_aligned = (reinterpret_cast<uintptr_t>(W) % 16 == 0) && ((ldw * 2) % 16 == 0);
-  // the padded row fits one slab of 16 chunks per lane
-  const int64_t kp = (K + 127) / 128 * 128;
-  return bf16 && a_fast && w_aligned && kp <= int64_t(kWave) * 16 * 8;
-}
-
-hipError_t launch_forward_front(const void* A, int64_t M, int64_t K, int64_t lda, int64_t k,
-                                float* tau, int64_t capacity, int32_t* row, int32_t* col,
-                                float* val, int32_t* row_ptr, void* ws, uint8_t* Aq, int64_t ldq,
-                                float* sA, const void* W, int64_t N, int64_t ldw, uint8_t* Wq,
-                                float* sW, uint32_t* colmax, bool* w_done, hipStream_t stream) {
-  const uint16_t* A16 = static_cast<const uint16_t*>(A);
-  const ColQuantArgs cq{static_cast<const uint16_t*>(W), K, N, ldw, colmax, Wq, ldq, sW};
-  // the padded row length (a multiple of 128) needs no more chunks than K:
-  // 512 * CH is a multiple of 128
-  const int ch = chunks_per_lane(K, 16);
-  if (chunks_per_lane(ldq * 2, 16) != ch) return hipErrorInvalidValue;
-  switch (ch) {
-#define FP4LIN_FF(CH)                                                                            \
-  case CH:                                                                                       \
-    return forward_front<CH>(A16, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws, Aq,   \
-                             ldq, sA, cq, w_done, stream);
-    FP4LIN_FF(1)
-    FP4LIN_FF(2)
-    FP4LIN_FF(4)
-    FP4LIN_FF(8)
-    FP4LIN_FF(16)
-#undef FP4LIN_FF
-    default:
-      return hipErrorInvalidValue;
-  }
+hipError_t launch_forward_front(const FrontArgs& f, hipStream_t stream) {
+  if (f.bf16)
+    return f.mx ? forward_front_dispatch<BF16In, true>(f, stream)
+                : forward_front_dispatch<BF16In, false>(f, stream);
+  return f.mx ? forward_front_dispatch<F32In, true>(f, stream)
+              : forward_front_dispatch<F32In, false>(f, stream);
 }
 
 }  // namespace fp4lin

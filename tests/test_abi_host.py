@@ -190,8 +190,11 @@ def test_quantize_weight_errors():
     assert quant_w(Wq=MISALIGNED) == _lib.ERR_ALIGN
     assert quant_w(ws=MISALIGNED) == _lib.ERR_ALIGN
     assert quant_w(wsb=4) == _lib.ERR_WORKSPACE
-    # tiles of 128 codes along K index the second grid dimension (at most 65535)
+    # K up to 65535 tiles of 128 codes (the micro-scaled quantizer's grid
+    # dimension, the same limit for both formats)
     assert quant_w(K=65535 * 128 + 1, N=1, ldw=1) == _lib.ERR_SHAPE
+    # the column passes' one-dimensional grids hold fewer than 2^32 workgroups
+    assert quant_w(K=1 << 22, N=1 << 30, ldw=1 << 30) == _lib.ERR_SHAPE
 
 
 def gemm(Aq=FAKE, sA=FAKE, Bq=FAKE, sB=FAKE, M=4, N=4, K=8, dA=None, W=None, wdt=1, ldw=4,
@@ -205,7 +208,7 @@ def test_gemm_errors():
     assert gemm(sB=None) == _lib.ERR_NULL
     assert gemm(Y=None) == _lib.ERR_NULL
     assert gemm(dA=coo(10), W=None) == _lib.ERR_NULL
-    for fld in ("row", "col", "val", "row_ptr"):
+    for fld in ("col", "val", "row_ptr"):
         assert gemm(dA=coo(10, null=fld), W=FAKE) == _lib.ERR_NULL
     assert gemm(dA=coo(10), W=FAKE, wdt=3) == _lib.ERR_DTYPE
     assert gemm(dA=coo(10), W=FAKE, ldw=3) == _lib.ERR_SHAPE

@@ -355,27 +355,30 @@ def forward_mx_views(ql, ws, M, K, N, dt, q):
     return o, tau, rp, Aq, As, Wq, Ws
 
 
+# ld: None (dense rows), "pad" (aligned rows, lda != K), "odd" (A and W rows
+# not 16-byte aligned). The K cover every slab pattern of the row kernels.
 FWD_MX_CASES = [(dt, ld, M, K, N)
                 for (M, K, N) in [(37, 1000, 300), (300, 4096, 520), (70, 8192, 129),
-                                  (33, 8200, 64)]
-                for (dt, ld) in [(wl.BF16, None), (wl.BF16, 4104), (wl.F32, None)]
-                if ld is None or ld >= K]
+                                  (33, 8200, 64), (24, 13824, 72), (20, 3584, 40)]
+                for (dt, ld) in [(wl.BF16, None), (wl.BF16, "pad"), (wl.BF16, "odd"),
+                                 (wl.F32, None)]]
 
 
 @pytest.mark.parametrize("dtype,ld,M,K,N", FWD_MX_CASES)
 def test_forward_mx_matches_stage_calls(ql, dtype, ld, M, K, N):
     """Every intermediate and Y of fp4lin_forward_mx are bit-identical to the
-    separate calls (the fused compaction + block quantization for aligned bf16
-    rows up to 8192 columns, the separate quantizer otherwise), and Y matches
-    the oracle."""
+    separate calls (the forward's compaction block-quantizes A, and W's pass
+    shares the row count's launch), and Y matches the oracle."""
     log(f"forward_mx {dtype} ld={ld} {M}x{K}x{N}")
     t = torch()
     rng = np.random.default_rng(M + K + N)
     A = wl.random_matrix(rng, M, K, dtype, dist="t3")
     W = wl.random_matrix(rng, K, N, dtype, scale=0.02)
     Ad, Wd = to_device(A), to_device(W)
-    if ld is not None:
-        Ad = padded(Ad, ld)
+    if ld == "pad":
+        Ad = padded(Ad, (K + 7) // 8 * 8 + 8)
+    elif ld == "odd":
+        Ad, Wd = padded(Ad, K + 1), padded(Wd, N + 1)
     q = 0.98
     Y, ws = ql.forward_mx(Ad, Wd, q, return_workspace=True)
     tau, coo = ql.outlier_select(Ad, q)

@@ -212,6 +212,18 @@ def test_quantize_weight_bf16_full_groups(ql, K, N):
     check_quantize_weight(ql, wl.random_matrix(rng, K, N, wl.BF16, scale=0.02))
 
 
+def test_quantize_weight_long_k(ql):
+    """K above 65535 splits of 64 rows (the column-max pass's tiles along K):
+    the column passes run on one-dimensional grids, so every split is
+    launched; each column's largest magnitude sits in the last split."""
+    K, N = 65535 * 64 + 100, 8
+    log(f"quantize_weight bf16 {K}x{N}")
+    rng = np.random.default_rng(17)
+    w = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    w[K - 1 - np.arange(N), np.arange(N)] = np.float32(0.75) * (1 + np.arange(N))
+    check_quantize_weight(ql, wl.from_f32(w, wl.BF16))
+
+
 def test_quantize_weight_bf16_special_columns(ql):
     """Zero, negative-zero, subnormal and one-value columns inside a tile that
     also holds ordinary columns (the tile then takes the generic encoder)."""
@@ -487,11 +499,13 @@ def workspace_views(ql, ws, M, K, N, dtype_code, q):
         Wq=take(o.Wq, N * ldq, np.uint8).reshape(N, ldq), sW=take(o.sW, N, np.float32))
 
 
-def check_forward(ql, L: wl.Layer, rows=None, lda=None):
+def check_forward(ql, L: wl.Layer, rows=None, lda=None, ldw=None):
     t = torch()
     A, W = to_device(L.A), to_device(L.W)
     if lda is not None:
         A = padded(A, lda)
+    if ldw is not None:
+        W = padded(W, ldw)
     Y, ws = ql.forward(A, W, L.q, return_workspace=True)
     t.cuda.synchronize()
     ops = O.forward_operands(L.A.f32, L.W.f32, L.q)
@@ -532,23 +546,30 @@ def test_forward_small(ql, dtype, M, K, N, q):
     check_forward(ql, L)
 
 
-# bfloat16 rows inside fp4lin_forward: 16-byte aligned rows of up to 8192
-# columns are compacted and quantized by one kernel, the others by the separate
-# select and quantize_act kernels.
-@pytest.mark.parametrize("M,K,N,lda", [
-    (24, 8192, 64, None),   # 16 chunks per lane, one slab: one kernel
-    (20, 8200, 72, None),   # two slabs: separate kernels
-    (40, 300, 80, 301),     # rows not 16-byte aligned: separate kernels
-    (40, 304, 80, 312),     # aligned rows with lda != K: one kernel
-    (9, 1024, 24, None),    # fewer rows than one workgroup of each select kernel
+# Rows inside fp4lin_forward stream through in slabs of 8, 4, 2 and 1 chunks
+# of 8 elements per lane (4096, 2048, 1024 and 512 columns), with a last
+# 1-chunk slab over a ragged end; rows that are not 16-byte aligned (or
+# K % 8 != 0) are read element by element, and so are W's rows when W is not
+# 16-byte aligned.
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("M,K,N,lda,ldw", [
+    (24, 8192, 64, None, None),   # two 8-chunk slabs
+    (20, 8200, 72, None, None),   # two 8-chunk slabs and a ragged end
+    (12, 13824, 40, None, None),  # 3 x 8, then 2 and 1 chunks
+    (16, 3584, 48, None, None),   # 4, 2 and 1 chunks
+    (40, 300, 80, 301, None),     # rows not 16-byte aligned
+    (40, 304, 80, 312, None),     # aligned rows with lda != K
+    (30, 1000, 70, None, 73),     # W rows not 16-byte aligned
+    (9, 1024, 24, None, None),    # fewer rows than one workgroup of each select kernel
+    (5, 7, 9, None, None),        # a ragged end only
 ])
-def test_forward_bf16_row_paths(ql, M, K, N, lda):
-    log(f"forward bf16 row paths {M}x{K}x{N} lda={lda}")
+def test_forward_row_paths(ql, dtype, M, K, N, lda, ldw):
+    log(f"forward row paths {dtype} {M}x{K}x{N} lda={lda} ldw={ldw}")
     rng = np.random.default_rng(M * 31 + K + N)
     a = wl.draw_activation(rng, M, K, "t3", max(1, K // 200), 50.0)
     w = wl.draw_weight(rng, K, N)
-    L = wl.Layer("bf16-rows", wl.from_f32(a, wl.BF16), wl.from_f32(w, wl.BF16), 0.99)
-    check_forward(ql, L, lda=lda)
+    L = wl.Layer("rows", wl.from_f32(a, dtype), wl.from_f32(w, dtype), 0.99)
+    check_forward(ql, L, lda=lda, ldw=ldw)
 
 
 def test_forward_q_one_is_plain_quantized_gemm(ql):
@@ -567,11 +588,28 @@ def test_forward_q_one_is_plain_quantized_gemm(ql):
     assert np.array_equal(host(Y).astype(np.float64), A.astype(np.float64) @ W.astype(np.float64))
 
 
-def test_forward_matches_stage_calls(ql):
-    """fp4lin_forward == the four public calls in order (same bits)."""
+@pytest.mark.parametrize("case", ["llama1.3b", "k13824", "f32", "unaligned"])
+def test_forward_matches_stage_calls(ql, case):
+    """fp4lin_forward == the four public calls in order (same bits): the
+    forward's count, compaction and quantization of A and its paired passes
+    over W against the separate select and quantizer kernels."""
+    log(f"forward vs stage calls {case}")
     t = torch()
-    L = wl.make_layer("llama1.3b_ffn_up", M=256)
+    lda = ldw = None
+    if case == "llama1.3b":
+        L = wl.make_layer("llama1.3b_ffn_up", M=256)
+    else:
+        M, K, N, dtype = {"k13824": (48, 13824, 160, wl.BF16), "f32": (64, 5120, 136, wl.F32),
+                          "unaligned": (40, 2000, 90, wl.BF16)}[case]
+        rng = np.random.default_rng(K + N)
+        a = wl.draw_activation(rng, M, K, "t3", max(1, K // 200), 50.0)
+        w = wl.draw_weight(rng, K, N)
+        L = wl.Layer(case, wl.from_f32(a, dtype), wl.from_f32(w, dtype), 0.999)
+        if case == "unaligned":
+            lda, ldw = K + 1, N + 3
     A, W = to_device(L.A), to_device(L.W)
+    if lda is not None:
+        A, W = padded(A, lda), padded(W, ldw)
     Y1, ws = ql.forward(A, W, L.q, return_workspace=True)
     tau, coo = ql.outlier_select(A, L.q)
     Aq, sA = ql.quantize_act(A, tau)
@@ -579,9 +617,7 @@ def test_forward_matches_stage_calls(ql):
     Y2 = ql.gemm(Aq, sA, Wq, sW, L.M, L.N, L.K, coo, W)
     t.cuda.synchronize()
     assert np.array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
-    # the forward compacts and quantizes A in one kernel; the separate calls
-    # must give the same intermediates
-    v = workspace_views(ql, ws, L.M, L.K, L.N, 1, L.q)
+    v = workspace_views(ql, ws, L.M, L.K, L.N, 1 if L.A.dtype == wl.BF16 else 0, L.q)
     nnz = v["nnz"]
     assert_bits_equal(v["tau"], host(tau)[0], "tau")
     assert_bits_equal(v["row_ptr"], host(coo.row_ptr), "row_ptr")
@@ -590,6 +626,8 @@ def test_forward_matches_stage_calls(ql):
     assert_bits_equal(v["val"], host(coo.val)[:nnz], "coo val")
     assert_bits_equal(v["Aq"], host(Aq), "Aq")
     assert_bits_equal(v["sA"], host(sA), "sA")
+    assert_bits_equal(v["Wq"], host(Wq), "Wq")
+    assert_bits_equal(v["sW"], host(sW), "sW")
 
 
 # ---------------------------------------------------------------------------
