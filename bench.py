@@ -74,7 +74,7 @@ def parse():
 
 # the GEMM runs the compensation in its epilogue up to this many COO entries
 # per row of A (the COO capacity bounds them), else as a second kernel
-FUSED_MAX_PER_ROW = 16
+FUSED_MAX_PER_ROW = 10
 
 
 def forward_rate(L, dev, steps, warmup):

@@ -33,16 +33,19 @@
 //
 // Layout and schedule:
 //  * A is M x ldq bytes and B is N x ldq bytes, K-contiguous packed rows.
-//  * A workgroup of 4 waves (2 x 2 grid, each wave 64 x 128 outputs) owns a
-//    128 x 256 output tile and walks K in 128-code (64-byte) steps through
-//    three LDS stages of 24 KiB. Operand tiles go from global memory straight
+//  * A workgroup of 8 waves (4 x 2 grid, each wave 64 x 128 outputs) owns a
+//    256 x 256 output tile and walks K in 128-code (64-byte) steps through
+//    three LDS stages of 32 KiB. Operand tiles go from global memory straight
 //    into LDS (buffer loads with an LDS destination, no register staging),
 //    issued three steps ahead into the stage the previous step finished.
 //    Each step issues its first 64-code sub-step of MFMAs, then waits for its
 //    own loads of the next stage and meets the other waves at the barrier
 //    while the matrix core works through the queued MFMAs, then issues the
 //    next loads, the second sub-step of MFMAs and the next step's first
-//    fragment reads. Two workgroups share a CU.
+//    fragment reads. One workgroup per CU, two waves per SIMD. (Against
+//    128 x 256 tiles with two 4-wave workgroups per CU, each wave moves 4
+//    instead of 6 KiB of operands per step for the same 16 MFMAs: 3-13%
+//    faster on the LLaMA shapes.)
 //  * Each 16-byte chunk of a staged row is stored at a chunk index XOR-ed with
 //    row bits, so that the lanes reading one chunk column of consecutive rows
 //    hit distinct banks.
@@ -61,8 +64,8 @@
 //    instructions than storing from the MFMA layout). The stores are
 //    non-temporal: the output stream is not kept in L2 at the expense of the
 //    operand tiles that concurrent workgroups re-read.
-//  * With the compensation, the tile leaves in four chunks of 32 rows x all
-//    256 columns (each wave row's 16 x 256 block in its own stage buffer).
+//  * With the compensation, the tile leaves in four chunks of 64 rows x all
+//    256 columns (each wave row's 16 x 256 block in half a stage buffer).
 //    After a barrier each wave finishes 8 whole rows of a chunk: a lane owns 4
 //    consecutive columns, so a non-zero costs one 8-byte (bf16 W) or 16-byte
 //    (fp32 W) gather per lane, addressed with the W row offset in the scalar
@@ -70,8 +73,7 @@
 //    loads. The non-zeros of a wave's 8 consecutive rows are one contiguous
 //    range of the row-major COO; they are gathered in groups of 8, two groups
 //    in flight, across row boundaries. Each row is stored once, 1 KiB per
-//    wave instruction. While one workgroup gathers, the other workgroup on the
-//    CU keeps the matrix core busy.
+//    wave instruction.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -232,10 +234,16 @@ __device__ inline void fma_wseg(float v, const WSeg<kBf16W>& w, float (&s)[4]) {
 }
 
 // Epilogue with the sparse compensation (see the header). The tile (BM x BN =
-// 128 x 256, four waves of 64 x 128) leaves in four chunks; chunk c holds the
-// rows wm * 64 + (c >> 1) * 32 + (c & 1) * 16 + [0, 16) of both wave rows wm,
-// all 256 columns, wave row wm's block in stage wm. Wave w then finishes the
-// 8 rows (w & 1) * 8 + [0, 8) of wave row w >> 1's block.
+// 256 x 256, eight waves of 64 x 128 in a 4 x 2 grid) leaves in four chunks;
+// chunk c holds the rows wm * 64 + (c >> 1) * 32 + (c & 1) * 16 + [0, 16) of
+// all four wave rows wm, all 256 columns: wave row wm's 16 x 256 block is
+// half (wm & 1) of stage wm >> 1 (with 128-row tiles of two wave rows, the
+// whole of stage wm). Wave w then finishes the 8 rows
+// (w & 1) * 8 + [0, 8) of wave row w >> 1's block. A block row is 256 floats
+// (two blocks fill a stage); the 32-float halves of its 128-byte groups swap
+// in rows with bit 2 set (lds_col), so that the lanes 32..63 of a staging
+// write, four rows below lanes 0..31, hit the other 32 banks, while a row
+// still reads back as 64 16-byte pieces.
 template <class C, bool kMx, bool kBf16W, bool kWVec>
 __device__ __attribute__((always_inline)) inline void fused_epilogue(
     v16f (&acc)[C::FM][C::FN], const float (&sa)[C::FM][16], const float (&sb)[C::FN],
@@ -243,10 +251,14 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
     float* __restrict__ Y, int64_t ldy, const CompArgs& cp, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col, const float* __restrict__ val) {
   constexpr int FM = C::FM, FN = C::FN, BN = C::BN;
-  static_assert(C::BM == 128 && BN == 256 && C::WM == 2 && C::WN == 2 && FM == 2 && FN == 4,
+  static_assert(C::BM == 64 * C::WM && (C::WM == 2 || C::WM == 4) && BN == 256 && C::WN == 2 &&
+                    FM == 2 && FN == 4,
                 "chunk layout of the fused epilogue");
-  constexpr int kPitch = BN + 8;  // floats; lanes 32..63 (4 rows down) hit the other 32 banks
-  static_assert(16 * kPitch * 4 <= C::kStageBytes, "a wave row's 16-row block fits one stage");
+  constexpr int kPitch = BN;  // floats
+  constexpr int kPerStage = C::WM / 2;  // 16-row blocks per stage buffer (wave rows / 2 stages)
+  static_assert(kPerStage * 16 * kPitch * 4 <= C::kStageBytes, "the blocks fit two stages");
+  // LDS column of column c in block row r
+  auto lds_col = [](int r, int c) { return c ^ (((r >> 2) & 1) << 5); };
   // non-zeros per gather group and groups in flight (the element-load path,
   // 4 loads per non-zero, keeps 8 x 2 within the vmcnt range)
   constexpr int G = kWVec ? 8 : 8;
@@ -262,9 +274,11 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
         for (int r = 0; r < 16; ++r)
           acc[fm][fn][r] = __fmul_rn(__fmul_rn(acc[fm][fn][r], sa[fm][r]), sb[fn]);
   }
-  float* const wblk = reinterpret_cast<float*>(wm == 0 ? st0 : st1);
+  float* const wblk =
+      reinterpret_cast<float*>(wm < kPerStage ? st0 : st1) + (wm % kPerStage) * 16 * kPitch;
   const int pr = wave >> 1, ph = wave & 1;
-  const float* const rblk = reinterpret_cast<const float*>(pr == 0 ? st0 : st1) + ph * 8 * kPitch;
+  const float* const rblk = reinterpret_cast<const float*>(pr < kPerStage ? st0 : st1) +
+                            (pr % kPerStage) * 16 * kPitch + ph * 8 * kPitch;
   const int c4 = 4 * lane;
   const int gc = n0 + c4;
   constexpr int esz = kBf16W ? 2 : 4;
@@ -392,7 +406,7 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
 #pragma unroll
         for (int u = 0; u < G; ++u) fma_wseg<kBf16W>(vq[d][u], wq[d][u], acc4);
         if (rq[d] >= 0) {
-          float* const p = rows + rq[d] * kPitch + c4;
+          float* const p = rows + rq[d] * kPitch + lds_col(rq[d], c4);
           f32x4 y = *reinterpret_cast<const f32x4*>(p);
           y[0] = __fadd_rn(y[0], acc4[0]);
           y[1] = __fadd_rn(y[1], acc4[1]);
@@ -419,7 +433,7 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int gr = g0 + i;
-      const f32x4 y = *reinterpret_cast<const f32x4*>(rows + i * kPitch + c4);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(rows + i * kPitch + lds_col(i, c4));
       if (gr < M) {
         float* dst = Y + int64_t(gr) * ldy + gc;
         if (y_full) {
@@ -443,7 +457,8 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
 #pragma unroll
       for (int rr = 0; rr < 8; ++rr) {
         const int rl = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-        wblk[rl * kPitch + wn * (FN * 32) + fn * 32 + (lane & 31)] = acc[fm][fn][h * 8 + rr];
+        wblk[rl * kPitch + lds_col(rl, wn * (FN * 32) + fn * 32 + (lane & 31))] =
+            acc[fm][fn][h * 8 + rr];
       }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -470,7 +485,7 @@ constexpr bool kFusedColumns = true;
 
 // Largest COO capacity per row of A for which the compensation runs in the
 // GEMM's epilogue (see run_gemm).
-constexpr int64_t kFusedMaxPerRow = 16;
+constexpr int64_t kFusedMaxPerRow = 10;
 
 // kComp: 0 no compensation; with it, 1 + (W is float32) + 2 * (W rows allow
 // 4-column vector gathers): 1 / 3 bfloat16 W, 2 / 4 float32 W.
@@ -786,37 +801,62 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
     }
 }
 
-using GemmTile = GemmCfg<128, 256, 2, 2, 64, 2>;
+// Tiles of the GEMM without compensation: 256 x 256 (eight waves, one
+// workgroup per CU) once the grid fills the 256 CUs twice, 128 x 256 (four
+// waves, two workgroups per CU) below that, where finer tiles balance better
+// (LLaMA 1.3B up, 352 large tiles: 45.6 against 41.6 us).
+using GemmTile = GemmCfg<256, 256, 4, 2, 64, 1>;
+using GemmSmallTile = GemmCfg<128, 256, 2, 2, 64, 2>;
+constexpr int64_t kLargeTilesMin = 512;
+// Tile of the GEMM with the compensation in its epilogue: the two workgroups
+// on a CU keep the matrix core busy in turn while either one gathers (13B up:
+// 509 against 521 us with 256 x 256 tiles).
+using GemmFusedTile = GemmCfg<128, 256, 2, 2, 64, 2>;
+
+template <class C, bool kMx>
+hipError_t launch_plain(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const float* sB,
+                        const uint8_t* As, const uint8_t* Bs, int64_t M, int64_t N, int64_t ldq,
+                        float* Y, int64_t ldy, hipStream_t stream) {
+  const int tiles_m = int((M + C::BM - 1) / C::BM);
+  const int tiles_n = int((N + C::BN - 1) / C::BN);
+  fp4_gemm_kernel<C, kMx, 0><<<dim3(unsigned(tiles_m * tiles_n)), C::kThreads, 0, stream>>>(
+      Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs, CompArgs{nullptr, 0, 0, 0},
+      nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
 
 template <bool kMx>
 hipError_t run_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const float* sB,
                     const uint8_t* As, const uint8_t* Bs, int64_t M, int64_t N, int64_t ldq,
                     const SparseArgs& sp, float* Y, int64_t ldy, hipStream_t stream) {
-  using C = GemmTile;
   // K steps are whole 64-byte chunks of the packed rows (the packed row length
   // is a multiple of 64 bytes), so no step reads past a row.
-  if (ldq % C::BKB != 0) return hipErrorInvalidValue;
-  const int tiles_m = int((M + C::BM - 1) / C::BM);
-  const int tiles_n = int((N + C::BN - 1) / C::BN);
-  const dim3 grid(unsigned(tiles_m * tiles_n));
-  CompArgs cp{nullptr, 0, 0, 0};
+  static_assert(GemmTile::BKB == 64 && GemmSmallTile::BKB == 64 && GemmFusedTile::BKB == 64,
+                "one K step per 64 bytes");
+  if (ldq % 64 != 0) return hipErrorInvalidValue;
   // The two schedules of the compensation give the same bits. The fused
   // epilogue saves the read-modify-write of Y (8 bytes per output), but its
   // gathers run in the GEMM's waves (two per SIMD), which hide memory latency
-  // worse than the separate kernel's eight; measured on the LLaMA-shaped
-  // workloads it wins up to ~14 non-zeros per row and loses from ~20 (13B up
-  // 5.1/row: 543 against 656 us; 13B down 13.8/row: 446 against 492; 1.3B up
-  // 20/row: 156 against 111; 7B up 41/row: 797 against 732). The COO's
+  // worse than the separate kernel's eight, and it needs the 128 x 256 tile.
+  // Measured on the LLaMA-shaped workloads (GEMM with compensation, us,
+  // fused against the large-tile GEMM + separate kernel): 13B up 5.1/row 509
+  // against 305 + 214; 13B down 13.8/row 406 against 273 + 118; 1.3B up
+  // 20/row 172 against 45 + 74; 7B up 41/row 843 against 219 + 468. The COO's
   // capacity bounds the non-zeros (for the select's own COO it is M*K*(1-q)).
   const bool fused = sp.row_ptr != nullptr && sp.capacity <= kFusedMaxPerRow * M;
   if (!fused) {
-    fp4_gemm_kernel<C, kMx, 0><<<grid, C::kThreads, 0, stream>>>(
-        Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs, cp, nullptr, nullptr,
-        nullptr);
-    const hipError_t e = hipGetLastError();
+    const int64_t large = ((M + GemmTile::BM - 1) / GemmTile::BM) * ((N + GemmTile::BN - 1) / GemmTile::BN);
+    const hipError_t e =
+        large >= kLargeTilesMin
+            ? launch_plain<GemmTile, kMx>(Aq, sA, Bq, sB, As, Bs, M, N, ldq, Y, ldy, stream)
+            : launch_plain<GemmSmallTile, kMx>(Aq, sA, Bq, sB, As, Bs, M, N, ldq, Y, ldy, stream);
     if (e != hipSuccess || sp.row_ptr == nullptr) return e;
     return launch_sparse_add(sp, M, N, Y, ldy, stream);
   }
+  CompArgs cp{nullptr, 0, 0, 0};
+  using CF = GemmFusedTile;
+  const int tiles_mf = int((M + CF::BM - 1) / CF::BM);
+  const int tiles_nf = int((N + CF::BN - 1) / CF::BN);
   const int64_t esz = sp.w_bf16 ? 2 : 4;
   // 4-column vector gathers need every W row start aligned to 4 elements
   // (8 bytes for bf16, 16 for fp32) and N a multiple of 4 (no lane straddles N)
@@ -826,8 +866,9 @@ hipError_t run_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const
   const int mode = (sp.w_bf16 ? 1 : 2) + (w_vec ? 2 : 0);
 #define FP4LIN_GEMM_COMP(MODE)                                                                  \
   case MODE:                                                                                    \
-    fp4_gemm_kernel<C, kMx, MODE><<<grid, C::kThreads, 0, stream>>>(                            \
-        Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs, cp, sp.row_ptr,      \
+    fp4_gemm_kernel<CF, kMx, MODE><<<dim3(unsigned(tiles_mf * tiles_nf)), CF::kThreads, 0,      \
+                                     stream>>>(                                                 \
+        Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_mf, Y, ldy, As, Bs, cp, sp.row_ptr,     \
         sp.col, sp.val);                                                                        \
     break;
   switch (mode) {

@@ -675,7 +675,7 @@ def test_gemm_equals_gemm_then_sparse_add(ql):
 def upload_coo(ql, delta, capacity=None):
     """The COO on the device, its arrays `capacity` entries long (at least
     nnz). fp4lin_gemm runs the compensation in its epilogue when the capacity
-    is at most 16 entries per row of A, else as a second kernel: the capacity
+    is at most 10 entries per row of A, else as a second kernel: the capacity
     picks the schedule, and both give the same bits."""
     nz = max(delta.nnz, 1, capacity or 0)
     pad = lambda a, dt: np.concatenate([np.asarray(a, dt), np.zeros(nz - len(a), dt)])
@@ -683,7 +683,7 @@ def upload_coo(ql, delta, capacity=None):
                          upload_f32(pad(delta.val32, np.float32)), upload_i32(delta.row_ptr))
 
 
-FUSED_MAX_PER_ROW = 16
+FUSED_MAX_PER_ROW = 10
 
 
 def schedule_capacity(schedule, M, nnz):
