@@ -125,30 +125,39 @@ __device__ inline int swz(int r, int c) {
   return c ^ ((r ^ (r >> 3)) & 7);
 }
 
+// Tiles of one launch: positions base .. base + nblocks / split - 1 of the
+// order of a tiles_m x tiles_n grid, each cut into split tiles along M (split
+// 2: the two 128-row halves of a 256-row tile).
+struct TileMap {
+  int base, tiles_m, tiles_n, split;
+};
+
 // Tile order: groups of G tile rows sweeping across N; each XCD takes a
 // contiguous run of that order (a bijection from workgroup id to tile).
 // kColumns: the tile columns one after another instead, each swept down M, so
 // that the tiles an XCD runs together share one 256-column strip of the
 // operands and of W (the compensation's gathers then stay in that XCD's L2).
 template <bool kColumns = false>
-__device__ inline void tile_coords(int bid, int nblocks, int tiles_m, int& tm, int& tn) {
+__device__ inline void tile_coords(int bid, int nblocks, const TileMap& tmap, int& tm, int& tn) {
   const int xcd = bid & 7;
   const int idx = bid >> 3;
   const int base = nblocks >> 3, rem = nblocks & 7;
   const int t = xcd * base + (xcd < rem ? xcd : rem) + idx;
   if constexpr (kColumns) {
-    tn = t / tiles_m;
-    tm = t - tn * tiles_m;
+    tn = t / tmap.tiles_m;
+    tm = t - tn * tmap.tiles_m;
     return;
   }
-  const int tiles_n = nblocks / tiles_m;
+  const int u = tmap.base + t / tmap.split;  // position in the order
+  const int half = t % tmap.split;
+  const int tiles_m = tmap.tiles_m;
   constexpr int G = 4;
-  const int per_group = G * tiles_n;
-  const int grp = t / per_group;
+  const int per_group = G * tmap.tiles_n;
+  const int grp = u / per_group;
   const int first_m = grp * G;
   const int gsize = (tiles_m - first_m) < G ? (tiles_m - first_m) : G;
-  const int within = t - grp * per_group;
-  tm = first_m + within % gsize;
+  const int within = u - grp * per_group;
+  tm = (first_m + within % gsize) * tmap.split + half;
   tn = within / gsize;
 }
 
@@ -493,7 +502,7 @@ template <class C, bool kMx, int kComp>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
     const uint8_t* __restrict__ Aq, const float* __restrict__ sA,
     const uint8_t* __restrict__ Bq, const float* __restrict__ sB, int M, int N, int ldq,
-    int tiles_m, float* __restrict__ Y, int64_t ldy, const uint8_t* __restrict__ As,
+    TileMap tmap, float* __restrict__ Y, int64_t ldy, const uint8_t* __restrict__ As,
     const uint8_t* __restrict__ Bs, CompArgs cp, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col, const float* __restrict__ val) {
   constexpr int BM = C::BM, BN = C::BN, WN = C::WN, BKB = C::BKB, CPR = C::CPR;
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
   const int wm = wave / WN;
   const int wn = wave % WN;
   int tm, tn;
-  tile_coords<(kComp != 0) && kFusedColumns>(blockIdx.x, gridDim.x, tiles_m, tm, tn);
+  tile_coords<(kComp != 0) && kFusedColumns>(blockIdx.x, gridDim.x, tmap, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int nkt = (ldq + BKB - 1) / BKB;
 
@@ -807,20 +816,23 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void fp4_gemm_kernel(
 // (LLaMA 1.3B up, 352 large tiles: 45.6 against 41.6 us).
 using GemmTile = GemmCfg<256, 256, 4, 2, 64, 1>;
 using GemmSmallTile = GemmCfg<128, 256, 2, 2, 64, 2>;
-constexpr int64_t kLargeTilesMin = 512;
+constexpr int kLargeTilesMin = 512;
+constexpr int kCUs = 256;  // MI355X
 // Tile of the GEMM with the compensation in its epilogue: the two workgroups
 // on a CU keep the matrix core busy in turn while either one gathers (13B up:
 // 509 against 521 us with 256 x 256 tiles).
 using GemmFusedTile = GemmCfg<128, 256, 2, 2, 64, 2>;
 
+// The GEMM without compensation over positions base .. base + count - 1 of
+// the order of a tiles_m x tiles_n grid of 256 x 256 tiles (C: those tiles,
+// or with 128-row C their two halves).
 template <class C, bool kMx>
 hipError_t launch_plain(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const float* sB,
                         const uint8_t* As, const uint8_t* Bs, int64_t M, int64_t N, int64_t ldq,
-                        float* Y, int64_t ldy, hipStream_t stream) {
-  const int tiles_m = int((M + C::BM - 1) / C::BM);
-  const int tiles_n = int((N + C::BN - 1) / C::BN);
-  fp4_gemm_kernel<C, kMx, 0><<<dim3(unsigned(tiles_m * tiles_n)), C::kThreads, 0, stream>>>(
-      Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_m, Y, ldy, As, Bs, CompArgs{nullptr, 0, 0, 0},
+                        float* Y, int64_t ldy, const TileMap& tmap, int count,
+                        hipStream_t stream) {
+  fp4_gemm_kernel<C, kMx, 0><<<dim3(unsigned(count * tmap.split)), C::kThreads, 0, stream>>>(
+      Aq, sA, Bq, sB, int(M), int(N), int(ldq), tmap, Y, ldy, As, Bs, CompArgs{nullptr, 0, 0, 0},
       nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
@@ -845,11 +857,31 @@ hipError_t run_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const
   // capacity bounds the non-zeros (for the select's own COO it is M*K*(1-q)).
   const bool fused = sp.row_ptr != nullptr && sp.capacity <= kFusedMaxPerRow * M;
   if (!fused) {
-    const int64_t large = ((M + GemmTile::BM - 1) / GemmTile::BM) * ((N + GemmTile::BN - 1) / GemmTile::BN);
-    const hipError_t e =
-        large >= kLargeTilesMin
-            ? launch_plain<GemmTile, kMx>(Aq, sA, Bq, sB, As, Bs, M, N, ldq, Y, ldy, stream)
-            : launch_plain<GemmSmallTile, kMx>(Aq, sA, Bq, sB, As, Bs, M, N, ldq, Y, ldy, stream);
+    static_assert(GemmTile::BM == 2 * GemmSmallTile::BM && GemmTile::BN == GemmSmallTile::BN,
+                  "a large tile is two small ones");
+    const int tiles_m = int((M + GemmTile::BM - 1) / GemmTile::BM);
+    const int tiles_n = int((N + GemmTile::BN - 1) / GemmTile::BN);
+    const int large = tiles_m * tiles_n;
+    hipError_t e;
+    if (large >= kLargeTilesMin) {
+      // whole rounds of large tiles (one per CU), then, when at most half a
+      // round is left, the rest of the order as 128-row halves, two
+      // workgroups per CU: a last round of large tiles would leave most CUs
+      // idle (7B, 96 left: 231 against 222 us; 13B down, 128 left: 279
+      // against 264), while a fuller one runs better as large tiles (13B up,
+      // 192 left: 293 against 300)
+      const int rest = large % kCUs;
+      const int whole = rest <= kCUs / 2 ? large - rest : large;
+      e = launch_plain<GemmTile, kMx>(Aq, sA, Bq, sB, As, Bs, M, N, ldq, Y, ldy,
+                                      TileMap{0, tiles_m, tiles_n, 1}, whole, stream);
+      if (e == hipSuccess && whole < large)
+        e = launch_plain<GemmSmallTile, kMx>(Aq, sA, Bq, sB, As, Bs, M, N, ldq, Y, ldy,
+                                             TileMap{whole, tiles_m, tiles_n, 2}, large - whole,
+                                             stream);
+    } else {
+      e = launch_plain<GemmSmallTile, kMx>(Aq, sA, Bq, sB, As, Bs, M, N, ldq, Y, ldy,
+                                           TileMap{0, tiles_m, tiles_n, 2}, large, stream);
+    }
     if (e != hipSuccess || sp.row_ptr == nullptr) return e;
     return launch_sparse_add(sp, M, N, Y, ldy, stream);
   }
@@ -868,7 +900,8 @@ hipError_t run_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const
   case MODE:                                                                                    \
     fp4_gemm_kernel<CF, kMx, MODE><<<dim3(unsigned(tiles_mf * tiles_nf)), CF::kThreads, 0,      \
                                      stream>>>(                                                 \
-        Aq, sA, Bq, sB, int(M), int(N), int(ldq), tiles_mf, Y, ldy, As, Bs, cp, sp.row_ptr,     \
+        Aq, sA, Bq, sB, int(M), int(N), int(ldq), TileMap{0, tiles_mf, tiles_nf, 1}, Y, ldy, As, \
+        Bs, cp, sp.row_ptr,                                                                     \
         sp.col, sp.val);                                                                        \
     break;
   switch (mode) {
