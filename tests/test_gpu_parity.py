@@ -732,12 +732,14 @@ def test_gemm_compensation_padded_layouts(ql, dtype, N, ldy_pad, ldw_pad, schedu
     assert np.array_equal(host(Ybuf2).view(np.uint32), full.view(np.uint32))
 
 
-def synthetic_delta(rng, M, K, lengths):
+def synthetic_delta(rng, M, K, lengths, pools=None):
     """A COO with the given number of non-zeros per row (distinct ascending
-    columns, values of mixed sign and magnitude), as the oracle's SparseDelta."""
+    columns, values of mixed sign and magnitude), as the oracle's SparseDelta.
+    pools: per row, the columns to draw from (default: all of K)."""
     rows, cols = [], []
     for i, n in enumerate(lengths):
-        c = np.sort(rng.choice(K, int(n), replace=False))
+        pool = K if pools is None else pools[i]
+        c = np.sort(rng.choice(pool, int(n), replace=False))
         rows.append(np.full(c.size, i))
         cols.append(c)
     row = np.concatenate(rows).astype(np.int32) if rows else np.zeros(0, np.int32)
@@ -759,6 +761,10 @@ U32 = 2.0 ** -24
     (257, 264, 3, "mixed"),       # unaligned W rows: element gathers
     (384, 512, 0, "dense-rows"),  # a few long rows among empty ones
     (128, 256, 0, "empty"),       # no non-zero at all
+    (300, 264, 0, "channels"),    # all rows in 12 columns (outlier channels): the same
+    (257, 203, 3, "channels"),    # W rows gathered by every row, ragged M and N, unaligned W
+    (256, 256, 0, "channels-17"),  # 17 shared columns
+    (384, 256, 0, "channels-mixed"),  # 8 shared columns in the first tile, 40 after
 ])
 def test_gemm_compensation_row_structures(ql, wdtype, M, N, ldw_pad, pattern):
     """The compensation under both schedules on COOs built to reach the fused
@@ -778,9 +784,19 @@ def test_gemm_compensation_row_structures(ql, wdtype, M, N, ldw_pad, pattern):
     elif pattern == "dense-rows":
         lengths = np.zeros(M, np.int64)
         lengths[[5, 6, 130, 131, 300, 383]] = [90, 1, 64, 33, 120, 15]
+    elif pattern.startswith("channels"):
+        wide = {"channels": 12, "channels-17": 17, "channels-mixed": 40}[pattern]
+        few = rng.choice(K, 8, replace=False)
+        many = rng.choice(K, wide, replace=False)
+        # rows 0..127 (the first 128-row tile) draw from 8 columns in the mixed pattern
+        pools = [few if (pattern == "channels-mixed" and i < 128) else many for i in range(M)]
+        lengths = np.array([rng.integers(0, min(len(pools[i]), 10) + 1) for i in range(M)])
+        lengths[::7] = 0  # rows without non-zeros between them
+        delta = synthetic_delta(rng, M, K, lengths, pools)
     else:
         lengths = np.zeros(M, np.int64)
-    delta = synthetic_delta(rng, M, K, lengths)
+    if not pattern.startswith("channels"):
+        delta = synthetic_delta(rng, M, K, lengths)
     ca = rng.integers(0, 16, (M, K)).astype(np.uint8)
     cb = rng.integers(0, 16, (N, K)).astype(np.uint8)
     sa = np.exp2(rng.integers(-4, 4, M)).astype(np.float32)
