@@ -32,6 +32,20 @@ struct BF16In {
   __device__ static inline uint32_t sign_bit(T v) { return uint32_t(v) >> 15; }
 };
 
+// One 16-byte load. kStream sets the non-temporal hint: a stream that is
+// read once per pass and is too large to stay in the last-level cache between
+// passes then does not evict the data that does stay there.
+template <bool kStream>
+__device__ inline uint4 load16(const void* p) {
+  if constexpr (kStream) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+  } else {
+    return *static_cast<const uint4*>(p);
+  }
+}
+
 // Eight consecutive elements, loaded with one 16-byte (fp32: two 16-byte)
 // access when the caller has established alignment, else one by one.
 template <class In>
@@ -39,21 +53,22 @@ struct Vec8 {
   typename In::T v[8];
 };
 
-template <class In, bool kAligned>
+template <class In, bool kAligned, bool kStream = false>
 __device__ inline void load8(const typename In::T* __restrict__ p, int64_t valid,
                              Vec8<In>& out) {
   if (kAligned && valid >= 8) {
     if constexpr (In::kBytes == 2) {
-      uint4 u = *reinterpret_cast<const uint4*>(p);
+      uint4 u = load16<kStream>(p);
       out.v[0] = uint16_t(u.x); out.v[1] = uint16_t(u.x >> 16);
       out.v[2] = uint16_t(u.y); out.v[3] = uint16_t(u.y >> 16);
       out.v[4] = uint16_t(u.z); out.v[5] = uint16_t(u.z >> 16);
       out.v[6] = uint16_t(u.w); out.v[7] = uint16_t(u.w >> 16);
     } else {
-      float4 a = *reinterpret_cast<const float4*>(p);
-      float4 b = *reinterpret_cast<const float4*>(p + 4);
-      out.v[0] = a.x; out.v[1] = a.y; out.v[2] = a.z; out.v[3] = a.w;
-      out.v[4] = b.x; out.v[5] = b.y; out.v[6] = b.z; out.v[7] = b.w;
+      const uint4 a = load16<kStream>(p), b = load16<kStream>(p + 4);
+      out.v[0] = __uint_as_float(a.x); out.v[1] = __uint_as_float(a.y);
+      out.v[2] = __uint_as_float(a.z); out.v[3] = __uint_as_float(a.w);
+      out.v[4] = __uint_as_float(b.x); out.v[5] = __uint_as_float(b.y);
+      out.v[6] = __uint_as_float(b.z); out.v[7] = __uint_as_float(b.w);
     }
   } else {
 #pragma unroll
@@ -66,11 +81,11 @@ __device__ inline void load8(const typename In::T* __restrict__ p, int64_t valid
 // wholly inside the row or wholly outside; the load address is clamped into
 // the row so that the vector load is unconditional and several of them can be
 // in flight before the first is used. Otherwise elements are loaded one by one.
-template <class In, bool kFast>
+template <class In, bool kFast, bool kStream = false>
 __device__ inline void load_chunk(const typename In::T* __restrict__ row, int64_t c, int64_t K,
                                   Vec8<In>& v) {
   if constexpr (kFast) {
-    load8<In, true>(row + (c < K ? c : K - 8), 8, v);
+    load8<In, true, kStream>(row + (c < K ? c : K - 8), 8, v);
     if (c >= K) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) v.v[i] = typename In::T(0);
@@ -84,13 +99,13 @@ __device__ inline void load_chunk(const typename In::T* __restrict__ row, int64_
 // lane, chunk j of lane l starting at column c0 + (j * 64 + l) * 8, so each j
 // is one coalesced 64-lane sweep and all CH loads of a slab are issued before
 // the first is used. Reductions over the row stay inside the wave.
-template <class In, bool kFast, int CH>
+template <class In, bool kFast, int CH, bool kStream = false>
 __device__ inline void load_wave_slab(const typename In::T* __restrict__ row, int64_t c0,
                                       int64_t K, Vec8<In> (&v)[CH]) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int j = 0; j < CH; ++j)
-    load_chunk<In, kFast>(row, c0 + (int64_t(j) * kWave + lane) * 8, K, v[j]);
+    load_chunk<In, kFast, kStream>(row, c0 + (int64_t(j) * kWave + lane) * 8, K, v[j]);
 }
 
 // Chunks per lane that cover `cols` columns in one slab, capped at kMax.

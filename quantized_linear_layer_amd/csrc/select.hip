@@ -255,7 +255,7 @@ __device__ inline uint32_t coarse_pick(const uint32_t* __restrict__ part, int np
 constexpr int kWinBins = 3;                     // coarse bins saved per workgroup
 constexpr int kWinWords = kWinBins * kFineBins;
 
-template <bool kFast, bool kFine, int CH>
+template <bool kFast, bool kFine, int CH, bool kStream>
 __global__ __launch_bounds__(kH16Threads) void select_hist16_kernel(
     const uint16_t* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rows_per_wg,
     uint32_t* __restrict__ part, int nparts, uint32_t k, SelState* __restrict__ st,
@@ -309,30 +309,56 @@ __global__ __launch_bounds__(kH16Threads) void select_hist16_kernel(
   const int64_t slab = int64_t(kWave) * CH * 8;
   const int64_t r0 = int64_t(blockIdx.x) * rows_per_wg;
   const int64_t r1 = (r0 + rows_per_wg < M) ? r0 + rows_per_wg : M;
-  for (int64_t r = r0 + __builtin_amdgcn_readfirstlane(t / kWave); r < r1; r += kH16Waves) {
-    const uint16_t* row = A + r * lda;
-    for (int64_t c0 = 0; c0 < K; c0 += slab) {
-      Vec8<BF16In> v[CH];
-      load_wave_slab<BF16In, kFast, CH>(row, c0, K, v);
+  // The wave's slabs in order (its rows r0 + w, r0 + w + 16, ..., each in
+  // slabs of CH chunk sweeps), two register buffers used in turn: the loads
+  // of the next slab are issued before the current one is counted, so they
+  // are in flight while its atomics run. Past the wave's last slab the
+  // prefetch repeats the current one and is not counted.
+  auto hist = [&](int64_t c0, const Vec8<BF16In>(&v)[CH]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        // K < 2^31: column offsets fit 32 bits. kFast: a chunk is wholly
-        // inside the row or wholly past it.
-        const int c = int(c0) + (j * kWave + lane) * 8;
-        if (kFast && c >= int(K)) continue;
+    for (int j = 0; j < CH; ++j) {
+      // K < 2^31: column offsets fit 32 bits. kFast: a chunk is wholly
+      // inside the row or wholly past it.
+      const int c = int(c0) + (j * kWave + lane) * 8;
+      if (kFast && c >= int(K)) continue;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t key = BF16In::key(v[j].v[i]);
-          if (kFast || c + i < int(K)) {
-            if constexpr (kFine) {
-              if ((key >> kFineBits) == prefix) atomicAdd(&h[key & (kFineBins - 1)], 1u);
-            } else {
-              atomicAdd(&h[key], 1u);
-            }
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t key = BF16In::key(v[j].v[i]);
+        if (kFast || c + i < int(K)) {
+          if constexpr (kFine) {
+            if ((key >> kFineBits) == prefix) atomicAdd(&h[key & (kFineBins - 1)], 1u);
+          } else {
+            atomicAdd(&h[key], 1u);
           }
         }
       }
     }
+  };
+  // the slab after (r, c0), or (r, c0) itself past the wave's last one
+  auto next = [&](int64_t r, int64_t c0, int64_t& rn, int64_t& cn) __attribute__((always_inline)) {
+    rn = r;
+    cn = c0 + slab;
+    if (cn >= K) {
+      cn = 0;
+      rn = r + kH16Waves;
+    }
+    return rn < r1;
+  };
+  int64_t r = r0 + __builtin_amdgcn_readfirstlane(t / kWave), c0 = 0;
+  Vec8<BF16In> va[CH], vb[CH];
+  if (r < r1) load_wave_slab<BF16In, kFast, CH, kStream>(A + r * lda, c0, K, va);
+  while (r < r1) {
+    int64_t rb, cb;
+    const bool more = next(r, c0, rb, cb);
+    load_wave_slab<BF16In, kFast, CH, kStream>(A + (more ? rb : r) * lda, more ? cb : c0, K, vb);
+    hist(c0, va);
+    if (!more) break;
+    int64_t ra, ca;
+    const bool more2 = next(rb, cb, ra, ca);
+    load_wave_slab<BF16In, kFast, CH, kStream>(A + (more2 ? ra : rb) * lda, more2 ? ca : cb, K, va);
+    hist(cb, vb);
+    r = ra;
+    c0 = ca;
   }
   __syncthreads();
   if constexpr (kFine) {
@@ -491,14 +517,14 @@ struct RowChunk<F32In> {
 // Chunk c (elements c .. c+7) of a row of K elements, zero past K. kFast: the
 // row is 16-byte aligned and K % 8 == 0 (vector loads; a chunk is wholly inside
 // the row or wholly past it). kFull: the chunk lies inside the row.
-template <bool kFast, bool kFull>
+template <bool kFast, bool kFull, bool kStream>
 __device__ inline void load_row_chunk(const uint16_t* __restrict__ row, int64_t c, int64_t K,
                                       uint4& w) {
   if constexpr (kFast) {
     if constexpr (kFull) {
-      w = *reinterpret_cast<const uint4*>(row + c);
+      w = load16<kStream>(row + c);
     } else {
-      w = *reinterpret_cast<const uint4*>(row + (c < K ? c : K - 8));
+      w = load16<kStream>(row + (c < K ? c : K - 8));
       if (c >= K) w = make_uint4(0, 0, 0, 0);
     }
   } else {
@@ -510,23 +536,23 @@ __device__ inline void load_row_chunk(const uint16_t* __restrict__ row, int64_t 
   }
 }
 
-template <bool kFast, bool kFull>
+template <bool kFast, bool kFull, bool kStream>
 __device__ inline void load_row_chunk(const float* __restrict__ row, int64_t c, int64_t K,
                                       Vec8<F32In>& v) {
   if constexpr (kFull)
-    load8<F32In, kFast>(row + c, 8, v);
+    load8<F32In, kFast, kStream>(row + c, 8, v);
   else
-    load_chunk<F32In, kFast>(row, c, K, v);
+    load_chunk<F32In, kFast, kStream>(row, c, K, v);
 }
 
 // Chunk j of lane l starts at column c0 + (64j + l) * 8.
-template <class In, bool kFast, bool kFull, int CH>
+template <class In, bool kFast, bool kFull, int CH, bool kStream>
 __device__ inline void load_row_slab(const typename In::T* __restrict__ row, int64_t c0,
                                      int64_t K, typename RowChunk<In>::T (&v)[CH]) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int j = 0; j < CH; ++j)
-    load_row_chunk<kFast, kFull>(row, c0 + (int64_t(j) * kWave + lane) * 8, K, v[j]);
+    load_row_chunk<kFast, kFull, kStream>(row, c0 + (int64_t(j) * kWave + lane) * 8, K, v[j]);
 }
 
 // Count of the entries of a chunk with |a| > tau (chunks past K are zero, and
@@ -720,7 +746,7 @@ __device__ inline uint32_t encode_chunk_mx(const Vec8<F32In>& v, float tau, int&
 // (Looking the key up between the first row's loads and their use measured
 // slower: it costs registers.) kAmax: also the row's amax clamped to tau into
 // amax[r].
-template <class In, bool kFast, bool kPick, bool kAmax>
+template <class In, bool kFast, bool kPick, bool kAmax, bool kStream>
 __device__ __attribute__((always_inline)) inline void count_rows_body(
     int64_t bid, const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda,
     int64_t rpw, SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
@@ -750,7 +776,7 @@ __device__ __attribute__((always_inline)) inline void count_rows_body(
     for_row_slabs(K, [&](auto ch, auto full, int64_t c0) __attribute__((always_inline)) {
       constexpr int CH = decltype(ch)::value;
       C v[CH];
-      load_row_slab<In, kFast, decltype(full)::value, CH>(row, c0, K, v);
+      load_row_slab<In, kFast, decltype(full)::value, CH, kStream>(row, c0, K, v);
 #pragma unroll
       for (int j = 0; j < CH; ++j) count_fold<kAmax>(v[j], bias, c, mk);
     });
@@ -772,12 +798,12 @@ __device__ __attribute__((always_inline)) inline void count_rows_body(
   }
 }
 
-template <class In, bool kFast, bool kPick>
+template <class In, bool kFast, bool kPick, bool kStream>
 __global__ __launch_bounds__(kRowWaves * kWave) void count_rows_kernel(
     const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
     SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
     uint32_t* __restrict__ cnt, uint32_t* __restrict__ gsum) {
-  count_rows_body<In, kFast, kPick, false>(blockIdx.x, A, M, K, lda, rpw, st, fine, tau, cnt,
+  count_rows_body<In, kFast, kPick, false, kStream>(blockIdx.x, A, M, K, lda, rpw, st, fine, tau, cnt,
                                            gsum, nullptr);
 }
 
@@ -792,7 +818,7 @@ constexpr int kQuantMx = 2;     // micro-scaled codes and block scales (Xs, step
 // adds the counts of the lower rows of the batch, so waves need no barrier
 // after the first. With kQuant, the codes of the row's padded length ldq * 2
 // (zero past K) go to Xq + r * ldq.
-template <class In, bool kFast, int kQuant>
+template <class In, bool kFast, int kQuant, bool kStream>
 __device__ __attribute__((always_inline)) inline void compact_rows_body(
     int64_t bid, const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda,
     int64_t rpw, const SelState* __restrict__ st, const float* __restrict__ tau_p,
@@ -849,7 +875,7 @@ __device__ __attribute__((always_inline)) inline void compact_rows_body(
         constexpr int CH = decltype(ch)::value;
         constexpr bool kFull = decltype(full)::value;
         C v[CH];
-        load_row_slab<In, kFast, kFull, CH>(row, c0, K, v);
+        load_row_slab<In, kFast, kFull, CH, kStream>(row, c0, K, v);
         compact_slab<C, CH>(v, c0, r, tkey, tau, pos, cap, out_row, out_col, out_val);
         if constexpr (kQuant != kQuantNone) {
 #pragma unroll
@@ -877,14 +903,14 @@ __device__ __attribute__((always_inline)) inline void compact_rows_body(
   }
 }
 
-template <class In, bool kFast>
+template <class In, bool kFast, bool kStream>
 __global__ __launch_bounds__(kRowWaves * kWave) void compact_rows_kernel(
     const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
     const SelState* __restrict__ st, const float* __restrict__ tau_p,
     const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ gsum, int64_t capacity,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
     float* __restrict__ out_val) {
-  compact_rows_body<In, kFast, kQuantNone>(blockIdx.x, A, M, K, lda, rpw, st, tau_p, cnt, gsum,
+  compact_rows_body<In, kFast, kQuantNone, kStream>(blockIdx.x, A, M, K, lda, rpw, st, tau_p, cnt, gsum,
                                            capacity, row_ptr, out_row, out_col, out_val, nullptr,
                                            0, nullptr, nullptr);
 }
@@ -916,7 +942,7 @@ struct WPass {
   int64_t gx, nb;
 };
 
-template <class In, bool kFast, bool kWAligned, bool kMx>
+template <class In, bool kFast, bool kWAligned, bool kMx, bool kStream>
 __global__ __launch_bounds__(kRowWaves * kWave) void count_wpass_kernel(
     const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
     SelState* st, const uint32_t* __restrict__ fine, float* __restrict__ tau,
@@ -925,7 +951,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void count_wpass_kernel(
   using T = typename In::T;
   int64_t i;
   if (pair_first(blockIdx.x, na, wp.nb, i))
-    count_rows_body<In, kFast, In::kBytes == 2, !kMx>(i, A, M, K, lda, rpw, st, fine, tau, cnt,
+    count_rows_body<In, kFast, In::kBytes == 2, !kMx, kStream>(i, A, M, K, lda, rpw, st, fine, tau, cnt,
                                                       gsum, amax);
   else if constexpr (kMx)
     quantize_cols_mx_body<In, kWAligned>(i % wp.gx, i / wp.gx, static_cast<const T*>(wp.W), wp.K,
@@ -936,7 +962,7 @@ __global__ __launch_bounds__(kRowWaves * kWave) void count_wpass_kernel(
                                wp.ldw, wp.colmax);
 }
 
-template <class In, bool kFast, bool kWAligned, bool kMx>
+template <class In, bool kFast, bool kWAligned, bool kMx, bool kStream>
 __global__ __launch_bounds__(kRowWaves * kWave) void compact_wpass_kernel(
     const typename In::T* __restrict__ A, int64_t M, int64_t K, int64_t lda, int64_t rpw,
     const SelState* __restrict__ st, const float* __restrict__ tau_p,
@@ -947,10 +973,9 @@ __global__ __launch_bounds__(kRowWaves * kWave) void compact_wpass_kernel(
   using T = typename In::T;
   int64_t i;
   if (pair_first(blockIdx.x, na, wp.nb, i))
-    compact_rows_body<In, kFast, kMx ? kQuantMx : kQuantToken>(i, A, M, K, lda, rpw, st, tau_p,
-                                                               cnt, gsum, capacity, row_ptr,
-                                                               out_row, out_col, out_val, Xq, ldq,
-                                                               sX, Xs);
+    compact_rows_body<In, kFast, kMx ? kQuantMx : kQuantToken, kStream>(
+        i, A, M, K, lda, rpw, st, tau_p, cnt, gsum, capacity, row_ptr, out_row, out_col, out_val,
+        Xq, ldq, sX, Xs);
   else if constexpr (!kMx)
     quantize_cols_body<In, kWAligned>(i % wp.gx, i / wp.gx, static_cast<const T*>(wp.W), wp.K,
                                       wp.N, wp.ldw, wp.colmax, wp.Wq, wp.ldq,
@@ -1016,7 +1041,7 @@ struct H16Work {
 
 // The two bfloat16 histogram passes (the coarse one also clears nclear words
 // at clear).
-template <bool kFast>
+template <bool kFast, bool kStream>
 hipError_t launch_hist16(const uint16_t* A, int64_t M, int64_t K, int64_t lda, int64_t k,
                          const H16Work& w, uint32_t* clear, int64_t nclear, hipStream_t stream) {
   // one workgroup per CU (MI355X: 256), at least one row per wave
@@ -1026,21 +1051,25 @@ hipError_t launch_hist16(const uint16_t* A, int64_t M, int64_t K, int64_t lda, i
   const dim3 g(static_cast<unsigned>(wgs));
   // k < M*K < 2^32
   const uint32_t k32 = uint32_t(k);
-  switch (chunks_per_lane(K, 16)) {
-#define FP4LIN_H16(CH)                                                                           \
-  case CH:                                                                                       \
-    select_hist16_kernel<kFast, false, CH><<<g, kH16Threads, 0, stream>>>(                       \
-        A, M, K, lda, per, w.part, 0, k32, w.st, w.fine, w.win, w.fwin, clear, nclear);          \
-    select_hist16_kernel<kFast, true, CH><<<g, kH16Threads, 0, stream>>>(                        \
-        A, M, K, lda, per, w.part, int(wgs), k32, w.st, w.fine, w.win, w.fwin, nullptr, 0);      \
+  // two slabs are held in registers at once: at most 8 chunks per lane (4
+  // with element loads)
+  auto run = [&](auto ch) {
+    constexpr int CH = decltype(ch)::value;
+    select_hist16_kernel<kFast, false, CH, kStream><<<g, kH16Threads, 0, stream>>>(
+        A, M, K, lda, per, w.part, 0, k32, w.st, w.fine, w.win, w.fwin, clear, nclear);
+    select_hist16_kernel<kFast, true, CH, kStream><<<g, kH16Threads, 0, stream>>>(
+        A, M, K, lda, per, w.part, int(wgs), k32, w.st, w.fine, w.win, w.fwin, nullptr, 0);
     return hipSuccess;
-    FP4LIN_H16(1)
-    FP4LIN_H16(2)
-    FP4LIN_H16(4)
-    FP4LIN_H16(8)
-    FP4LIN_H16(16)
-#undef FP4LIN_H16
+  };
+  switch (chunks_per_lane(K, kFast ? 8 : 4)) {
+    case 1:
+      return run(std::integral_constant<int, 1>{});
+    case 2:
+      return run(std::integral_constant<int, 2>{});
+    case 4:
+      return run(std::integral_constant<int, 4>{});
     default:
+      if constexpr (kFast) return run(std::integral_constant<int, 8>{});
       return hipErrorInvalidValue;
   }
 }
@@ -1070,7 +1099,7 @@ void launch_hist32(const float* A, int64_t M, int64_t K, int64_t lda, int64_t k,
   }
 }
 
-template <class In, bool kFast>
+template <class In, bool kFast, bool kStream>
 hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t k, float* tau,
                       int64_t capacity, int32_t* row, int32_t* col, float* val,
                       int32_t* row_ptr, void* ws, hipStream_t stream) {
@@ -1080,7 +1109,7 @@ hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t
   const uint32_t* fine = nullptr;
   if constexpr (In::kBytes == 2) {
     const H16Work h(w);
-    const hipError_t e = launch_hist16<kFast>(A, M, K, lda, k, h, nullptr, 0, stream);
+    const hipError_t e = launch_hist16<kFast, kStream>(A, M, K, lda, k, h, nullptr, 0, stream);
     if (e != hipSuccess) return e;
     fine = h.fine;
   } else {
@@ -1088,9 +1117,9 @@ hipError_t run_select(const void* Ap, int64_t M, int64_t K, int64_t lda, int64_t
   }
   const int64_t rpw = rows_per_wave(M);
   const dim3 g(static_cast<unsigned>(row_groups(M)));
-  count_rows_kernel<In, kFast, In::kBytes == 2><<<g, kRowWaves * kWave, 0, stream>>>(
+  count_rows_kernel<In, kFast, In::kBytes == 2, kStream><<<g, kRowWaves * kWave, 0, stream>>>(
       A, M, K, lda, rpw, w.st, fine, tau, w.cnt, w.gsum);
-  compact_rows_kernel<In, kFast><<<g, kRowWaves * kWave, 0, stream>>>(
+  compact_rows_kernel<In, kFast, kStream><<<g, kRowWaves * kWave, 0, stream>>>(
       A, M, K, lda, rpw, w.st, tau, w.cnt, w.gsum, capacity, row_ptr, row, col, val);
   return hipGetLastError();
 }
@@ -1101,7 +1130,7 @@ bool rows_fast(const void* A, int esz, int64_t K, int64_t lda) {
 
 // Histograms, then the row count with W's first pass, then the compaction
 // (with the quantization of A) with W's codes.
-template <class In, bool kFast, bool kWAligned, bool kMx>
+template <class In, bool kFast, bool kWAligned, bool kMx, bool kStream>
 hipError_t forward_front(const FrontArgs& f, hipStream_t stream) {
   using T = typename In::T;
   const T* A = static_cast<const T*>(f.A);
@@ -1111,7 +1140,8 @@ hipError_t forward_front(const FrontArgs& f, hipStream_t stream) {
   const uint32_t* fine = nullptr;
   if constexpr (In::kBytes == 2) {
     const H16Work h(w);
-    const hipError_t e = launch_hist16<kFast>(A, f.M, f.K, f.lda, f.k, h, clear, nclear, stream);
+    const hipError_t e =
+        launch_hist16<kFast, kStream>(A, f.M, f.K, f.lda, f.k, h, clear, nclear, stream);
     if (e != hipSuccess) return e;
     fine = h.fine;
   } else {
@@ -1130,7 +1160,7 @@ hipError_t forward_front(const FrontArgs& f, hipStream_t stream) {
     wp.gx = (f.N + kColStrip - 1) / kColStrip;
     wp.nb = wp.gx * ((f.K + kColRows - 1) / kColRows);
   }
-  count_wpass_kernel<In, kFast, kWAligned, kMx>
+  count_wpass_kernel<In, kFast, kWAligned, kMx, kStream>
       <<<dim3(unsigned(na + wp.nb)), kRowWaves * kWave, 0, stream>>>(
           A, f.M, f.K, f.lda, rpw, w.st, fine, f.tau, w.cnt, w.gsum, static_cast<float*>(f.sA),
           na, wp);
@@ -1142,7 +1172,7 @@ hipError_t forward_front(const FrontArgs& f, hipStream_t stream) {
     wp.gx = (f.N + kTN - 1) / kTN;
     wp.nb = wp.gx * (Kp / kTK);
   }
-  compact_wpass_kernel<In, kFast, kWAligned, kMx>
+  compact_wpass_kernel<In, kFast, kWAligned, kMx, kStream>
       <<<dim3(unsigned(na + wp.nb)), kRowWaves * kWave, 0, stream>>>(
           A, f.M, f.K, f.lda, rpw, w.st, f.tau, w.cnt, w.gsum, f.capacity, f.row_ptr, f.row,
           f.col, f.val, f.Aq, f.ldq, kMx ? nullptr : static_cast<float*>(f.sA),
@@ -1150,16 +1180,46 @@ hipError_t forward_front(const FrontArgs& f, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The row kernels and the bfloat16 histogram passes read A with the
+// non-temporal hint when the operands of the passes (A, and W in the forward)
+// exceed this many bytes: the last-level cache (256 MB on MI355X) then cannot
+// keep them from one pass to the next, and streaming A through without
+// allocating keeps more of W (read twice, then gathered by the compensation)
+// resident. Below it, A stays cached for the passes after the first.
+constexpr int64_t kStreamBytes = int64_t(192) << 20;
+
 template <class In, bool kMx>
 hipError_t forward_front_dispatch(const FrontArgs& f, hipStream_t stream) {
   const bool fast = rows_fast(f.A, In::kBytes, f.K, f.lda);
   const bool w_aligned = (reinterpret_cast<uintptr_t>(f.W) % 16 == 0) &&
                          ((f.ldw * In::kBytes) % 16 == 0);
+  const bool streamed = (f.M * f.K + f.K * f.N) * In::kBytes > kStreamBytes;
+  auto run = [&](auto fast_c, auto waligned_c) {
+    constexpr bool kF = decltype(fast_c)::value, kW = decltype(waligned_c)::value;
+    return streamed ? forward_front<In, kF, kW, kMx, true>(f, stream)
+                    : forward_front<In, kF, kW, kMx, false>(f, stream);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (fast) return w_aligned ? run(T_{}, T_{}) : run(T_{}, F_{});
+  return w_aligned ? run(F_{}, T_{}) : run(F_{}, F_{});
+}
+
+template <class In>
+hipError_t select_dispatch(const void* A, int64_t M, int64_t K, int64_t lda, int64_t k,
+                           float* tau, int64_t capacity, int32_t* row, int32_t* col, float* val,
+                           int32_t* row_ptr, void* ws, hipStream_t stream) {
+  const bool fast = rows_fast(A, In::kBytes, K, lda);
+  const bool streamed = M * K * In::kBytes > kStreamBytes;
   if (fast)
-    return w_aligned ? forward_front<In, true, true, kMx>(f, stream)
-                     : forward_front<In, true, false, kMx>(f, stream);
-  return w_aligned ? forward_front<In, false, true, kMx>(f, stream)
-                   : forward_front<In, false, false, kMx>(f, stream);
+    return streamed ? run_select<In, true, true>(A, M, K, lda, k, tau, capacity, row, col, val,
+                                                 row_ptr, ws, stream)
+                    : run_select<In, true, false>(A, M, K, lda, k, tau, capacity, row, col, val,
+                                                  row_ptr, ws, stream);
+  return streamed ? run_select<In, false, true>(A, M, K, lda, k, tau, capacity, row, col, val,
+                                                row_ptr, ws, stream)
+                  : run_select<In, false, false>(A, M, K, lda, k, tau, capacity, row, col, val,
+                                                 row_ptr, ws, stream);
 }
 
 }  // namespace
@@ -1174,16 +1234,10 @@ hipError_t launch_outlier_select(const void* A, bool bf16, int64_t M, int64_t K,
                                  int64_t k, float* tau, int64_t capacity, int32_t* row,
                                  int32_t* col, float* val, int32_t* row_ptr, void* ws,
                                  hipStream_t stream) {
-  const bool fast = rows_fast(A, bf16 ? 2 : 4, K, lda);
-  if (bf16)
-    return fast ? run_select<BF16In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr,
-                                           ws, stream)
-                : run_select<BF16In, false>(A, M, K, lda, k, tau, capacity, row, col, val,
-                                            row_ptr, ws, stream);
-  return fast ? run_select<F32In, true>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr,
+  return bf16 ? select_dispatch<BF16In>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr,
                                         ws, stream)
-              : run_select<F32In, false>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr,
-                                         ws, stream);
+              : select_dispatch<F32In>(A, M, K, lda, k, tau, capacity, row, col, val, row_ptr, ws,
+                                       stream);
 }
 
 hipError_t launch_forward_front(const FrontArgs& f, hipStream_t stream) {

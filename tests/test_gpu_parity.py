@@ -588,6 +588,24 @@ def test_forward_q_one_is_plain_quantized_gemm(ql):
     assert np.array_equal(host(Y).astype(np.float64), A.astype(np.float64) @ W.astype(np.float64))
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_forward_streamed_rows(ql, dtype):
+    """A of 210 MB, above the 192 MiB (A + W) at which the row kernels and the
+    histogram passes read A with the non-temporal hint: the forward's tau,
+    COO, codes and scales are bit-exact, Y matches on every 61st row, and the
+    public select (the same rule on A alone) is bit-exact too. K = 6400 ends
+    in a ragged slab in every row kernel."""
+    M, K, N = (8192, 6400, 72) if dtype == wl.F32 else (16384, 6400, 72)
+    log(f"streamed rows {dtype} {M}x{K}x{N}")
+    rng = np.random.default_rng(6400)
+    a = wl.draw_activation(rng, M, K, "t3", max(1, K // 200), 50.0)
+    w = wl.draw_weight(rng, K, N)
+    L = wl.Layer(f"streamed-{dtype}", wl.from_f32(a, dtype), wl.from_f32(w, dtype), 0.99)
+    del a
+    check_forward(ql, L, rows=np.arange(0, M, 61))
+    check_select(ql, L.A, L.q)
+
+
 @pytest.mark.parametrize("case", ["llama1.3b", "k13824", "f32", "unaligned"])
 def test_forward_matches_stage_calls(ql, case):
     """fp4lin_forward == the four public calls in order (same bits): the
