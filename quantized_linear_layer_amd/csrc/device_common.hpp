@@ -32,6 +32,11 @@ struct BF16In {
   __device__ static inline uint32_t sign_bit(T v) { return uint32_t(v) >> 15; }
 };
 
+// Operand bytes above which a kernel streams its single-use data with the
+// non-temporal hint: most of the 256 MB last-level cache (MI355X), so that
+// below it everything a layer reads stays cached from one kernel to the next.
+constexpr int64_t kStreamBytes = int64_t(192) << 20;
+
 // One 16-byte load. kStream sets the non-temporal hint: a stream that is
 // read once per pass and is too large to stay in the last-level cache between
 // passes then does not evict the data that does stay there.

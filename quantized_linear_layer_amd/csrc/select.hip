@@ -1182,11 +1182,10 @@ hipError_t forward_front(const FrontArgs& f, hipStream_t stream) {
 
 // The row kernels and the bfloat16 histogram passes read A with the
 // non-temporal hint when the operands of the passes (A, and W in the forward)
-// exceed this many bytes: the last-level cache (256 MB on MI355X) then cannot
-// keep them from one pass to the next, and streaming A through without
-// allocating keeps more of W (read twice, then gathered by the compensation)
-// resident. Below it, A stays cached for the passes after the first.
-constexpr int64_t kStreamBytes = int64_t(192) << 20;
+// exceed kStreamBytes: the last-level cache then cannot keep them from one
+// pass to the next, and streaming A through without allocating keeps more of
+// W (read twice, then gathered by the compensation) resident. Below it, A
+// stays cached for the passes after the first.
 
 template <class In, bool kMx>
 hipError_t forward_front_dispatch(const FrontArgs& f, hipStream_t stream) {

@@ -20,6 +20,8 @@
 // order, so the waves running together on an XCD read the same W strip
 // through its L2. Single-wave workgroups free their slot as soon as their own
 // row is done. Rows without non-zeros are left untouched.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -97,14 +99,22 @@ __device__ inline WRaw<kBf16> load_part(const void* __restrict__ W, int64_t off,
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Y is streamed once per unit. The result is stored non-temporally, so the
-// stream of Y lines does not evict the W strip that the gathers reuse from L2;
-// the Y read is a plain load (measured a little faster than a non-temporal one).
-__device__ inline f32x4 load_y4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+// stream of Y lines does not evict the W strip that the gathers reuse from L2.
+// When Y and W together exceed what the last-level cache holds (kStreamY) the
+// Y read is non-temporal too, which keeps W resident there for the gathers;
+// below that a plain load measured faster (Y then stays cached itself).
+template <bool kStreamY>
+__device__ inline f32x4 load_y4(const float* p) {
+  if constexpr (kStreamY)
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  else
+    return *reinterpret_cast<const f32x4*>(p);
+}
 __device__ inline void store_y4(f32x4 v, float* p) {
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
 }
 
-template <bool kBf16>
+template <bool kBf16, bool kStreamY>
 __global__ __launch_bounds__(64) void sparse_add_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
     const float* __restrict__ val, const void* __restrict__ W, int64_t ldw, int w_bytes,
@@ -141,7 +151,7 @@ __global__ __launch_bounds__(64) void sparse_add_kernel(
   float yo[kCPL];
   if (valid > 0) {
     if (y_full) {
-      const f32x4 u0 = load_y4(yrow), u1 = load_y4(yrow + 4);
+      const f32x4 u0 = load_y4<kStreamY>(yrow), u1 = load_y4<kStreamY>(yrow + 4);
       yo[0] = u0[0]; yo[1] = u0[1]; yo[2] = u0[2]; yo[3] = u0[3];
       yo[4] = u1[0]; yo[5] = u1[1]; yo[6] = u1[2]; yo[7] = u1[3];
     } else {
@@ -274,16 +284,22 @@ hipError_t launch_sparse_add(const SparseArgs& sp, int64_t M, int64_t N, float* 
   // One single-wave workgroup per unit, launched in chunks that keep the
   // thread count of one launch below 2^32.
   constexpr int64_t kChunk = int64_t(1) << 24;
+  const bool stream_y = M * N * 4 + sp.w_rows * N * esz > kStreamBytes;
+  auto run = [&](auto bf16_c, auto stream_c, int64_t base, int64_t blocks) {
+    sparse_add_kernel<decltype(bf16_c)::value, decltype(stream_c)::value>
+        <<<dim3(unsigned(blocks)), 64, 0, stream>>>(sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw,
+                                                    w_bytes, w_vec ? 1 : 0, Y, ldy,
+                                                    y_vec ? 1 : 0, int(M), int(N), base,
+                                                    base + blocks);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   for (int64_t base = 0; base < units; base += kChunk) {
     const int64_t blocks = units - base < kChunk ? units - base : kChunk;
     if (sp.w_bf16)
-      sparse_add_kernel<true><<<dim3(unsigned(blocks)), 64, 0, stream>>>(
-          sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_bytes, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0,
-          int(M), int(N), base, base + blocks);
+      stream_y ? run(T_{}, T_{}, base, blocks) : run(T_{}, F_{}, base, blocks);
     else
-      sparse_add_kernel<false><<<dim3(unsigned(blocks)), 64, 0, stream>>>(
-          sp.row_ptr, sp.col, sp.val, sp.W, sp.ldw, w_bytes, w_vec ? 1 : 0, Y, ldy, y_vec ? 1 : 0,
-          int(M), int(N), base, base + blocks);
+      stream_y ? run(F_{}, T_{}, base, blocks) : run(F_{}, F_{}, base, blocks);
   }
   return hipGetLastError();
 }

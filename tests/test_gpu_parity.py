@@ -606,6 +606,20 @@ def test_forward_streamed_rows(ql, dtype):
     check_select(ql, L.A, L.q)
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_forward_streamed_y(ql, dtype):
+    """Y of 210 MB with 25.6 COO entries per row: the compensation runs after
+    the GEMM and reads Y with the non-temporal hint (Y + W above 192 MiB);
+    Y matches on every 61st row and the operands are bit-exact."""
+    M, K, N = 8192, 256, 6400
+    log(f"streamed Y {dtype} {M}x{K}x{N}")
+    rng = np.random.default_rng(6401)
+    a = wl.draw_activation(rng, M, K, "t3", 2, 50.0)
+    w = wl.draw_weight(rng, K, N)
+    L = wl.Layer(f"streamed-y-{dtype}", wl.from_f32(a, dtype), wl.from_f32(w, dtype), 0.9)
+    check_forward(ql, L, rows=np.arange(0, M, 61))
+
+
 @pytest.mark.parametrize("case", ["llama1.3b", "k13824", "f32", "unaligned"])
 def test_forward_matches_stage_calls(ql, case):
     """fp4lin_forward == the four public calls in order (same bits): the
