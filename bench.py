@@ -770,10 +770,12 @@ def main():
         torch.cuda.empty_cache()
         up, down = wl.make_13b_pair(seed=args.seed)
         n13 = max(1, min(args.steps, 10))
-        out["llama13b_ffn_up"] = forward_rate(up, dev, n13, 3)
+        # 20 untimed calls first: the GPU sat idle during the CPU baseline, and
+        # its clock needs some milliseconds of load to come back up
+        out["llama13b_ffn_up"] = forward_rate(up, dev, n13, 20)
         del up
         torch.cuda.empty_cache()
-        out["llama13b_ffn_down"] = forward_rate(down, dev, n13, 3)
+        out["llama13b_ffn_down"] = forward_rate(down, dev, n13, 20)
         del down
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
