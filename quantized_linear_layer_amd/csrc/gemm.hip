@@ -268,10 +268,8 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
   static_assert(kPerStage * 16 * kPitch * 4 <= C::kStageBytes, "the blocks fit two stages");
   // LDS column of column c in block row r
   auto lds_col = [](int r, int c) { return c ^ (((r >> 2) & 1) << 5); };
-  // non-zeros per gather group and groups in flight (the element-load path,
-  // 4 loads per non-zero, keeps 8 x 2 within the vmcnt range)
-  constexpr int G = kWVec ? 8 : 8;
-  constexpr int D = kWVec ? 2 : 2;
+  // non-zeros per gather group (one group per row is in flight ahead)
+  constexpr int G = 8;
 
   // scales applied once, in place (the accumulators are then the output)
   if constexpr (!kMx) {
@@ -305,138 +303,103 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
   // the whole tile width lies below N and Y takes 16-byte stores (uniform)
   const bool y_full = ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) && ((ldy & 3) == 0) &&
                       n0 + BN <= N;
-  // The COO is read-only while the kernel runs: reading it through the
-  // constant address space lets every (wave-uniform) entry load be a scalar
-  // load into SGPRs, also after the epilogue's stores to Y. (Through generic
-  // pointers the compiler used vector loads for some of them, and its wait
-  // counting then made each gather group wait for every load in flight.)
+  // Row boundaries come through the constant address space as scalar loads
+  // (the COO is read-only while the kernel runs). The entries themselves
+  // (column, value) are read as buffers that return zero at or past nnz, a
+  // group of G by lanes 0 .. G-1 of one vector load, and reach the wave as
+  // scalars through readlane: the scalar unit, which a CU shares among its
+  // waves, is left almost nothing to do per non-zero (with scalar entry
+  // loads, bounds clamps, per-slot weight masks and a search of the row
+  // boundaries it ran about 30 scalar instructions per non-zero and set the
+  // pace of the whole epilogue).
   typedef const __attribute__((address_space(4))) int32_t cint32;
-  typedef const __attribute__((address_space(4))) float cfloat;
   cint32* const rp_c = (cint32*)row_ptr;
-  cint32* const col_c = (cint32*)col;
-  cfloat* const val_c = (cfloat*)val;
+  const int nnz = rp_c[M];
+  const __amdgpu_buffer_rsrc_t rsCol =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(col), 0, nnz * 4, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsVal =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(val), 0, nnz * 4, kBufferFlags);
+  // entries e0 .. e0+G-1: lane u < G gets entry e0 + u (zero past nnz)
+  auto load_entries = [&](int e0, int& cv, float& vv) {
+    const int voff = lane < G ? (e0 + lane) * 4 : nnz * 4;
+    cv = __builtin_amdgcn_raw_buffer_load_b32(rsCol, voff, 0, 0);
+    vv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsVal, voff, 0, 0));
+  };
+  // the G gathers of a group whose first n entries are the row's (n may
+  // exceed G): slots past n take weight 0 (0 * w adds nothing, so the fp32
+  // sum keeps its value) and read the W row of whatever entry they hold
+  auto gather = [&](int cv, float vv, int n, WSeg<kBf16W> (&w)[G], float (&wt)[G]) {
+    const int offv = cv * row_bytes;  // < K * ldw * element size < 2^31
+    const float vm = lane < n ? vv : 0.0f;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int so = __builtin_amdgcn_readlane(offv, u);
+      wt[u] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(vm), u));
+      w[u] = load_wseg<kBf16W, kWVec>(rsW, voffW, so);
+    }
+  };
 
   // Rows g0 .. g0+7 of the chunk just staged (their LDS rows at rblk, which
-  // only this wave touches until the next barrier). The non-zeros are taken
-  // in groups of G that start at a row's first non-zero; a row's last group
-  // gives its unused slots weight 0 (0 * w adds nothing, so the sum stays the
-  // same fp32 value), so every group is G unconditional multiply-adds and only
-  // a row's last group branches, to put Y0 + s into its LDS row. The groups go
-  // through a ring of D buffers (D groups in flight); the loop runs a count of
-  // groups fixed beforehand, padded with all-zero groups to a multiple of D,
-  // so that every iteration is the same code. No store is issued in the loop:
-  // the 8 rows leave for Y after it. A wave issues one instruction per 4
-  // cycles, so the scalar work per non-zero is kept to a few instructions.
+  // only this wave touches until the next barrier), one row after the other
+  // in compile-time order. A row's first G non-zeros are one group; its
+  // entries are loaded two rows ahead and its gathers one row ahead, so the
+  // gathers of row j+1 are in flight while row j is multiplied. The rare
+  // longer rows take their further groups one at a time after the first.
+  // Every row, empty or not, issues the same loads, so the counter waits the
+  // compiler places stay exact; then Y0 + s goes into the row's LDS row. No
+  // store is issued in the loop: the 8 rows leave for Y after it.
   auto finish_rows = [&](int g0) {
     float* const rows = const_cast<float*>(rblk);
     // the 9 row boundaries (rows past M have no entries)
     int rp[9];
 #pragma unroll
     for (int j = 0; j < 9; ++j) rp[j] = rp_c[g0 + j < M ? g0 + j : M];
-    const int eb = rp[0], ee = rp[8];
-    if (eb < ee) {
-      // groups in all: a row of n non-zeros takes ceil(n / G)
-      int ngroups = 0;
+    if (rp[0] < rp[8]) {
+      int ce[2];
+      float ve[2];
+      WSeg<kBf16W> wq[2][G];
+      float wt[2][G];
+      load_entries(rp[0], ce[0], ve[0]);
+      load_entries(rp[1], ce[1], ve[1]);
+      gather(ce[0], ve[0], rp[1] - rp[0], wq[0], wt[0]);
+      auto row = [&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        if constexpr (j + 2 <= 7) load_entries(rp[j + 2], ce[j & 1], ve[j & 1]);
+        if constexpr (j + 1 <= 7)
+          gather(ce[(j + 1) & 1], ve[(j + 1) & 1], rp[j + 2] - rp[j + 1], wq[(j + 1) & 1],
+                 wt[(j + 1) & 1]);
+        float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ngroups += (rp[j + 1] - rp[j] + G - 1) / G;
-      // the next group to load: first non-zero gb, end of its row rend, row ri
-      int gb = eb, rend = 0, ri = 0;
-      // row of entry e (0..7) and the end of that row, from the boundaries in
-      // scalar registers (no indexing of registers)
-      auto locate = [&](int e) {
-        int i = 0, r = rp[8];
+        for (int u = 0; u < G; ++u) fma_wseg<kBf16W>(wt[j & 1][u], wq[j & 1][u], acc4);
+        // further groups of a row of more than G non-zeros
+        for (int e0 = rp[j] + G; e0 < rp[j + 1]; e0 += G) {
+          int cv;
+          float vv;
+          load_entries(e0, cv, vv);
+          WSeg<kBf16W> w[G];
+          float t[G];
+          gather(cv, vv, rp[j + 1] - e0, w, t);
 #pragma unroll
-        for (int t = 7; t >= 1; --t) {
-          const bool above = rp[t] > e;
-          r = above ? rp[t] : r;      // boundaries ascend: the last one kept is the least above e
-          i = (!above && i == 0) ? t : i;
+          for (int u = 0; u < G; ++u) fma_wseg<kBf16W>(t[u], w[u], acc4);
         }
-        ri = __builtin_amdgcn_readfirstlane(i);
-        rend = __builtin_amdgcn_readfirstlane(r);
-      };
-      locate(eb);
-      WSeg<kBf16W> wq[D][G];
-      float vq[D][G];
-      int rq[D];     // row of the group, or -1: not its row's last group
-      // load the group at (gb, rend, ri), then step to the next one; past the
-      // last group the loads repeat entry ee - 1 with weight 0
-      auto load_group = [&](int d) {
-        int k[G];
-        float v[G];
-        if (gb + G <= ee) {
-#pragma unroll
-          for (int u = 0; u < G; ++u) {
-            k[u] = col_c[gb + u];
-            v[u] = val_c[gb + u];
-          }
-        } else {
-          // near the range's end: global-pointer loads, which the compiler
-          // cannot fold into the whole-group loads above (they would lose
-          // their 8-dword form)
-#pragma unroll
-          for (int u = 0; u < G; ++u) {
-            const int e = gb + u < ee ? gb + u : ee - 1;
-            k[u] = __builtin_amdgcn_readfirstlane(col[e]);
-            v[u] = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(val[e])));
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < G; ++u) wq[d][u] = load_wseg<kBf16W, kWVec>(rsW, voffW, k[u] * row_bytes);
-        const bool last = gb + G >= rend;
-        if (last) {
-          // the row's last group: slots past its end weigh 0
-#pragma unroll
-          for (int u = 0; u < G; ++u) vq[d][u] = gb + u < rend ? v[u] : 0.0f;
-        } else {
-#pragma unroll
-          for (int u = 0; u < G; ++u) vq[d][u] = v[u];
-        }
-        rq[d] = (last && gb < ee) ? ri : -1;
-        // the gathers stay where they are issued (the scheduler would sink
-        // them towards their use to save registers, which undoes the prefetch)
-        __builtin_amdgcn_sched_barrier(0);
-        if (!last) {
-          gb += G;
-        } else {
-          gb = rend;
-          if (gb < ee) locate(gb);
-          else rend = ee + G;  // past the end: zero groups from here on
-        }
-      };
-      float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      // gathers issued after a group's own when it is consumed: the D - 1
-      // groups behind it (nothing else in the loop counts in vmcnt), so one
-      // wait per group covers its G gathers
-      constexpr int kLoadsAfter = (D - 1) * G * (kWVec ? 1 : 4);
-      static_assert(kLoadsAfter < 64, "vmcnt immediate");
-      auto consume = [&](int d) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(kLoadsAfter, 15));
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < G; ++u) fma_wseg<kBf16W>(vq[d][u], wq[d][u], acc4);
-        if (rq[d] >= 0) {
-          float* const p = rows + rq[d] * kPitch + lds_col(rq[d], c4);
+        if (rp[j + 1] > rp[j]) {
+          float* const p = rows + j * kPitch + lds_col(j, c4);
           f32x4 y = *reinterpret_cast<const f32x4*>(p);
           y[0] = __fadd_rn(y[0], acc4[0]);
           y[1] = __fadd_rn(y[1], acc4[1]);
           y[2] = __fadd_rn(y[2], acc4[2]);
           y[3] = __fadd_rn(y[3], acc4[3]);
           *reinterpret_cast<f32x4*>(p) = y;
-          acc4[0] = acc4[1] = acc4[2] = acc4[3] = 0.0f;
         }
       };
-#pragma unroll
-      for (int d = 0; d < D; ++d) load_group(d);
-      for (int it = (ngroups + D - 1) / D; it > 0; --it) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-          consume(d);
-          load_group(d);
-        }
-      }
-      // the groups issued past the end have landed before their registers are
-      // reused (one wait here instead of one per store below)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm(0, 15));
+      row(std::integral_constant<int, 0>{});
+      row(std::integral_constant<int, 1>{});
+      row(std::integral_constant<int, 2>{});
+      row(std::integral_constant<int, 3>{});
+      row(std::integral_constant<int, 4>{});
+      row(std::integral_constant<int, 5>{});
+      row(std::integral_constant<int, 6>{});
+      row(std::integral_constant<int, 7>{});
     }
     // the 8 rows, Y0 + s (rows without non-zeros: Y0 as it is), to Y
 #pragma unroll
@@ -851,10 +814,10 @@ hipError_t run_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq, const
   // gathers run in the GEMM's waves (two per SIMD), which hide memory latency
   // worse than the separate kernel's eight, and it needs the 128 x 256 tile.
   // Measured on the LLaMA-shaped workloads (GEMM with compensation, us,
-  // fused against the large-tile GEMM + separate kernel): 13B up 5.1/row 509
-  // against 305 + 214; 13B down 13.8/row 406 against 273 + 118; 1.3B up
-  // 20/row 172 against 45 + 74; 7B up 41/row 843 against 219 + 468. The COO's
-  // capacity bounds the non-zeros (for the select's own COO it is M*K*(1-q)).
+  // fused against the large-tile GEMM + separate kernel): 13B up 5.1/row
+  // 437-459 against 295 + 215; 13B down 13.8/row 384 against 364; 1.3B up
+  // 20/row 144 against 112; 7B up 41/row 948 against 656. The COO's capacity
+  // bounds the non-zeros (for the select's own COO it is M*K*(1-q)).
   const bool fused = sp.row_ptr != nullptr && sp.capacity <= kFusedMaxPerRow * M;
   if (!fused) {
     static_assert(GemmTile::BM == 2 * GemmSmallTile::BM && GemmTile::BN == GemmSmallTile::BN,
