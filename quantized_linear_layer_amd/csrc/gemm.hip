@@ -66,14 +66,14 @@
 //    operand tiles that concurrent workgroups re-read.
 //  * With the compensation, the tile leaves in four chunks of 64 rows x all
 //    256 columns (each wave row's 16 x 256 block in half a stage buffer).
-//    After a barrier each wave finishes 8 whole rows of a chunk: a lane owns 4
-//    consecutive columns, so a non-zero costs one 8-byte (bf16 W) or 16-byte
-//    (fp32 W) gather per lane, addressed with the W row offset in the scalar
-//    operand of a buffer load, and its column and value come from scalar
-//    loads. The non-zeros of a wave's 8 consecutive rows are one contiguous
-//    range of the row-major COO; they are gathered in groups of 8, two groups
-//    in flight, across row boundaries. Each row is stored once, 1 KiB per
-//    wave instruction.
+//    After a barrier each wave finishes 8 whole rows of a chunk, one after the
+//    other: a lane owns 4 consecutive columns, so a non-zero costs one 8-byte
+//    (bf16 W) or 16-byte (fp32 W) gather per lane, addressed with the W row
+//    offset in the scalar operand of a buffer load. A row's first 8 entries
+//    (column, value) come in with one vector load by lanes 0..7 and reach the
+//    wave through readlane; entries are loaded two rows ahead and gathered
+//    one row ahead of the row being multiplied. Each row is stored once,
+//    1 KiB per wave instruction.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -314,6 +314,9 @@ __device__ __attribute__((always_inline)) inline void fused_epilogue(
   // pace of the whole epilogue).
   typedef const __attribute__((address_space(4))) int32_t cint32;
   cint32* const rp_c = (cint32*)row_ptr;
+  // nnz <= capacity <= 10 M (this schedule's limit) and M < 2^25 (packed rows
+  // of at least 64 bytes addressed with 32-bit offsets), so byte offsets of
+  // entries fit 32 bits
   const int nnz = rp_c[M];
   const __amdgpu_buffer_rsrc_t rsCol =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(col), 0, nnz * 4, kBufferFlags);
