@@ -215,15 +215,42 @@ __device__ inline uint32_t wave_exclusive_scan(uint32_t v, uint32_t& total) {
 // range, and |x| * inv <= 6 cannot overflow), so the code is the table lookup
 // at n = (uint)min(y4, 20) with no NaN to guard against; otherwise (a zero or
 // subnormal row amax) the encoder of the generic path is used.
-__device__ inline uint32_t bf16_pair_code(uint32_t w, float tau, float inv4) {
-  const float lo = fminf(fabsf(__uint_as_float(w << 16)), tau);
-  const float hi = fminf(fabsf(__uint_as_float(w & 0xffff0000u)), tau);
-  const uint32_t nlo = uint32_t(fminf(__fmul_rn(lo, inv4), 20.0f));
-  const uint32_t nhi = uint32_t(fminf(__fmul_rn(hi, inv4), 20.0f));
+// The clamp to tau costs no operation of its own: rounding is monotone, so
+// RN32(min(|x|, tau) * 4inv) = min(RN32(|x| * 4inv), RN32(tau * 4inv)), and with
+// the cap at 20 both minima fold into one against cap4 = min(RN32(tau * 4inv), 20).
+__device__ inline float code_cap4(float tau, float inv4) {
+  return fminf(__fmul_rn(tau, inv4), 20.0f);
+}
+
+// Magnitude codes of the two elements of a bfloat16 pair word (bits 0-2: the
+// low half, bits 4-6: the high half).
+__device__ inline uint32_t bf16_pair_mag(uint32_t w, float inv4, float cap4) {
+  const uint32_t nlo = uint32_t(fminf(__fmul_rn(fabsf(__uint_as_float(w << 16)), inv4), cap4));
+  const uint32_t nhi =
+      uint32_t(fminf(__fmul_rn(fabsf(__uint_as_float(w & 0xffff0000u)), inv4), cap4));
   constexpr uint64_t kLut = e2m1_lut();
   const uint32_t mlo = uint32_t(kLut >> (3u * nlo)) & 7u;
   const uint32_t mhi = uint32_t(kLut >> (3u * nhi)) & 7u;
-  return mlo | (mhi << 4) | ((w >> 12) & 0x8u) | ((w >> 24) & 0x80u);
+  return mlo | (mhi << 4);
+}
+
+// Sign bits of the 8 codes of a bfloat16 chunk (bit 3 of each nibble): byte k
+// of the code word holds elements 2k (low half of word k) and 2k+1 (high
+// half), whose signs are bit 7 of bytes 1 and 3 of word k. Four byte permutes
+// gather those bytes, one per word, into place.
+__device__ inline uint32_t bf16_chunk_signs(const uint4& w) {
+  const uint32_t hs = __builtin_amdgcn_perm(w.y, w.x, 0x0c0c0703u) |
+                      __builtin_amdgcn_perm(w.w, w.z, 0x07030c0cu);
+  const uint32_t ls = __builtin_amdgcn_perm(w.y, w.x, 0x0c0c0501u) |
+                      __builtin_amdgcn_perm(w.w, w.z, 0x05010c0cu);
+  return (hs & 0x80808080u) | ((ls >> 4) & 0x08080808u);
+}
+
+// The 8 codes of a bfloat16 chunk (4 * inv finite), low nibble first.
+__device__ inline uint32_t bf16_chunk_code(const uint4& w, float inv4, float cap4) {
+  return bf16_pair_mag(w.x, inv4, cap4) | (bf16_pair_mag(w.y, inv4, cap4) << 8) |
+         (bf16_pair_mag(w.z, inv4, cap4) << 16) | (bf16_pair_mag(w.w, inv4, cap4) << 24) |
+         bf16_chunk_signs(w);
 }
 
 __device__ inline uint32_t bf16_pair_code_slow(uint32_t w, float tau, float inv) {
@@ -267,13 +294,11 @@ __device__ inline void quantize_bf16_row(const uint4 (&w)[CH], int64_t Kp, float
   if (lane == 0) *s_out = s;
   const float inv4 = __fmul_rn(inv, 4.0f);
   if (inv4 < __builtin_huge_valf()) {
+    const float cap4 = code_cap4(tau, inv4);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int64_t c = (int64_t(j) * kWave + lane) * 8;
-      if (c < Kp)
-        *reinterpret_cast<uint32_t*>(qrow + c / 2) =
-            bf16_pair_code(w[j].x, tau, inv4) | (bf16_pair_code(w[j].y, tau, inv4) << 8) |
-            (bf16_pair_code(w[j].z, tau, inv4) << 16) | (bf16_pair_code(w[j].w, tau, inv4) << 24);
+      if (c < Kp) *reinterpret_cast<uint32_t*>(qrow + c / 2) = bf16_chunk_code(w[j], inv4, cap4);
     }
   } else {
 #pragma unroll

@@ -627,35 +627,54 @@ __device__ inline float chunk_value(const Vec8<F32In>& v, int i) {
   return __uint_as_float(uint32_t(d >> (32 * (i & 1))));
 }
 
-__device__ inline uint32_t chunk_key(const uint4& w, int i) {
+// Element mask of a chunk: bit i set when element i's magnitude key exceeds
+// tau's. bfloat16: as in count_fold, adding bias = 0x7fff - tkey to both
+// 15-bit keys of a word sets bit 15 of a half exactly when its key exceeds
+// tkey; the flags of word i (elements 2i and 2i+1, bits 15 and 31) are moved
+// to bits 2i and 2i+16, and the upper ones then down to 2i+1.
+__device__ inline uint32_t chunk_mask(const uint4& w, uint32_t, uint32_t bias2) {
   const uint32_t q[4] = {w.x, w.y, w.z, w.w};
-  return ((i & 1) ? (q[i >> 1] >> 16) : q[i >> 1]) & 0x7fffu;
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x |= (((q[i] & 0x7fff7fffu) + bias2) & 0x80008000u) >> (15 - 2 * i);
+  return (x | (x >> 15)) & 0xffu;
 }
 
-__device__ inline uint32_t chunk_key(const Vec8<F32In>& v, int i) { return F32In::key(v.v[i]); }
+__device__ inline uint32_t chunk_mask(const Vec8<F32In>& v, uint32_t tkey, uint32_t) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m |= uint32_t(F32In::key(v.v[i]) > tkey) << i;
+  return m;
+}
 
 // Write every |a| > tau entry of a slab, ascending column, from position pos.
 // The entries of chunk (j, lane) follow those of all chunks (j', *) with
-// j' < j and (j, lane') with lane' < lane; per element position i of a chunk
-// a wave ballot of the predicate gives, through mbcnt, how many entries the
-// lower lanes hold at that position, so the rank needs no LDS and no barrier.
+// j' < j and (j, lane') with lane' < lane. A lane's count n of entries in its
+// chunk is at most 8; the entries of the lower lanes number the sum over
+// t >= 1 of how many lower lanes have n >= t, one wave ballot and mbcnt per t,
+// stopping at the first t no lane reaches (entries are sparse: usually after
+// t = 2, and at once for a chunk sweep without any). No LDS, no barrier.
 template <class C, int CH>
 __device__ inline void compact_slab(const C (&v)[CH], int64_t c0, int64_t r, uint32_t tkey,
-                                    float tau, uint32_t& pos, uint32_t cap,
+                                    uint32_t bias, float tau, uint32_t& pos, uint32_t cap,
                                     int32_t* __restrict__ out_row, int32_t* __restrict__ out_col,
                                     float* __restrict__ out_val) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    uint32_t lower = 0, total = 0, mine = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool p = chunk_key(v[j], i) > tkey;
-      const uint64_t b = __ballot(p);
+    uint32_t mine = chunk_mask(v[j], tkey, bias);
+    const uint32_t n = uint32_t(__popc(mine));
+    uint64_t b = __ballot(n != 0u);
+    if (b == 0) continue;  // wave-uniform: no entry in this chunk sweep
+    uint32_t lower = __builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32),
+                                               __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0u));
+    uint32_t total = uint32_t(__popcll(b));
+    for (uint32_t t = 2; t <= 8; ++t) {
+      b = __ballot(n >= t);
+      if (b == 0) break;
       lower = __builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32),
                                         __builtin_amdgcn_mbcnt_lo(uint32_t(b), lower));
       total += uint32_t(__popcll(b));
-      mine |= uint32_t(p) << i;
     }
     // One store per array for each set bit of the lane, lowest first: a lane
     // rarely holds more than one entry of a chunk, so the wave usually
@@ -681,19 +700,17 @@ __device__ inline void compact_slab(const C (&v)[CH], int64_t c0, int64_t r, uin
 
 // Token-wise codes of a chunk clamped to tau, 8 per 32-bit word (low nibble
 // first). bfloat16 with quick (4 * inv finite): two codes per word of the
-// chunk from y4 = RN32(|x| * 4inv) (bf16_pair_code); otherwise, and for
+// chunk from y4 = RN32(|x| * 4inv) (bf16_chunk_code); otherwise, and for
 // float32, the generic encoder.
 __device__ inline uint32_t encode_chunk(const uint4& w, float tau, float inv, float inv4,
-                                        bool quick) {
-  if (quick)
-    return bf16_pair_code(w.x, tau, inv4) | (bf16_pair_code(w.y, tau, inv4) << 8) |
-           (bf16_pair_code(w.z, tau, inv4) << 16) | (bf16_pair_code(w.w, tau, inv4) << 24);
+                                        float cap4, bool quick) {
+  if (quick) return bf16_chunk_code(w, inv4, cap4);
   return bf16_pair_code_slow(w.x, tau, inv) | (bf16_pair_code_slow(w.y, tau, inv) << 8) |
          (bf16_pair_code_slow(w.z, tau, inv) << 16) | (bf16_pair_code_slow(w.w, tau, inv) << 24);
 }
 
 __device__ inline uint32_t encode_chunk(const Vec8<F32In>& v, float tau, float inv, float,
-                                        bool) {
+                                        float, bool) {
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -834,6 +851,7 @@ __device__ __attribute__((always_inline)) inline void compact_rows_body(
   const int64_t r0 = bid * R;
   const int64_t r1 = (r0 + R < M) ? r0 + R : M;
   const uint32_t tkey = st->tau_key;
+  const uint32_t bias = count_bias<In>(tkey);
   const float tau = *tau_p;
   const uint32_t cap = uint32_t(capacity < INT32_MAX ? capacity : INT32_MAX);
   const int64_t Kp = ldq * 2;
@@ -862,11 +880,12 @@ __device__ __attribute__((always_inline)) inline void compact_rows_body(
     if (r < r1) {
       const typename In::T* row = A + r * lda;
       uint8_t* qrow = Xq + r * ldq;
-      float inv = 0.0f, inv4 = 0.0f;
+      float inv = 0.0f, inv4 = 0.0f, cap4 = 0.0f;
       if constexpr (kQuant == kQuantToken) {
         float s;
         vector_scale(sX[r], s, inv);
         inv4 = __fmul_rn(inv, 4.0f);
+        cap4 = code_cap4(tau, inv4);
         if (lane == 0) sX[r] = s;
       }
       const bool quick = inv4 < __builtin_huge_valf();
@@ -876,14 +895,14 @@ __device__ __attribute__((always_inline)) inline void compact_rows_body(
         constexpr bool kFull = decltype(full)::value;
         C v[CH];
         load_row_slab<In, kFast, kFull, CH, kStream>(row, c0, K, v);
-        compact_slab<C, CH>(v, c0, r, tkey, tau, pos, cap, out_row, out_col, out_val);
+        compact_slab<C, CH>(v, c0, r, tkey, bias, tau, pos, cap, out_row, out_col, out_val);
         if constexpr (kQuant != kQuantNone) {
 #pragma unroll
           for (int j = 0; j < CH; ++j) {
             // chunks in [K, Kp) are zero and encode to the zero padding
             const int64_t c = c0 + (int64_t(j) * kWave + lane) * 8;
             if constexpr (kQuant == kQuantToken) {
-              const uint32_t word = encode_chunk(v[j], tau, inv, inv4, quick);
+              const uint32_t word = encode_chunk(v[j], tau, inv, inv4, cap4, quick);
               if (kFull || c < Kp) *reinterpret_cast<uint32_t*>(qrow + c / 2) = word;
             } else {
               int e;
