@@ -447,6 +447,31 @@ def test_gemm_integer_exact(ql, M, N, K):
     assert np.array_equal(Y.astype(np.float64), want)
 
 
+# The 256 x 256 tiles (grids of at least 512 of them) at 1, 2, 3, 5, 8 and 33
+# K steps of 128 codes: every count below the three LDS stages and every
+# residue modulo them, at a launch geometry the small shapes above do not reach.
+@pytest.mark.parametrize("K", [128, 256, 384, 640, 1024, 4224])
+def test_gemm_large_tiles_k_steps(ql, K):
+    """Unit scales, 4096 x 8192 (512 large tiles): sampled rows (the first and
+    last of every 256-row tile and 32 more) are the exact integer product over
+    all 8192 columns."""
+    M, N = 4096, 8192
+    log(f"gemm large tiles {M}x{N}x{K}")
+    rng = np.random.default_rng(K)
+    ca = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    cb = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    t = torch()
+    Y = ql.gemm(upload_u8(O.pack_rows(ca)), t.ones(M, dtype=t.float32, device="cuda:0"),
+                upload_u8(O.pack_rows(cb)), t.ones(N, dtype=t.float32, device="cuda:0"), M, N, K)
+    t.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, M, 256), np.arange(255, M, 256),
+                                     rng.choice(M, 32, replace=False)]))
+    sel = t.as_tensor(rows, device="cuda:0")
+    want = O.integer_product(ca[rows], cb)
+    assert np.array_equal(host(Y[sel]).astype(np.float64), want)
+    del Y
+
+
 def test_gemm_one_hot_layout(ql):
     """A[i,k] = 1 only at k = p[i]; B[j,k] = 1 only at k = r[j]: Y[i,j] = [p[i] == r[j]]."""
     M, N, K = 96, 80, 512
