@@ -222,8 +222,11 @@ fp4lin_status fp4lin_quantize_weight(const void* W, fp4lin_dtype dt, int64_t K, 
  *   s[i,j]   = sum_{(i,k) in dA} val*W[k,j], accumulated from 0 in ascending k
  *              with fp32 fused multiply-add, then added once to the product
  *              (rows without non-zeros: the product as it is).
- * The compensation runs in the same kernel's epilogue (compensation
- * paragraph: dA W added back), so Y is written once.
+ * The compensation (compensation paragraph: dA W added back) has two
+ * schedules with the same bits, picked from dA.capacity: up to 10 entries per
+ * row of A (capacity <= 10*M) it runs in the GEMM's epilogue and Y is written
+ * once; above that the GEMM writes Y and a second kernel adds s to it (faster
+ * at those densities).
  *   Aq, sA   device, M x packed_ld(K) bytes, M floats
  *   Bq, sB   device, N x packed_ld(K) bytes (N-major), N floats
  *   dA       host pointer to a COO descriptor, or NULL for no compensation;
@@ -246,8 +249,8 @@ fp4lin_status fp4lin_gemm(const uint8_t* Aq, const float* sA, const uint8_t* Bq,
  * non-zeros of dA, ascending k, of val * W[k,:], accumulated from 0 with fp32
  * fused multiply-add. Rows without non-zeros are not touched. fp4lin_gemm with
  * a non-NULL dA gives bit for bit what fp4lin_gemm with dA = NULL followed by
- * this call gives (it computes the same sum in its epilogue, without reading
- * Y back).
+ * this call gives, with either of its schedules (in its epilogue it computes
+ * the same sum without reading Y back).
  *   dA       host pointer to a COO descriptor (device arrays; row is not read)
  *   W        device K x N weight (dtype wdt, leading dimension ldw); column
  *            indices of dA must be < K
